@@ -1,0 +1,144 @@
+"""The unsharded layer in float64, written as its textbook definition (oracle side).
+
+Data flow ("Tensor parallel scaling curves", section "What tensor parallelism
+actually splits", and "Tensor Parallelism Fundamentals", section "Mechanics of
+Matrix Slicing"): the attention block computes q, k, v = x @ W_q, x @ W_k,
+x @ W_v, attends per head and projects with W_o; the MLP block applies gate and
+up projections and a down projection. Weights are logical [in, out].
+
+Readings the pages leave open:
+- The nonlinearity between gate/up and down is SwiGLU: silu(x @ W_gate) *
+  (x @ W_up), silu(z) = z * sigmoid(z) (Shazeer 2020, "GLU Variants Improve
+  Transformer").
+- RMSNorm is y = x * gamma / sqrt(mean(x^2) + eps) (Zhang & Sennrich 2019).
+- Decode attention: one query per sequence, scores scaled by 1/sqrt(d), a
+  softmax over the kv_len cached keys, no mask and no rotary embedding. The new
+  token's k and v overwrite cache position kv_len - 1 before attending. Query
+  head h reads kv head floor(h / (n_q / n_kv)) (grouped-query attention).
+- The full layer is pre-norm with residual adds: h = x + attn(norm1(x)),
+  out = h + mlp(norm2(h)); ``residual=False`` gives the pages' literal flow.
+- No biases.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import numpy as np
+
+
+def f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def rmsnorm(x, gamma, eps: float) -> np.ndarray:
+    """x * gamma / sqrt(mean over the last axis of x^2 + eps)."""
+    x = f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * f64(gamma)
+
+
+def sigmoid(z) -> np.ndarray:
+    z = f64(z)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z) -> np.ndarray:
+    """z * sigmoid(z)."""
+    z = f64(z)
+    return z * sigmoid(z)
+
+
+def swiglu(gate, up) -> np.ndarray:
+    """silu(gate) * up."""
+    return silu(gate) * f64(up)
+
+
+def linear(x, w) -> np.ndarray:
+    """x @ W with W logical [in, out]."""
+    return f64(x) @ f64(w)
+
+
+def mlp_block(x, w_gate, w_up, w_down, gamma=None, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """Optional RMSNorm, then SwiGLU MLP. Returns every intermediate."""
+    u = rmsnorm(x, gamma, eps) if gamma is not None else f64(x)
+    g = linear(u, w_gate)
+    v = linear(u, w_up)
+    a = swiglu(g, v)
+    y = linear(a, w_down)
+    return {"u": u, "gate": g, "up": v, "a": a, "y": y}
+
+
+def softmax(s) -> np.ndarray:
+    s = f64(s)
+    e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def decode_attention(q, k_cache, v_cache, kv_len: int, n_q: int, n_kv: int, d: int) -> np.ndarray:
+    """Grouped-query decode attention.
+
+    q [B, n_q * d]; caches [B, n_kv, capacity, d]; attends to positions 0..kv_len-1.
+    Returns [B, n_q * d] in head-major order.
+    """
+    q = f64(q).reshape(q.shape[0], n_q, d)
+    B = q.shape[0]
+    group = n_q // n_kv
+    out = np.zeros((B, n_q, d))
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        for h in range(n_q):
+            g = h // group
+            keys = f64(k_cache[b, g, :kv_len])          # [kv_len, d]
+            vals = f64(v_cache[b, g, :kv_len])
+            p = softmax((keys @ q[b, h]) * scale)       # [kv_len]
+            out[b, h] = p @ vals
+    return out.reshape(B, n_q * d)
+
+
+def append_kv(k_cache, v_cache, k_new, v_new, kv_len: int, n_kv: int, d: int):
+    """Copies of the caches with the new token's k, v [B, n_kv * d] at position kv_len - 1."""
+    kc = f64(k_cache).copy()
+    vc = f64(v_cache).copy()
+    B = kc.shape[0]
+    kc[:, :, kv_len - 1, :] = f64(k_new).reshape(B, n_kv, d)
+    vc[:, :, kv_len - 1, :] = f64(v_new).reshape(B, n_kv, d)
+    return kc, vc
+
+
+def attention_block(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len: int, n_q: int, n_kv: int,
+                    d: int, gamma=None, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """Optional RMSNorm, QKV projections, KV append, decode attention, output projection."""
+    u = rmsnorm(x, gamma, eps) if gamma is not None else f64(x)
+    q = linear(u, w_q)
+    k = linear(u, w_k)
+    v = linear(u, w_v)
+    kc, vc = append_kv(k_cache, v_cache, k, v, kv_len, n_kv, d)
+    o = decode_attention(q, kc, vc, kv_len, n_q, n_kv, d)
+    y = linear(o, w_o)
+    return {"u": u, "q": q, "k": k, "v": v, "k_cache": kc, "v_cache": vc, "o": o, "y": y}
+
+
+def layer(x, w: Dict[str, np.ndarray], k_cache, v_cache, kv_len: int, n_q: int, n_kv: int, d: int,
+          eps: float = 1e-5, residual: bool = True) -> Dict[str, np.ndarray]:
+    """Attention block then MLP block.
+
+    ``w`` holds gamma1, w_q, w_k, w_v, w_o, gamma2, w_gate, w_up, w_down (gammas may be None).
+    With ``residual`` the block is pre-norm with residual adds; without it, the MLP
+    consumes the attention output directly, as in the pages' pseudocode.
+    """
+    attn = attention_block(x, w["w_q"], w["w_k"], w["w_v"], w["w_o"], k_cache, v_cache, kv_len,
+                           n_q, n_kv, d, w.get("gamma1"), eps)
+    h = f64(x) + attn["y"] if residual else attn["y"]
+    mlp = mlp_block(h, w["w_gate"], w["w_up"], w["w_down"], w.get("gamma2"), eps)
+    out = h + mlp["y"] if residual else mlp["y"]
+    return {"attn": attn, "h": h, "mlp": mlp, "out": out}
+
+
+def attn_proj_block(x, attn_in, w_q, w_k, w_v, w_o) -> Dict[str, np.ndarray]:
+    """QKV projections of x and W_o applied to a given attention output (no attention between)."""
+    return {"q": linear(x, w_q), "k": linear(x, w_k), "v": linear(x, w_v), "y": linear(attn_in, w_o)}
+
+
+def maybe(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    return None if a is None else f64(a)

@@ -1,0 +1,144 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Each case patches one oracle function with a plausible slip (a dropped term, a
+wrong sign or index, a transposed operand) and runs the pins that cover it.
+"""
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import layer as L
+from oracle import plan
+from oracle import sharded as S
+
+
+def _all_layer_pins():
+    P.pin_silu(L.silu)
+    P.pin_rmsnorm(L.rmsnorm)
+    P.pin_mlp_vs_naive(L.mlp_block)
+    P.pin_attention_vs_naive(L.decode_attention)
+    P.pin_attention_special_cases(L.decode_attention)
+    P.pin_sharded_mlp(S.sharded_mlp, L.mlp_block)
+    P.pin_sharded_layer(S.sharded_layer, L.layer)
+    P.pin_layer_vs_naive(L.layer)
+
+
+def _all_sharded_pins():
+    P.pin_silu(S._silu)
+    P.pin_rmsnorm(lambda x, g, eps: S._norm(x, g, eps))
+    P.pin_column_concat_naive(S.column_shard, plan.rank_plan, plan.ModelDesc)
+    P.pin_row_partials_sum(S.row_shard, S.sum_partials, plan.rank_plan, plan.ModelDesc)
+    P.pin_sharded_mlp(S.sharded_mlp, L.mlp_block)
+    P.pin_sharded_layer(S.sharded_layer, L.layer)
+
+
+def _all_plan_pins():
+    P.pin_kv_worked_example(plan.kv_elements_per_sequence, plan.kv_bytes_per_gpu)
+    P.pin_weight_footprint(plan.weight_bytes_per_gpu)
+    P.pin_head_blocks(plan.rank_plan, plan.ModelDesc)
+    P.pin_workload_shapes(plan.rank_plan, plan.ModelDesc)
+    P.pin_plan_errors(plan.rank_plan, plan.ModelDesc, plan.PlanError)
+
+
+_orig_rank_plan = plan.rank_plan
+_orig_attention = L.decode_attention
+_orig_rank_attention = S.rank_attention
+
+
+def _plan_shift_heads(desc, t, rank):
+    p = dict(_orig_rank_plan(desc, t, rank))
+    p["q_head_begin"] = rank * p["q_heads"] + (1 if rank and p["q_heads"] > 1 else 0)
+    return p
+
+
+def _plan_wrong_inter(desc, t, rank):
+    p = dict(_orig_rank_plan(desc, t, rank))
+    p["inter_begin"] = (t - 1 - rank) * p["inter_cols"] if rank == 0 else p["inter_begin"]
+    return p
+
+
+def _attention_group_modulo(q, k, v, kv_len, n_q, n_kv, d):
+    # query head h reads kv head h % n_kv instead of h // (n_q / n_kv)
+    qq = np.asarray(q, np.float64).reshape(q.shape[0], n_q, d)
+    B = qq.shape[0]
+    out = np.zeros((B, n_q, d))
+    for b in range(B):
+        for h in range(n_q):
+            g = h % n_kv
+            p = L.softmax(np.asarray(k[b, g, :kv_len], np.float64) @ qq[b, h] / np.sqrt(d))
+            out[b, h] = p @ np.asarray(v[b, g, :kv_len], np.float64)
+    return out.reshape(B, n_q * d)
+
+
+def _attention_no_scale(q, k, v, kv_len, n_q, n_kv, d):
+    return _orig_attention(np.asarray(q, np.float64) * np.sqrt(d), k, v, kv_len, n_q, n_kv, d)
+
+
+def _attention_short(q, k, v, kv_len, n_q, n_kv, d):
+    return _orig_attention(q, k, v, max(kv_len - 1, 1), n_q, n_kv, d)
+
+
+def _append_wrong_slot(kc, vc, kn, vn, kv_len, n_kv, d):
+    # writes the new token at position kv_len instead of kv_len - 1
+    kc2 = np.asarray(kc, np.float64).copy()
+    vc2 = np.asarray(vc, np.float64).copy()
+    j = min(kv_len, kc2.shape[2] - 1)
+    B = kc2.shape[0]
+    kc2[:, :, j] = np.asarray(kn, np.float64).reshape(B, n_kv, d)
+    vc2[:, :, j] = np.asarray(vn, np.float64).reshape(B, n_kv, d)
+    return kc2, vc2
+
+
+MUTATIONS = {
+    # elementwise
+    "silu_sign": (L, "silu", lambda z: np.asarray(z, float) * L.sigmoid(-np.asarray(z, float)), _all_layer_pins),
+    "silu_is_sigmoid": (L, "silu", lambda z: L.sigmoid(z), _all_layer_pins),
+    "sharded_silu_half": (S, "_silu", lambda z: np.asarray(z, float) * (1 + np.tanh(0.5 * np.asarray(z, float))),
+                          _all_sharded_pins),
+    "rmsnorm_sum_not_mean": (L, "rmsnorm", lambda x, g, e: np.asarray(x, float) / np.sqrt(
+        np.sum(np.asarray(x, float) ** 2, axis=-1, keepdims=True) + e) * np.asarray(g, float), _all_layer_pins),
+    "rmsnorm_axis0": (L, "rmsnorm", lambda x, g, e: np.asarray(x, float) / np.sqrt(
+        np.mean(np.asarray(x, float) ** 2, axis=0, keepdims=True) + e) * np.asarray(g, float), _all_layer_pins),
+    "rmsnorm_eps_outside": (L, "rmsnorm", lambda x, g, e: np.asarray(x, float) / (np.sqrt(
+        np.mean(np.asarray(x, float) ** 2, axis=-1, keepdims=True)) + e) * np.asarray(g, float), _all_layer_pins),
+    "rmsnorm_no_gamma": (L, "rmsnorm", lambda x, g, e: np.asarray(x, float) / np.sqrt(
+        np.mean(np.asarray(x, float) ** 2, axis=-1, keepdims=True) + e), _all_layer_pins),
+    "sharded_norm_no_eps": (S, "_norm", lambda x, g, e: S._f(x) / np.sqrt(
+        np.mean(S._f(x) ** 2, axis=1, keepdims=True)) * (1.0 if g is None else S._f(g)), _all_sharded_pins),
+    # blocks
+    "swiglu_on_up": (L, "swiglu", lambda g, u: L.silu(u) * np.asarray(g, float), _all_layer_pins),
+    "linear_reads_out_in": (L, "linear", lambda x, w: np.asarray(x, float) @ np.asarray(w, float).reshape(
+        np.shape(w)[1], np.shape(w)[0]).T, _all_layer_pins),
+    "attention_group_modulo": (L, "decode_attention", _attention_group_modulo, _all_layer_pins),
+    "attention_no_scale": (L, "decode_attention", _attention_no_scale, _all_layer_pins),
+    "attention_drops_last_key": (L, "decode_attention", _attention_short, _all_layer_pins),
+    "append_wrong_slot": (L, "append_kv", _append_wrong_slot, _all_layer_pins),
+    # decomposition
+    "sum_drops_last_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
+        [np.asarray(p, float) for p in parts[:-1]] or [np.zeros_like(parts[0])], axis=0)
+        + (0.0 if residual is None else np.asarray(residual, float)), _all_sharded_pins),
+    "column_shard_off_by_one": (S, "column_shard", lambda w, b, c: np.asarray(w)[:, b + (1 if b else 0):b + c + (1 if b else 0)],
+                                _all_sharded_pins),
+    "row_shard_as_columns": (S, "row_shard", lambda w, b, c: np.asarray(w)[b:b + c, :][:, ::-1], _all_sharded_pins),
+    "rank_attention_residual_per_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
+        [np.asarray(p, float) + (0.0 if residual is None else np.asarray(residual, float)) for p in parts], axis=0),
+        _all_sharded_pins),
+    # planner
+    "kv_missing_factor_two": (plan, "kv_elements_per_sequence", lambda L_, h, d, s: L_ * h * d * s, _all_plan_pins),
+    "kv_not_divided_by_t": (plan, "kv_bytes_per_gpu", lambda L_, h, d, s, b, B, t:
+                            plan.kv_elements_per_sequence(L_, h, d, s) * b * B, _all_plan_pins),
+    "weights_not_divided": (plan, "weight_bytes_per_gpu", lambda total, t: total, _all_plan_pins),
+    "heads_shifted": (plan, "rank_plan", _plan_shift_heads, _all_plan_pins),
+    "inter_block_swapped": (plan, "rank_plan", _plan_wrong_inter, _all_sharded_pins),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    mod, attr, fn, pins = MUTATIONS[name]
+    monkeypatch.setattr(mod, attr, fn)
+    if mod is plan:
+        # the sharded module reaches the planner through its own import of the module
+        monkeypatch.setattr(S._plan, attr, fn)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        pins()

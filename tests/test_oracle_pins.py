@@ -1,0 +1,77 @@
+"""The oracle against its pins (CPU only)."""
+import oracle_pins as P
+from oracle import layer as L
+from oracle import plan
+from oracle import sharded as S
+
+
+def test_kv_worked_example():
+    P.pin_kv_worked_example(plan.kv_elements_per_sequence, plan.kv_bytes_per_gpu)
+
+
+def test_weight_footprint():
+    P.pin_weight_footprint(plan.weight_bytes_per_gpu)
+
+
+def test_head_blocks():
+    P.pin_head_blocks(plan.rank_plan, plan.ModelDesc)
+
+
+def test_workload_shapes():
+    P.pin_workload_shapes(plan.rank_plan, plan.ModelDesc)
+
+
+def test_plan_errors():
+    P.pin_plan_errors(plan.rank_plan, plan.ModelDesc, plan.PlanError)
+
+
+def test_silu_layer():
+    P.pin_silu(L.silu)
+
+
+def test_silu_sharded():
+    P.pin_silu(S._silu)
+
+
+def test_rmsnorm_layer():
+    P.pin_rmsnorm(L.rmsnorm)
+
+
+def test_rmsnorm_sharded():
+    P.pin_rmsnorm(lambda x, g, eps: S._norm(x, g, eps))
+
+
+def test_mlp_vs_naive():
+    P.pin_mlp_vs_naive(L.mlp_block)
+
+
+def test_attention_vs_naive():
+    P.pin_attention_vs_naive(L.decode_attention)
+
+
+def test_attention_special_cases():
+    P.pin_attention_special_cases(L.decode_attention)
+
+
+def test_column_concat_bitwise():
+    P.pin_column_concat_naive(S.column_shard, plan.rank_plan, plan.ModelDesc)
+
+
+def test_row_partials_sum():
+    P.pin_row_partials_sum(S.row_shard, S.sum_partials, plan.rank_plan, plan.ModelDesc)
+
+
+def test_sharded_mlp_matches_unsharded():
+    P.pin_sharded_mlp(S.sharded_mlp, L.mlp_block)
+
+
+def test_sharded_layer_matches_unsharded():
+    P.pin_sharded_layer(S.sharded_layer, L.layer)
+
+
+def test_layer_literal_flow():
+    P.pin_layer_literal_flow(L.layer, L.attention_block, L.mlp_block)
+
+
+def test_layer_vs_naive():
+    P.pin_layer_vs_naive(L.layer)
