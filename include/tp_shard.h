@@ -1,0 +1,262 @@
+/*
+ * tp_shard.h - one GPU's shard of a Megatron-style tensor-parallel transformer
+ * layer on MI355X (gfx950). C ABI of libtpshard.so.
+ *
+ * What is computed. Each transformer layer's projections are split over t
+ * GPUs ("Tensor parallel scaling curves", section "What tensor parallelism
+ * actually splits"): Q, K, V are split by columns so each rank owns a
+ * contiguous block of attention heads, the attention output projection W_o by
+ * rows, the MLP gate and up projections by columns and the down projection by
+ * rows. A column-parallel projection takes the replicated input and yields
+ * this rank's slice of output columns; a row-parallel projection takes the
+ * column-parallel output directly and yields a partial sum of the full output;
+ * an all-reduce adds the t partials ("Tensor Parallelism Fundamentals",
+ * section "Mechanics of Matrix Slicing"). Two such sums occur per layer,
+ * after W_o and after the down projection. On one GPU the all-reduce is
+ * replaced by tp_partial_sum over t partials held in device memory.
+ *
+ * Readings where the pages are silent: SwiGLU, silu(gate) * up, between the
+ * gate/up and down projections; RMSNorm x * gamma / sqrt(mean(x^2) + eps) in
+ * front of the column projections; decode attention with one query per
+ * sequence, scale 1/sqrt(head_dim), no mask and no rotary embedding, query
+ * head h reading kv head h / (n_q / n_kv); no biases.
+ *
+ * Conventions shared by every entry point
+ *  - Memory. The caller owns and allocates all memory. Pointers named as
+ *    device pointers refer to device memory of the current HIP device; the
+ *    library never allocates, frees, synchronises or changes the device.
+ *    Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *    and the call returns before it completes.
+ *  - Layouts. Matrices are row-major. Activations are [m, features]. A
+ *    weight is stored [out, in] with `in` (the contraction dimension K)
+ *    contiguous. Row partials are float32. bf16 is IEEE bfloat16 bits;
+ *    float32 and bf16 inputs are multiplied with float32 accumulation.
+ *  - Alignment. Every device pointer must be 16-byte aligned and K a multiple
+ *    of 8 (bf16) or 4 (float32), so that rows stream in 128-bit loads.
+ *  - Workspace. Entry points with `ws` need device scratch memory of at least
+ *    the size the matching *_workspace_bytes function returns, 256-byte
+ *    aligned, and zero-filled by the caller once, before its first use. Every
+ *    call leaves the workspace's counters at zero again, so it can be reused
+ *    without clearing. Calls sharing one workspace must not overlap in time
+ *    (same stream, or ordered by events).
+ *  - Errors. Arguments are validated on the host before anything is
+ *    enqueued; on failure nothing is enqueued and a tp_status other than
+ *    TP_OK is returned. tp_last_error() then gives a thread-local message
+ *    naming the argument and a hint for the fix. A failed HIP launch returns
+ *    TP_ERR_HIP with the HIP error name in that message.
+ *  - Determinism. No floating-point atomics are used: repeated calls on the
+ *    same inputs give bitwise identical outputs.
+ */
+#ifndef TP_SHARD_H
+#define TP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum tp_status {
+    TP_OK = 0,
+    TP_ERR_NULL = 1,        /* a required pointer is NULL */
+    TP_ERR_SHAPE = 2,       /* a size is zero, negative or beyond a supported limit */
+    TP_ERR_INDIVISIBLE = 3, /* t does not divide the heads or intermediate size, or n_q % n_kv != 0 */
+    TP_ERR_RANK = 4,        /* t outside 1..8, or rank outside 0..t-1 */
+    TP_ERR_DTYPE = 5,       /* dtype not supported by this entry point */
+    TP_ERR_ALIGN = 6,       /* a pointer not 16-byte aligned, or K not a multiple of the 128-bit vector */
+    TP_ERR_WORKSPACE = 7,   /* workspace NULL, misaligned or smaller than required */
+    TP_ERR_KV = 8,          /* kv_len outside 1..capacity */
+    TP_ERR_ALIAS = 9,       /* an output range overlaps an input range */
+    TP_ERR_HIP = 10         /* a HIP launch failed */
+} tp_status;
+
+/* A layer's unsharded shape. n_q_heads = 0 means no attention block,
+ * intermediate = 0 no MLP block. n_layers, seq_len, batch and bytes_per_elem
+ * only feed the footprints of tp_shard_plan. */
+typedef struct tp_model_desc {
+    int64_t hidden;          /* H */
+    int64_t intermediate;    /* I */
+    int32_t n_q_heads;       /* n_q */
+    int32_t n_kv_heads;      /* n_kv */
+    int32_t head_dim;        /* d */
+    int32_t n_layers;        /* L */
+    int64_t seq_len;         /* cached tokens per sequence S */
+    int64_t batch;           /* sequences B */
+    int32_t bytes_per_elem;  /* bytes per cached element */
+    float eps;               /* RMSNorm epsilon */
+} tp_model_desc;
+
+/* What one rank owns. Blocks are contiguous and in rank order. */
+typedef struct tp_rank_plan {
+    int32_t t, rank;
+    int32_t q_head_begin, q_heads;    /* q heads [q_head_begin, q_head_begin + q_heads) */
+    int32_t kv_head_begin, kv_heads;  /* kv heads, likewise */
+    int64_t inter_begin, inter_cols;  /* intermediate columns of gate, up and rows of down */
+    int64_t qkv_cols;                 /* (q_heads + 2 kv_heads) * d: rows of this rank's W_qkv */
+    int64_t o_rows;                   /* q_heads * d: the K of this rank's W_o */
+    int64_t weight_elems;             /* this rank's projection weights, one layer (norms excluded) */
+    int64_t kv_elems_per_seq_all_layers; /* 2 L n_kv d S: one sequence, all layers, unsharded */
+    int64_t kv_bytes_rank;            /* 2 L n_kv d S bytes_per_elem B / t */
+} tp_rank_plan;
+
+/*
+ * tp_shard_plan - what rank `rank` of `t` owns ("Tensor parallel scaling
+ * curves", section "What tensor parallelism actually splits": the rank holds
+ * heads[rank*h_per_gpu : (rank+1)*h_per_gpu]; "Tensor Parallelism
+ * Fundamentals", section "Memory Overhead and Communication Bottlenecks":
+ * weights and KV cache per GPU are the totals divided by t).
+ * Host only; touches no device. Intermediate columns follow the same
+ * contiguous rank order as heads; t must divide n_q, n_kv and I
+ * (TP_ERR_INDIVISIBLE), 1 <= t <= 8 and 0 <= rank < t (TP_ERR_RANK).
+ */
+tp_status tp_shard_plan(const tp_model_desc* desc, int32_t t, int32_t rank, tp_rank_plan* out);
+
+/* Flags for tp_linear_workspace_bytes. */
+#define TP_LINEAR_SWIGLU 1   /* column projection with fused SwiGLU (w_up given) */
+#define TP_LINEAR_NORM   2   /* column projection with fused RMSNorm (gamma given) */
+
+/* Workspace bytes tp_column_linear / tp_row_linear_partial need for these sizes. */
+size_t tp_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, tp_dtype dtype, int32_t flags);
+
+/*
+ * tp_column_linear - column-parallel projection ("Tensor Parallelism
+ * Fundamentals", section "Mechanics of Matrix Slicing": the weight is split
+ * by columns, the input is replicated, each GPU computes its slice of output
+ * columns with no communication).
+ *   u = gamma ? RMSNorm(x; gamma, eps) : x
+ *   y = w_up ? silu(u @ w^T) * (u @ w_up^T)  :  u @ w^T
+ * x      device [m, k] activations (dtype)
+ * w      device [n, k] this rank's column block, stored [out, in] (dtype)
+ * w_up   device [n, k] or NULL: the paired up projection; enables fused SwiGLU
+ * gamma  device [k] or NULL: RMSNorm scale; enables fused RMSNorm
+ * y      device [m, n] output (dtype)
+ * ws     workspace of tp_linear_workspace_bytes(m, k, n, dtype, flags)
+ * Errors: TP_ERR_NULL (x, w, y), TP_ERR_SHAPE (m, k, n < 1), TP_ERR_ALIGN,
+ * TP_ERR_WORKSPACE, TP_ERR_ALIAS (y overlaps x, w, w_up or gamma), TP_ERR_DTYPE.
+ */
+tp_status tp_column_linear(const void* x, const void* w, const void* w_up, const void* gamma, float eps,
+                           void* y, int64_t m, int64_t k, int64_t n, tp_dtype dtype,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tp_swiglu - the rank-local gating between the column-parallel gate/up and
+ * the row-parallel down projection: out = silu(gate) * up, silu(z) = z /
+ * (1 + e^-z), elementwise over [m, n]. The pages name the gate and up
+ * projections ("Tensor parallel scaling curves", section "What tensor
+ * parallelism actually splits"); the gating itself is the SwiGLU reading.
+ * gate, up, out: device [m, n] (dtype). out may equal gate or up (in place);
+ * any other overlap is TP_ERR_ALIAS.
+ */
+tp_status tp_swiglu(const void* gate, const void* up, void* out, int64_t m, int64_t n, tp_dtype dtype,
+                    void* stream);
+
+/*
+ * tp_row_linear_partial - row-parallel projection ("Tensor Parallelism
+ * Fundamentals", section "Mechanics of Matrix Slicing": the weight is split
+ * by rows, the column-parallel output is fed in directly, each GPU yields a
+ * partial sum of the full output).
+ *   partial = a @ w^T, float32
+ * a       device [m, k] this rank's column-parallel output (dtype)
+ * w       device [n, k] this rank's row block, stored [out, in] (dtype)
+ * partial device [m, n] float32
+ * ws      workspace of tp_linear_workspace_bytes(m, k, n, dtype, 0)
+ */
+tp_status tp_row_linear_partial(const void* a, const void* w, float* partial, int64_t m, int64_t k, int64_t n,
+                                tp_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tp_partial_sum - the value the all-reduce after a row-parallel projection
+ * returns ("Tensor parallel scaling curves", section "What tensor parallelism
+ * actually splits": the row-wise splits need an all-reduce to sum the
+ * partial results), computed on one device:
+ *   out = sum_{r=0}^{t-1} partials[r]  (+ residual), in rank order, float32.
+ * partials  host array of t device pointers, each [m, n] float32, 1 <= t <= 8
+ * residual  device [m, n] (out_dtype) or NULL; added once, after the sum
+ * out       device [m, n] (out_dtype); must not overlap any partial
+ */
+tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* residual, void* out,
+                         int64_t m, int64_t n, tp_dtype out_dtype, void* stream);
+
+/* Workspace bytes of tp_decode_attention. */
+size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                    int64_t kv_len);
+
+/*
+ * tp_decode_attention - attention over the heads this rank owns ("Tensor
+ * parallel scaling curves", section "What tensor parallelism actually
+ * splits": local attention on owned heads, no communication). For sequence
+ * b and owned query head h with kv head g = h / (q_heads / kv_heads):
+ *   o[b, h] = sum_j softmax_j(q[b, h] . K[b, g, j] / sqrt(d)) V[b, g, j],
+ *   j = 0 .. kv_len - 1.
+ * q      device [batch, q_heads * d] bf16
+ * k, v   device [batch, kv_heads, capacity, d] bf16 caches
+ * out    device [batch, q_heads * d] bf16
+ * d must be 64 or 128; q_heads / kv_heads at most 16 (TP_ERR_SHAPE);
+ * 1 <= kv_len <= capacity (TP_ERR_KV). bf16 only (TP_ERR_DTYPE).
+ */
+tp_status tp_decode_attention(const void* q, const void* k, const void* v, void* out, int64_t batch,
+                              int32_t q_heads, int32_t kv_heads, int32_t head_dim, int64_t capacity,
+                              int64_t kv_len, tp_dtype dtype, void* ws, size_t ws_bytes, void* stream);
+
+typedef enum tp_stage { TP_STAGE_ATTN = 0, TP_STAGE_MLP = 1 } tp_stage;
+
+/* One rank's weights for one layer, all device pointers, stored [out, in]. */
+typedef struct tp_rank_weights {
+    const void* attn_norm;  /* [H] gamma in front of QKV, or NULL for no norm */
+    const void* w_qkv;      /* [qkv_cols, H]: this rank's Q rows, then K rows, then V rows */
+    const void* w_o;        /* [H, o_rows] */
+    const void* mlp_norm;   /* [H] gamma in front of gate/up, or NULL */
+    const void* w_gate;     /* [inter_cols, H] */
+    const void* w_up;       /* [inter_cols, H] */
+    const void* w_down;     /* [H, inter_cols] */
+} tp_rank_weights;
+
+/* This rank's KV cache for one layer: k, v device [batch, kv_heads, capacity, d]. */
+typedef struct tp_kv_view {
+    void* k;
+    void* v;
+    int64_t capacity;
+    int64_t kv_len;          /* keys attended over, the new token included */
+} tp_kv_view;
+
+/* Workspace bytes of tp_layer_shard_forward for this stage and m. */
+size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                                int64_t m, tp_dtype dtype);
+
+/*
+ * tp_layer_shard_forward - one rank's share of one block of the layer,
+ * ending in the row-parallel partial that the all-reduce would sum ("Tensor
+ * parallel scaling curves", section "What tensor parallelism actually
+ * splits", pseudocode for the attention block and the two all-reduces per
+ * layer).
+ * TP_STAGE_ATTN (decode, bf16): u = RMSNorm(in; attn_norm); [q|k|v] =
+ *   u @ W_qkv^T; the new k, v are written to the cache at position
+ *   kv_len - 1; o = decode attention over the owned heads;
+ *   partial = o @ W_o^T. m is the batch (one new token per sequence).
+ * TP_STAGE_MLP (bf16 or float32, any m): u = RMSNorm(in; mlp_norm);
+ *   a = silu(u @ W_gate^T) * (u @ W_up^T); partial = a @ W_down^T.
+ * in       device [m, H] (dtype): x for ATTN; h = x + sum of attention
+ *          partials for MLP
+ * kv       ATTN only: this rank's cache view; ignored (may be NULL) for MLP
+ * partial  device [m, H] float32
+ * The caller sums the t ranks' partials with tp_partial_sum.
+ */
+tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                                 const tp_rank_weights* weights, const void* in, const tp_kv_view* kv,
+                                 float* partial, int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Name of a status code, e.g. "TP_ERR_SHAPE". */
+const char* tp_status_name(tp_status status);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* tp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_SHARD_H */

@@ -1,0 +1,490 @@
+// C-ABI entry points of libtpshard.so: argument validation, shard planning,
+// workspace sizing and kernel dispatch. Every check runs on the host before
+// anything is enqueued; nothing here allocates device memory or synchronises.
+#include "tp_shard.h"
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tp_status fail(tp_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+tp_status ok() {
+    g_err.clear();
+    return TP_OK;
+}
+
+tp_status hip_fail(hipError_t e, const char* what) {
+    return fail(TP_ERR_HIP, "%s: HIP error %s (%s); check that the pointers are device memory of the current "
+                "device and the stream belongs to it", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+size_t esize(tp_dtype dt) { return dt == TP_BF16 ? 2 : 4; }
+size_t vec_elems(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int kGemvMaxM = 16;   // above this a bf16 projection runs on MFMA when supported
+
+tp_status check_dtype(tp_dtype dt) {
+    if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d is neither TP_F32 nor TP_BF16", (int)dt);
+    return TP_OK;
+}
+
+tp_status check_dims(int64_t m, int64_t k, int64_t n) {
+    if (m < 1 || k < 1 || n < 1)
+        return fail(TP_ERR_SHAPE, "sizes must be >= 1 (m=%lld k=%lld n=%lld)", (long long)m, (long long)k, (long long)n);
+    if (m > kMaxDim || k > kMaxDim || n > kMaxDim || m * n > (int64_t(1) << 40) || n * k > (int64_t(1) << 40))
+        return fail(TP_ERR_SHAPE, "sizes too large (m=%lld k=%lld n=%lld); each must be <= 2^30",
+                    (long long)m, (long long)k, (long long)n);
+    return TP_OK;
+}
+
+tp_status check_ptr(const void* p, const char* name) {
+    if (!p) return fail(TP_ERR_NULL, "%s is NULL", name);
+    if (!aligned16(p)) return fail(TP_ERR_ALIGN, "%s=%p is not 16-byte aligned; allocate with the default "
+                                   "allocator or pad to 16 bytes", name, p);
+    return TP_OK;
+}
+
+tp_status check_ws(void* ws, size_t have, size_t need) {
+    if (need == 0) return TP_OK;
+    if (!ws) return fail(TP_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (reinterpret_cast<uintptr_t>(ws) & 255u)
+        return fail(TP_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+    if (have < need)
+        return fail(TP_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed; size it with the matching "
+                    "*_workspace_bytes call", have, need);
+    return TP_OK;
+}
+
+#define TRY(expr)                       \
+    do {                                \
+        tp_status st_ = (expr);         \
+        if (st_ != TP_OK) return st_;   \
+    } while (0)
+
+bool use_gemm(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi) {
+    return dt == TP_BF16 && epi != tpk::EPI_QKV && m > kGemvMaxM && tpk::gemm_supported((int)m, (int)n, (int)k, epi);
+}
+
+// Workspace layout of a projection: [normalised activations (GEMM path with
+// norm)][split-K scratch (GEMV path)].
+size_t linear_ws(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
+    if (use_gemm(m, k, n, dt, epi)) return norm ? round256((size_t)m * k * esize(dt)) : 0;
+    return round256(tpk::gemv_plan((int)m, (int)k, (int)n, dt == TP_BF16, epi).ws_bytes);
+}
+
+// Enqueue one projection. x [m,k], w (and w_up) [n,k]; y per epilogue.
+tp_status run_linear(const void* x, const void* w, const void* w_up, const void* gamma, float eps, void* y,
+                     int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, void* ws, size_t ws_bytes,
+                     hipStream_t s, const tpk::GemvArgs* qkv = nullptr) {
+    const bool norm = gamma != nullptr;
+    TRY(check_ws(ws, ws_bytes, linear_ws(m, k, n, dt, epi, norm)));
+    if (use_gemm(m, k, n, dt, epi)) {
+        const void* xin = x;
+        if (norm) {
+            hipError_t e = tpk::rmsnorm_launch(x, gamma, ws, (int)m, (int)k, eps, 1, s);
+            if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+            xin = ws;
+        }
+        tpk::GemmArgs g{};
+        g.x = xin; g.w = w; g.w_up = w_up; g.y = y;
+        g.M = (int)m; g.N = (int)n; g.K = (int)k; g.epi = epi;
+        hipError_t e = tpk::gemm_launch(g, s);
+        if (e != hipSuccess) return hip_fail(e, "MFMA GEMM launch");
+        return ok();
+    }
+    tpk::GemvArgs a{};
+    if (qkv) a = *qkv;
+    a.x = x; a.w = w; a.w_up = w_up; a.gamma = gamma; a.y = y;
+    a.m = (int)m; a.K = (int)k; a.N = (int)n; a.eps = eps;
+    a.is_bf16 = dt == TP_BF16;
+    a.epi = epi;
+    a.norm = norm;
+    const tpk::GemvPlan p = tpk::gemv_plan(a.m, a.K, a.N, a.is_bf16, epi);
+    hipError_t e = tpk::gemv_launch(a, p, ws, s);
+    if (e != hipSuccess) return hip_fail(e, "GEMV launch");
+    return ok();
+}
+
+tp_status plan_impl(const tp_model_desc* d, int32_t t, int32_t rank, tp_rank_plan* out) {
+    if (!d) return fail(TP_ERR_NULL, "desc is NULL");
+    if (!out) return fail(TP_ERR_NULL, "out is NULL");
+    if (t < 1 || t > 8) return fail(TP_ERR_RANK, "t=%d outside 1..8 (tensor parallelism stays inside one node)", t);
+    if (rank < 0 || rank >= t) return fail(TP_ERR_RANK, "rank=%d outside 0..%d", rank, t - 1);
+    if (d->hidden <= 0 || d->intermediate < 0 || d->n_q_heads < 0)
+        return fail(TP_ERR_SHAPE, "hidden must be > 0, intermediate and n_q_heads >= 0");
+    const bool attn = d->n_q_heads > 0;
+    if (attn) {
+        if (d->n_kv_heads <= 0 || d->head_dim <= 0)
+            return fail(TP_ERR_SHAPE, "attention needs n_kv_heads > 0 and head_dim > 0");
+        if (d->n_q_heads % d->n_kv_heads)
+            return fail(TP_ERR_INDIVISIBLE, "n_q_heads=%d is not a multiple of n_kv_heads=%d", d->n_q_heads,
+                        d->n_kv_heads);
+        if (d->n_q_heads % t || d->n_kv_heads % t)
+            return fail(TP_ERR_INDIVISIBLE, "t=%d must divide n_q_heads=%d and n_kv_heads=%d; pick t from the "
+                        "common divisors", t, d->n_q_heads, d->n_kv_heads);
+    }
+    if (d->intermediate % t)
+        return fail(TP_ERR_INDIVISIBLE, "t=%d must divide intermediate=%lld", t, (long long)d->intermediate);
+    const int64_t H = d->hidden;
+    const int32_t q_r = attn ? d->n_q_heads / t : 0;
+    const int32_t kv_r = attn ? d->n_kv_heads / t : 0;
+    const int64_t hd = attn ? d->head_dim : 0;
+    const int64_t i_r = d->intermediate / t;
+    tp_rank_plan p{};
+    p.t = t;
+    p.rank = rank;
+    p.q_head_begin = rank * q_r;
+    p.q_heads = q_r;
+    p.kv_head_begin = rank * kv_r;
+    p.kv_heads = kv_r;
+    p.inter_begin = rank * i_r;
+    p.inter_cols = i_r;
+    p.qkv_cols = (q_r + 2 * kv_r) * hd;
+    p.o_rows = q_r * hd;
+    p.weight_elems = H * (q_r + 2 * kv_r) * hd + q_r * hd * H + 3 * H * i_r;
+    if (attn) {
+        const int64_t per_seq = 2 * (int64_t)d->n_layers * d->n_kv_heads * hd * d->seq_len;
+        const int64_t total = per_seq * d->bytes_per_elem * d->batch;
+        p.kv_elems_per_seq_all_layers = per_seq;
+        p.kv_bytes_rank = total / t;
+    }
+    *out = p;
+    return ok();
+}
+
+// The plan the caller passes must be the one tp_shard_plan gives for its t and rank.
+tp_status check_plan(const tp_model_desc* d, const tp_rank_plan* p) {
+    if (!d) return fail(TP_ERR_NULL, "desc is NULL");
+    if (!p) return fail(TP_ERR_NULL, "plan is NULL");
+    tp_rank_plan ref{};
+    TRY(plan_impl(d, p->t, p->rank, &ref));
+    if (ref.q_head_begin != p->q_head_begin || ref.q_heads != p->q_heads || ref.kv_heads != p->kv_heads ||
+        ref.inter_begin != p->inter_begin || ref.inter_cols != p->inter_cols || ref.qkv_cols != p->qkv_cols ||
+        ref.o_rows != p->o_rows)
+        return fail(TP_ERR_SHAPE, "plan does not match desc for t=%d rank=%d; build it with tp_shard_plan",
+                    p->t, p->rank);
+    return TP_OK;
+}
+
+struct LayerWs {
+    size_t act1, act2, lin, attn, total;
+};
+
+LayerWs layer_ws(const tp_model_desc* d, const tp_rank_plan* p, tp_stage stage, int64_t m, tp_dtype dt) {
+    LayerWs w{};
+    const int64_t H = d->hidden;
+    if (stage == TP_STAGE_ATTN) {
+        w.act1 = round256((size_t)m * p->o_rows * 2);   // q
+        w.act2 = round256((size_t)m * p->o_rows * 2);   // attention output
+        const size_t l1 = linear_ws(m, H, p->qkv_cols, dt, tpk::EPI_QKV, true);
+        const size_t l2 = linear_ws(m, p->o_rows, H, dt, tpk::EPI_PARTIAL, false);
+        w.lin = l1 > l2 ? l1 : l2;
+        w.attn = round256(tpk::attn_plan((int)m, p->q_heads, p->kv_heads, d->head_dim, (int)d->seq_len).ws_bytes);
+    } else {
+        w.act1 = round256((size_t)m * p->inter_cols * esize(dt));  // SwiGLU output
+        const size_t l1 = linear_ws(m, H, p->inter_cols, dt, tpk::EPI_SWIGLU, true);
+        const size_t l2 = linear_ws(m, p->inter_cols, H, dt, tpk::EPI_PARTIAL, false);
+        w.lin = l1 > l2 ? l1 : l2;
+    }
+    w.total = w.act1 + w.act2 + w.lin + w.attn;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_name(tp_status s) {
+    switch (s) {
+        case TP_OK: return "TP_OK";
+        case TP_ERR_NULL: return "TP_ERR_NULL";
+        case TP_ERR_SHAPE: return "TP_ERR_SHAPE";
+        case TP_ERR_INDIVISIBLE: return "TP_ERR_INDIVISIBLE";
+        case TP_ERR_RANK: return "TP_ERR_RANK";
+        case TP_ERR_DTYPE: return "TP_ERR_DTYPE";
+        case TP_ERR_ALIGN: return "TP_ERR_ALIGN";
+        case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+        case TP_ERR_KV: return "TP_ERR_KV";
+        case TP_ERR_ALIAS: return "TP_ERR_ALIAS";
+        case TP_ERR_HIP: return "TP_ERR_HIP";
+    }
+    return "TP_ERR_UNKNOWN";
+}
+
+const char* tp_last_error(void) { return g_err.c_str(); }
+
+tp_status tp_shard_plan(const tp_model_desc* desc, int32_t t, int32_t rank, tp_rank_plan* out) {
+    return plan_impl(desc, t, rank, out);
+}
+
+size_t tp_linear_workspace_bytes(int64_t m, int64_t k, int64_t n, tp_dtype dtype, int32_t flags) {
+    if (m < 1 || k < 1 || n < 1 || (dtype != TP_F32 && dtype != TP_BF16)) return 0;
+    const int epi = (flags & TP_LINEAR_SWIGLU) ? tpk::EPI_SWIGLU : tpk::EPI_STORE;
+    const size_t a = linear_ws(m, k, n, dtype, epi, (flags & TP_LINEAR_NORM) != 0);
+    const size_t b = linear_ws(m, k, n, dtype, tpk::EPI_PARTIAL, false);
+    return a > b ? a : b;
+}
+
+tp_status tp_column_linear(const void* x, const void* w, const void* w_up, const void* gamma, float eps, void* y,
+                           int64_t m, int64_t k, int64_t n, tp_dtype dtype, void* ws, size_t ws_bytes,
+                           void* stream) {
+    TRY(check_dtype(dtype));
+    TRY(check_ptr(x, "x"));
+    TRY(check_ptr(w, "w"));
+    TRY(check_ptr(y, "y"));
+    if (w_up) TRY(check_ptr(w_up, "w_up"));
+    if (gamma) TRY(check_ptr(gamma, "gamma"));
+    TRY(check_dims(m, k, n));
+    if (k % (int64_t)vec_elems(dtype))
+        return fail(TP_ERR_ALIGN, "k=%lld is not a multiple of %zu (rows are read in 128-bit vectors)",
+                    (long long)k, vec_elems(dtype));
+    if (!(eps >= 0.0f)) return fail(TP_ERR_SHAPE, "eps must be >= 0");
+    const size_t es = esize(dtype);
+    const size_t ny = (size_t)m * n * es;
+    if (overlaps(y, ny, x, (size_t)m * k * es) || overlaps(y, ny, w, (size_t)n * k * es) ||
+        overlaps(y, ny, w_up, (size_t)n * k * es) || overlaps(y, ny, gamma, (size_t)k * es))
+        return fail(TP_ERR_ALIAS, "y overlaps an input; use a separate output buffer");
+    if (ws && overlaps(ws, ws_bytes, y, ny)) return fail(TP_ERR_ALIAS, "workspace overlaps y");
+    const int epi = w_up ? tpk::EPI_SWIGLU : tpk::EPI_STORE;
+    return run_linear(x, w, w_up, gamma, eps, y, m, k, n, dtype, epi, ws, ws_bytes, (hipStream_t)stream);
+}
+
+tp_status tp_row_linear_partial(const void* a, const void* w, float* partial, int64_t m, int64_t k, int64_t n,
+                                tp_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_dtype(dtype));
+    TRY(check_ptr(a, "a"));
+    TRY(check_ptr(w, "w"));
+    TRY(check_ptr(partial, "partial"));
+    TRY(check_dims(m, k, n));
+    if (k % (int64_t)vec_elems(dtype))
+        return fail(TP_ERR_ALIGN, "k=%lld is not a multiple of %zu (rows are read in 128-bit vectors)",
+                    (long long)k, vec_elems(dtype));
+    const size_t es = esize(dtype);
+    const size_t np = (size_t)m * n * 4;
+    if (overlaps(partial, np, a, (size_t)m * k * es) || overlaps(partial, np, w, (size_t)n * k * es))
+        return fail(TP_ERR_ALIAS, "partial overlaps an input");
+    if (ws && overlaps(ws, ws_bytes, partial, np)) return fail(TP_ERR_ALIAS, "workspace overlaps partial");
+    return run_linear(a, w, nullptr, nullptr, 0.f, partial, m, k, n, dtype, tpk::EPI_PARTIAL, ws, ws_bytes,
+                      (hipStream_t)stream);
+}
+
+tp_status tp_swiglu(const void* gate, const void* up, void* out, int64_t m, int64_t n, tp_dtype dtype,
+                    void* stream) {
+    TRY(check_dtype(dtype));
+    TRY(check_ptr(gate, "gate"));
+    TRY(check_ptr(up, "up"));
+    TRY(check_ptr(out, "out"));
+    TRY(check_dims(m, 1, n));
+    const size_t nb = (size_t)m * n * esize(dtype);
+    if ((out != gate && overlaps(out, nb, gate, nb)) || (out != up && overlaps(out, nb, up, nb)))
+        return fail(TP_ERR_ALIAS, "out partially overlaps gate or up (only exact in-place is allowed)");
+    hipError_t e = tpk::swiglu_launch(gate, up, out, m * n, dtype == TP_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "SwiGLU launch");
+    return ok();
+}
+
+tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* residual, void* out, int64_t m,
+                         int64_t n, tp_dtype out_dtype, void* stream) {
+    TRY(check_dtype(out_dtype));
+    if (!partials) return fail(TP_ERR_NULL, "partials is NULL");
+    if (t < 1 || t > 8) return fail(TP_ERR_RANK, "t=%d outside 1..8", t);
+    TRY(check_ptr(out, "out"));
+    if (residual) TRY(check_ptr(residual, "residual"));
+    TRY(check_dims(m, 1, n));
+    tpk::PartialPtrs ps{};
+    const size_t np = (size_t)m * n * 4;
+    const size_t no = (size_t)m * n * esize(out_dtype);
+    for (int r = 0; r < t; ++r) {
+        char name[32];
+        snprintf(name, sizeof name, "partials[%d]", r);
+        TRY(check_ptr(partials[r], name));
+        if (overlaps(out, no, partials[r], np)) return fail(TP_ERR_ALIAS, "out overlaps %s", name);
+        ps.p[r] = partials[r];
+    }
+    if (residual && residual != out && overlaps(out, no, residual, no))
+        return fail(TP_ERR_ALIAS, "out partially overlaps residual (only exact in-place is allowed)");
+    hipError_t e = tpk::partial_sum_launch(ps, t, residual, out, m * n, out_dtype == TP_BF16, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
+    return ok();
+}
+
+size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                                    int64_t kv_len) {
+    if (batch < 1 || q_heads < 1 || kv_heads < 1 || q_heads % kv_heads || kv_len < 1) return 0;
+    return round256(tpk::attn_plan((int)batch, q_heads, kv_heads, head_dim, (int)kv_len).ws_bytes);
+}
+
+static tp_status check_attention(const void* q, const void* k, const void* v, const void* out, int64_t batch,
+                                 int32_t q_heads, int32_t kv_heads, int32_t head_dim, int64_t capacity,
+                                 int64_t kv_len, tp_dtype dtype) {
+    if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "decode attention supports bf16 only");
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(out, "out"));
+    if (batch < 1 || batch > (1 << 20)) return fail(TP_ERR_SHAPE, "batch=%lld outside 1..2^20", (long long)batch);
+    if (q_heads < 1 || kv_heads < 1) return fail(TP_ERR_SHAPE, "q_heads and kv_heads must be >= 1");
+    if (q_heads % kv_heads) return fail(TP_ERR_INDIVISIBLE, "q_heads=%d not a multiple of kv_heads=%d", q_heads, kv_heads);
+    const int gq = q_heads / kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+        return fail(TP_ERR_SHAPE, "q_heads/kv_heads=%d must be 1, 2, 4, 8 or 16", gq);
+    if (head_dim != 64 && head_dim != 128) return fail(TP_ERR_SHAPE, "head_dim=%d must be 64 or 128", head_dim);
+    if (capacity < 1 || capacity > (int64_t(1) << 24)) return fail(TP_ERR_SHAPE, "capacity outside 1..2^24");
+    if (kv_len < 1 || kv_len > capacity)
+        return fail(TP_ERR_KV, "kv_len=%lld outside 1..capacity=%lld", (long long)kv_len, (long long)capacity);
+    if ((kv_len + 255) / 256 > 128LL * 1024) return fail(TP_ERR_KV, "kv_len too large");
+    const size_t no = (size_t)batch * q_heads * head_dim * 2;
+    const size_t nc = (size_t)batch * kv_heads * capacity * head_dim * 2;
+    if (overlaps(out, no, q, no) || overlaps(out, no, k, nc) || overlaps(out, no, v, nc))
+        return fail(TP_ERR_ALIAS, "out overlaps q or the caches");
+    return TP_OK;
+}
+
+tp_status tp_decode_attention(const void* q, const void* k, const void* v, void* out, int64_t batch, int32_t q_heads,
+                              int32_t kv_heads, int32_t head_dim, int64_t capacity, int64_t kv_len, tp_dtype dtype,
+                              void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_attention(q, k, v, out, batch, q_heads, kv_heads, head_dim, capacity, kv_len, dtype));
+    const tpk::AttnPlan p = tpk::attn_plan((int)batch, q_heads, kv_heads, head_dim, (int)kv_len);
+    TRY(check_ws(ws, ws_bytes, p.ws_bytes));
+    tpk::AttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.capacity = capacity; a.kv_len = (int)kv_len;
+    a.batch = (int)batch; a.q_heads = q_heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
+    hipError_t e = tpk::attn_launch(a, p, ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage, int64_t m,
+                                tp_dtype dtype) {
+    if (!desc || !plan || m < 1 || (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP)) return 0;
+    if (dtype != TP_F32 && dtype != TP_BF16) return 0;
+    if (stage == TP_STAGE_ATTN && (plan->q_heads < 1 || desc->seq_len < 1)) return 0;
+    if (stage == TP_STAGE_MLP && plan->inter_cols < 1) return 0;
+    return layer_ws(desc, plan, stage, m, dtype).total;
+}
+
+tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                                 const tp_rank_weights* wts, const void* in, const tp_kv_view* kv, float* partial,
+                                 int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_dtype(dtype));
+    TRY(check_plan(desc, plan));
+    if (!wts) return fail(TP_ERR_NULL, "weights is NULL");
+    if (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP) return fail(TP_ERR_SHAPE, "unknown stage %d", (int)stage);
+    TRY(check_ptr(in, "in"));
+    TRY(check_ptr(partial, "partial"));
+    const int64_t H = desc->hidden;
+    TRY(check_dims(m, H, H));
+    if (H % (int64_t)vec_elems(dtype))
+        return fail(TP_ERR_ALIGN, "hidden=%lld is not a multiple of %zu", (long long)H, vec_elems(dtype));
+    const size_t es = esize(dtype);
+    if (overlaps(partial, (size_t)m * H * 4, in, (size_t)m * H * es)) return fail(TP_ERR_ALIAS, "partial overlaps in");
+    hipStream_t s = (hipStream_t)stream;
+
+    if (stage == TP_STAGE_ATTN) {
+        if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "the attention stage supports bf16 only");
+        if (plan->q_heads < 1) return fail(TP_ERR_SHAPE, "desc has no attention heads");
+        if (!kv) return fail(TP_ERR_NULL, "kv is NULL for the attention stage");
+        TRY(check_ptr(wts->w_qkv, "weights->w_qkv"));
+        TRY(check_ptr(wts->w_o, "weights->w_o"));
+        if (wts->attn_norm) TRY(check_ptr(wts->attn_norm, "weights->attn_norm"));
+        if (plan->o_rows % 8) return fail(TP_ERR_ALIGN, "q_heads*head_dim=%lld not a multiple of 8", (long long)plan->o_rows);
+        TRY(check_ptr(kv->k, "kv->k"));
+        TRY(check_ptr(kv->v, "kv->v"));
+        const int gq = plan->q_heads / plan->kv_heads;
+        if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+            return fail(TP_ERR_SHAPE, "q heads per kv head = %d must be 1, 2, 4, 8 or 16", gq);
+        if (desc->head_dim != 64 && desc->head_dim != 128)
+            return fail(TP_ERR_SHAPE, "head_dim=%d must be 64 or 128", desc->head_dim);
+        if (m > (1 << 20)) return fail(TP_ERR_SHAPE, "batch m=%lld too large", (long long)m);
+        if (kv->capacity < 1 || kv->capacity > (int64_t(1) << 24))
+            return fail(TP_ERR_SHAPE, "kv capacity outside 1..2^24");
+        if (kv->kv_len < 1 || kv->kv_len > kv->capacity)
+            return fail(TP_ERR_KV, "kv_len=%lld outside 1..capacity=%lld", (long long)kv->kv_len,
+                        (long long)kv->capacity);
+        {
+            const size_t nc = (size_t)m * plan->kv_heads * kv->capacity * desc->head_dim * 2;
+            if (overlaps(kv->k, nc, kv->v, nc)) return fail(TP_ERR_ALIAS, "kv->k overlaps kv->v");
+            if (overlaps(kv->k, nc, in, (size_t)m * H * 2) || overlaps(kv->v, nc, in, (size_t)m * H * 2) ||
+                overlaps(kv->k, nc, partial, (size_t)m * H * 4) || overlaps(kv->v, nc, partial, (size_t)m * H * 4))
+                return fail(TP_ERR_ALIAS, "the KV cache overlaps in or partial");
+        }
+        if (kv->capacity != desc->seq_len)
+            return fail(TP_ERR_KV, "kv capacity %lld differs from desc seq_len %lld", (long long)kv->capacity,
+                        (long long)desc->seq_len);
+        const LayerWs L = layer_ws(desc, plan, stage, m, dtype);
+        TRY(check_ws(ws, ws_bytes, L.total));
+        char* b = reinterpret_cast<char*>(ws);
+        void* qbuf = b;
+        void* obuf = b + L.act1;
+        void* lin = b + L.act1 + L.act2;
+        void* aws = b + L.act1 + L.act2 + L.lin;
+        tpk::GemvArgs extra{};
+        extra.k_cache = kv->k;
+        extra.v_cache = kv->v;
+        extra.capacity = kv->capacity;
+        extra.pos = kv->kv_len - 1;
+        extra.q_cols = (int)plan->o_rows;
+        extra.kv_cols = plan->kv_heads * desc->head_dim;
+        extra.head_dim = desc->head_dim;
+        extra.kv_heads = plan->kv_heads;
+        TRY(run_linear(in, wts->w_qkv, nullptr, wts->attn_norm, desc->eps, qbuf, m, H, plan->qkv_cols, dtype,
+                       tpk::EPI_QKV, lin, L.lin, s, &extra));
+        tpk::AttnArgs a{};
+        a.q = qbuf; a.k = kv->k; a.v = kv->v; a.out = obuf;
+        a.capacity = kv->capacity; a.kv_len = (int)kv->kv_len;
+        a.batch = (int)m; a.q_heads = plan->q_heads; a.kv_heads = plan->kv_heads; a.head_dim = desc->head_dim;
+        const tpk::AttnPlan ap = tpk::attn_plan(a.batch, a.q_heads, a.kv_heads, a.head_dim, (int)desc->seq_len);
+        const tpk::AttnPlan ap_len = tpk::attn_plan(a.batch, a.q_heads, a.kv_heads, a.head_dim, a.kv_len);
+        if (ap_len.ws_bytes > ap.ws_bytes) return fail(TP_ERR_WORKSPACE, "attention workspace too small");
+        hipError_t e = tpk::attn_launch(a, ap_len, aws, s);
+        if (e != hipSuccess) return hip_fail(e, "attention launch");
+        return run_linear(obuf, wts->w_o, nullptr, nullptr, 0.f, partial, m, plan->o_rows, H, dtype,
+                          tpk::EPI_PARTIAL, lin, L.lin, s);
+    }
+
+    if (plan->inter_cols < 1) return fail(TP_ERR_SHAPE, "desc has no MLP");
+    TRY(check_ptr(wts->w_gate, "weights->w_gate"));
+    TRY(check_ptr(wts->w_up, "weights->w_up"));
+    TRY(check_ptr(wts->w_down, "weights->w_down"));
+    if (wts->mlp_norm) TRY(check_ptr(wts->mlp_norm, "weights->mlp_norm"));
+    if (plan->inter_cols % (int64_t)vec_elems(dtype))
+        return fail(TP_ERR_ALIGN, "inter_cols=%lld not a multiple of %zu", (long long)plan->inter_cols, vec_elems(dtype));
+    const LayerWs L = layer_ws(desc, plan, stage, m, dtype);
+    TRY(check_ws(ws, ws_bytes, L.total));
+    char* b = reinterpret_cast<char*>(ws);
+    void* abuf = b;
+    void* lin = b + L.act1;
+    TRY(run_linear(in, wts->w_gate, wts->w_up, wts->mlp_norm, desc->eps, abuf, m, H, plan->inter_cols, dtype,
+                   tpk::EPI_SWIGLU, lin, L.lin, s));
+    return run_linear(abuf, wts->w_down, nullptr, nullptr, 0.f, partial, m, plan->inter_cols, H, dtype,
+                      tpk::EPI_PARTIAL, lin, L.lin, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Bandwidth-bound elementwise kernels: the on-device sum of the t row-parallel
+// partials (the value the all-reduce returns), standalone SwiGLU, and the
+// row-wise RMSNorm used in front of the prefill GEMM. All use 128-bit loads
+// and grid-stride loops sized to a few workgroups per compute unit.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+constexpr int EW_THREADS = 256;
+
+static int ew_blocks(int64_t items) {
+    int64_t b = (items + EW_THREADS - 1) / EW_THREADS;
+    if (b > 256 * 8) b = 256 * 8;
+    if (b < 1) b = 1;
+    return (int)b;
+}
+
+// Sum of partials: each thread handles 4 float32 per partial (one 128-bit load
+// from each), added in rank order, then the residual.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(EW_THREADS) void partial_sum_kernel(PartialPtrs ps, int t, const void* residual,
+                                                                 void* out, int64_t count) {
+    const int64_t n4 = count / 4;
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n4; i += stride) {
+        float4 acc = reinterpret_cast<const float4*>(ps.p[0])[i];
+        for (int r = 1; r < t; ++r) {
+            const float4 v = reinterpret_cast<const float4*>(ps.p[r])[i];
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        if (OUT_BF16) {
+            if (residual) {
+                const uint2 rv = reinterpret_cast<const uint2*>(residual)[i];
+                acc.x += bf16lo(rv.x); acc.y += bf16hi(rv.x); acc.z += bf16lo(rv.y); acc.w += bf16hi(rv.y);
+            }
+            uint2 o;
+            o.x = pack_bf16x2(acc.x, acc.y);
+            o.y = pack_bf16x2(acc.z, acc.w);
+            reinterpret_cast<uint2*>(out)[i] = o;
+        } else {
+            if (residual) {
+                const float4 rv = reinterpret_cast<const float4*>(residual)[i];
+                acc.x += rv.x; acc.y += rv.y; acc.z += rv.z; acc.w += rv.w;
+            }
+            reinterpret_cast<float4*>(out)[i] = acc;
+        }
+    }
+    // tail (count not a multiple of 4)
+    const int64_t tail0 = n4 * 4;
+    for (int64_t i = tail0 + (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < count; i += stride) {
+        float acc = ps.p[0][i];
+        for (int r = 1; r < t; ++r) acc += ps.p[r][i];
+        if (OUT_BF16) {
+            if (residual) acc += bf16_to_f32(reinterpret_cast<const uint16_t*>(residual)[i]);
+            reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(acc);
+        } else {
+            if (residual) acc += reinterpret_cast<const float*>(residual)[i];
+            reinterpret_cast<float*>(out)[i] = acc;
+        }
+    }
+}
+
+hipError_t partial_sum_launch(const PartialPtrs& ps, int t, const void* residual, void* out, int64_t count,
+                              int out_bf16, hipStream_t s) {
+    const int blocks = ew_blocks((count + 3) / 4);
+    if (out_bf16)
+        hipLaunchKernelGGL(partial_sum_kernel<true>, dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
+    else
+        hipLaunchKernelGGL(partial_sum_kernel<false>, dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
+    return hipGetLastError();
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(EW_THREADS) void swiglu_kernel(const void* gate, const void* up, void* out,
+                                                            int64_t count) {
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+    if (BF16) {
+        const int64_t n8 = count / 8;
+        for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n8; i += stride) {
+            const uint4 g = reinterpret_cast<const uint4*>(gate)[i];
+            const uint4 u = reinterpret_cast<const uint4*>(up)[i];
+            const uint32_t* gp = &g.x;
+            const uint32_t* up_ = &u.x;
+            uint4 o;
+            uint32_t* op = &o.x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                op[j] = pack_bf16x2(silu_f32(bf16lo(gp[j])) * bf16lo(up_[j]), silu_f32(bf16hi(gp[j])) * bf16hi(up_[j]));
+            reinterpret_cast<uint4*>(out)[i] = o;
+        }
+        for (int64_t i = n8 * 8 + (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < count; i += stride) {
+            const float g = bf16_to_f32(reinterpret_cast<const uint16_t*>(gate)[i]);
+            const float u = bf16_to_f32(reinterpret_cast<const uint16_t*>(up)[i]);
+            reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+        }
+    } else {
+        const int64_t n4 = count / 4;
+        for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n4; i += stride) {
+            const float4 g = reinterpret_cast<const float4*>(gate)[i];
+            const float4 u = reinterpret_cast<const float4*>(up)[i];
+            float4 o;
+            o.x = silu_f32(g.x) * u.x; o.y = silu_f32(g.y) * u.y;
+            o.z = silu_f32(g.z) * u.z; o.w = silu_f32(g.w) * u.w;
+            reinterpret_cast<float4*>(out)[i] = o;
+        }
+        for (int64_t i = n4 * 4 + (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < count; i += stride) {
+            const float g = reinterpret_cast<const float*>(gate)[i];
+            reinterpret_cast<float*>(out)[i] = silu_f32(g) * reinterpret_cast<const float*>(up)[i];
+        }
+    }
+}
+
+hipError_t swiglu_launch(const void* gate, const void* up, void* out, int64_t count, int is_bf16, hipStream_t s) {
+    const int blocks = ew_blocks((count + 7) / 8);
+    if (is_bf16)
+        hipLaunchKernelGGL(swiglu_kernel<true>, dim3(blocks), dim3(EW_THREADS), 0, s, gate, up, out, count);
+    else
+        hipLaunchKernelGGL(swiglu_kernel<false>, dim3(blocks), dim3(EW_THREADS), 0, s, gate, up, out, count);
+    return hipGetLastError();
+}
+
+// One workgroup per row: sum of squares, then u = x * gamma * inv_rms.
+template <bool BF16>
+__global__ __launch_bounds__(EW_THREADS) void rmsnorm_kernel(const void* x, const void* gamma, void* u, int K,
+                                                             float eps) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int row = blockIdx.x;
+    const int nv = K / VEC;
+    __shared__ float wsum[EW_THREADS / 64];
+    const uint4* xr = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(x) + (size_t)row * K * (BF16 ? 2 : 4));
+    const uint4* gr = reinterpret_cast<const uint4*>(gamma);
+    uint4* ur = reinterpret_cast<uint4*>(reinterpret_cast<char*>(u) + (size_t)row * K * (BF16 ? 2 : 4));
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < nv; c += EW_THREADS) {
+        const uint4 v = xr[c];
+        const uint32_t* p = &v.x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (BF16) {
+                const float a = bf16lo(p[j]), b = bf16hi(p[j]);
+                ss = fmaf(a, a, ss); ss = fmaf(b, b, ss);
+            } else {
+                const float a = __uint_as_float(p[j]);
+                ss = fmaf(a, a, ss);
+            }
+        }
+    }
+    ss = group_sum<64>(ss);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < EW_THREADS / 64; ++w) tot += wsum[w];
+    const float inv = 1.0f / sqrtf(tot / (float)K + eps);
+    for (int c = threadIdx.x; c < nv; c += EW_THREADS) {
+        const uint4 v = xr[c];
+        const uint4 g = gr[c];
+        const uint32_t* p = &v.x;
+        const uint32_t* q = &g.x;
+        uint4 o;
+        uint32_t* op = &o.x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (BF16) {
+                op[j] = pack_bf16x2(bf16lo(p[j]) * inv * bf16lo(q[j]), bf16hi(p[j]) * inv * bf16hi(q[j]));
+            } else {
+                op[j] = __float_as_uint(__uint_as_float(p[j]) * inv * __uint_as_float(q[j]));
+            }
+        }
+        ur[c] = o;
+    }
+}
+
+hipError_t rmsnorm_launch(const void* x, const void* gamma, void* u, int m, int K, float eps, int is_bf16,
+                          hipStream_t s) {
+    if (is_bf16)
+        hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3(m), dim3(EW_THREADS), 0, s, x, gamma, u, K, eps);
+    else
+        hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3(m), dim3(EW_THREADS), 0, s, x, gamma, u, K, eps);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

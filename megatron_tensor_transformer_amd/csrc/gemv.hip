@@ -1,0 +1,400 @@
+// Thin-M projections for decode on gfx950: column-parallel (optionally with
+// fused RMSNorm, SwiGLU or KV-cache append) and row-parallel partials.
+//
+// Decode reads each weight byte once and does M multiply-adds with it, so the
+// kernel is bound by HBM for small M and close to the VALU limit at M = 16.
+// Layout of the work:
+//  - A workgroup (NW waves) owns a tile of weight rows and one K chunk. The
+//    activation chunk [MT, kc] is staged in LDS once per workgroup (gamma
+//    folded in when RMSNorm is fused) and reused by every row of the tile.
+//  - A wave is split into 64/G groups of G lanes; a group walks one weight row
+//    with 128-bit loads, so each load instruction reads 64/G rows x G*16
+//    contiguous bytes. Each lane handles RWG rows, keeping RWG x MT float32
+//    accumulators; the activation vector read from LDS is shared by those rows.
+//  - bf16 products use v_dot2 (two multiply-adds per lane per instruction,
+//    float32 accumulation, no unpacking); float32 inputs use fma.
+//  - The G lanes of a group are reduced by a fixed butterfly; results go
+//    through a small LDS tile so the epilogue writes outputs in coalesced
+//    order.
+//  - When K is split over S workgroups, each writes its float32 tile to the
+//    workspace and bumps a per-tile counter; the last to arrive sums the S
+//    slices in split order (deterministic) and runs the epilogue, then resets
+//    the counter. RMSNorm's sum of squares travels the same way, so the
+//    normalisation stays fused: inv_rms multiplies the contraction result.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+constexpr int GEMV_G = 16;     // lanes per weight row
+constexpr int GEMV_NW = 4;     // waves per workgroup
+constexpr size_t GEMV_X_LDS = 64 * 1024;   // LDS budget for the staged activation chunk
+
+template <int MT> struct RowsPerLane { static constexpr int v = MT >= 8 ? 4 : 2; };
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> { static constexpr int vec = 8; };
+template <> struct Elem<float> { static constexpr int vec = 4; };
+
+// acc[m] += dot(w, x) over one 128-bit vector.
+__device__ __forceinline__ float vdot(const uint4& w, const uint4& x, float acc, uint16_t*) {
+    acc = dot2_bf16(w.x, x.x, acc);
+    acc = dot2_bf16(w.y, x.y, acc);
+    acc = dot2_bf16(w.z, x.z, acc);
+    acc = dot2_bf16(w.w, x.w, acc);
+    return acc;
+}
+__device__ __forceinline__ float vdot(const uint4& w, const uint4& x, float acc, float*) {
+    acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+    acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+    acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+    acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+    return acc;
+}
+
+// Sum of squares of a vector and the vector scaled by gamma (rounded back to T).
+__device__ __forceinline__ float vsumsq(const uint4& v, uint16_t*) {
+    float s = 0.f;
+    const uint32_t* p = &v.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float a = bf16lo(p[i]), b = bf16hi(p[i]);
+        s = fmaf(a, a, s);
+        s = fmaf(b, b, s);
+    }
+    return s;
+}
+__device__ __forceinline__ float vsumsq(const uint4& v, float*) {
+    const uint32_t* p = &v.x;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(p[i]), __uint_as_float(p[i]), s);
+    return s;
+}
+__device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, uint16_t*) {
+    uint4 r;
+    const uint32_t* a = &v.x;
+    const uint32_t* b = &g.x;
+    uint32_t* o = &r.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16lo(a[i]) * bf16lo(b[i]), bf16hi(a[i]) * bf16hi(b[i]));
+    return r;
+}
+__device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, float*) {
+    uint4 r;
+    r.x = __float_as_uint(__uint_as_float(v.x) * __uint_as_float(g.x));
+    r.y = __float_as_uint(__uint_as_float(v.y) * __uint_as_float(g.y));
+    r.z = __float_as_uint(__uint_as_float(v.z) * __uint_as_float(g.z));
+    r.w = __float_as_uint(__uint_as_float(v.w) * __uint_as_float(g.w));
+    return r;
+}
+
+__device__ __forceinline__ void store_out(void* y, size_t idx, float v, uint16_t*) {
+    reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
+}
+__device__ __forceinline__ void store_out(void* y, size_t idx, float v, float*) {
+    reinterpret_cast<float*>(y)[idx] = v;
+}
+
+struct GemvDev {
+    GemvArgs a;
+    int kc, splits, n_tiles;
+    float* part;       // [tiles*mblocks][S][MT*RPT]
+    float* ssq;        // [tiles*mblocks][S][MT]
+    unsigned* cnt;     // [tiles*mblocks]
+};
+
+template <typename T, int MT, int EPI, bool NORM>
+__global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
+    constexpr int G = GEMV_G;
+    constexpr int NW = GEMV_NW;
+    constexpr int NT = NW * 64;
+    constexpr int VEC = Elem<T>::vec;
+    constexpr int RWG = RowsPerLane<MT>::v;
+    constexpr int GROUPS = 64 / G;
+    constexpr int RPW = GROUPS * RWG;
+    constexpr int RPT = NW * RPW;
+    constexpr bool SWI = (EPI == EPI_SWIGLU);
+    constexpr int HALF = RPT / 2;
+    constexpr int OUTS = SWI ? HALF : RPT;
+    constexpr int STEP = G * VEC;   // K elements one group covers per step
+
+    const GemvArgs& a = d.a;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int kc = d.kc;
+    T* xs = reinterpret_cast<T*>(smem);
+    float* res = reinterpret_cast<float*>(smem + (size_t)MT * kc * sizeof(T));
+    float* ssl = res + MT * RPT;
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane / G, sub = lane % G;
+    const int tile = blockIdx.x, split = blockIdx.y, mb = blockIdx.z;
+    const int K = a.K, N = a.N;
+    const int k0 = split * kc;
+    const int klen = min(kc, K - k0);
+    const int m0 = mb * MT;
+    const int mvalid = min(MT, a.m - m0);
+
+    // Weight rows of this lane. Rows past N are clamped to a valid row; their
+    // results are never stored.
+    const T* wrow[RWG];
+#pragma unroll
+    for (int rg = 0; rg < RWG; ++rg) {
+        const int rho = wave * RPW + rg * GROUPS + grp;
+        int n;
+        const T* base;
+        if (SWI) {
+            n = tile * HALF + (rho < HALF ? rho : rho - HALF);
+            base = reinterpret_cast<const T*>(rho < HALF ? a.w : a.w_up);
+        } else {
+            n = tile * RPT + rho;
+            base = reinterpret_cast<const T*>(a.w);
+        }
+        n = min(n, N - 1);
+        wrow[rg] = base + (size_t)n * K + k0;
+    }
+    const int steps = (klen + STEP - 1) / STEP;
+
+    auto load_w = [&](uint4* dst, int j) {
+        const int k = (j * G + sub) * VEC;
+#pragma unroll
+        for (int rg = 0; rg < RWG; ++rg) {
+            dst[rg] = (k < klen) ? load_stream_u4(wrow[rg] + k) : make_uint4(0, 0, 0, 0);
+        }
+    };
+
+    // Issue the first weight loads before staging the activations: they do
+    // not depend on them, so their latency overlaps the staging.
+    uint4 wa[RWG], wb[RWG];
+    load_w(wa, 0);
+
+    // Stage the activation chunk (times gamma) and its sum of squares.
+    const T* x = reinterpret_cast<const T*>(a.x);
+    const T* gam = reinterpret_cast<const T*>(a.gamma);
+    for (int mm = wave; mm < MT; mm += NW) {
+        float ss = 0.f;
+        for (int c = lane; c < kc / VEC; c += 64) {
+            const int k = c * VEC;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (mm < mvalid && k < klen) {
+                v = load_u4(x + (size_t)(m0 + mm) * K + k0 + k);
+                if (NORM) {
+                    ss += vsumsq(v, (T*)nullptr);
+                    v = vscale(v, load_u4(gam + k0 + k), (T*)nullptr);
+                }
+            }
+            *reinterpret_cast<uint4*>(xs + (size_t)mm * kc + k) = v;
+        }
+        if (NORM) {
+            ss = group_sum<64>(ss);
+            if (lane == 0) ssl[mm] = ss;
+        }
+    }
+    __syncthreads();
+
+    float acc[RWG][MT];
+#pragma unroll
+    for (int rg = 0; rg < RWG; ++rg)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[rg][m] = 0.f;
+
+    auto compute = [&](const uint4* wv, int j) {
+        const int k = (j * G + sub) * VEC;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * kc + k);
+#pragma unroll
+            for (int rg = 0; rg < RWG; ++rg) acc[rg][m] = vdot(wv[rg], xv, acc[rg][m], (T*)nullptr);
+        }
+    };
+
+    for (int j = 0; j < steps; j += 2) {
+        if (j + 1 < steps) load_w(wb, j + 1);
+        compute(wa, j);
+        if (j + 1 < steps) {
+            if (j + 2 < steps) load_w(wa, j + 2);
+            compute(wb, j + 1);
+        }
+    }
+
+    // Reduce each row over its G lanes; lanes share out the stores.
+#pragma unroll
+    for (int rg = 0; rg < RWG; ++rg) {
+        const int rho = wave * RPW + rg * GROUPS + grp;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const float v = group_sum<G>(acc[rg][m]);
+            if (((rg * MT + m) % G) == sub) res[m * RPT + rho] = v;
+        }
+    }
+    __syncthreads();
+
+    const int tile_id = mb * d.n_tiles + tile;
+    if (d.splits > 1) {
+        float* base = d.part + (size_t)tile_id * d.splits * (MT * RPT);
+        float* mine = base + (size_t)split * (MT * RPT);
+        for (int i = tid; i < MT * RPT; i += NT) mine[i] = res[i];
+        if (NORM && tid < MT) d.ssq[((size_t)tile_id * d.splits + split) * MT + tid] = ssl[tid];
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = (atomicAdd(&d.cnt[tile_id], 1u) == (unsigned)(d.splits - 1));
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        for (int i = tid; i < MT * RPT; i += NT) {
+            float v = 0.f;
+            for (int s = 0; s < d.splits; ++s) v += base[(size_t)s * (MT * RPT) + i];
+            res[i] = v;
+        }
+        if (NORM && tid < MT) {
+            float v = 0.f;
+            for (int s = 0; s < d.splits; ++s) v += d.ssq[((size_t)tile_id * d.splits + s) * MT + tid];
+            ssl[tid] = v;
+        }
+        if (tid == 0) atomicExch(&d.cnt[tile_id], 0u);
+        __syncthreads();
+    }
+
+    // Epilogue.
+    for (int i = tid; i < mvalid * OUTS; i += NT) {
+        const int m = i / OUTS, o = i - m * OUTS;
+        const float inv = NORM ? 1.0f / sqrtf(ssl[m] / (float)K + a.eps) : 1.0f;
+        const int row = m0 + m;
+        if (SWI) {
+            const int n = tile * HALF + o;
+            if (n < N) {
+                const float g = res[m * RPT + o] * inv;
+                const float u = res[m * RPT + HALF + o] * inv;
+                store_out(a.y, (size_t)row * N + n, silu_f32(g) * u, (T*)nullptr);
+            }
+        } else {
+            const int n = tile * RPT + o;
+            if (n >= N) continue;
+            const float v = res[m * RPT + o] * inv;
+            if (EPI == EPI_PARTIAL) {
+                reinterpret_cast<float*>(a.y)[(size_t)row * N + n] = v;
+            } else if (EPI == EPI_STORE) {
+                store_out(a.y, (size_t)row * N + n, v, (T*)nullptr);
+            } else {  // EPI_QKV
+                if (n < a.q_cols) {
+                    store_out(a.y, (size_t)row * a.q_cols + n, v, (T*)nullptr);
+                } else {
+                    const int r = n - a.q_cols;
+                    const bool is_k = r < a.kv_cols;
+                    const int rr = is_k ? r : r - a.kv_cols;
+                    const int g = rr / a.head_dim, e = rr - g * a.head_dim;
+                    const size_t idx = (((size_t)row * a.kv_heads + g) * a.capacity + a.pos) * a.head_dim + e;
+                    store_out(is_k ? a.k_cache : a.v_cache, idx, v, (T*)nullptr);
+                }
+            }
+        }
+    }
+}
+
+static int rows_per_tile(int mt) { return GEMV_NW * (64 / GEMV_G) * (mt >= 8 ? 4 : 2); }
+
+GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
+    GemvPlan p{};
+    p.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
+    if (!is_bf16 && p.mt != 1 && p.mt != 4) p.mt = (m <= 4) ? 4 : 16;
+    p.mblocks = (m + p.mt - 1) / p.mt;
+    p.rows_per_tile = rows_per_tile(p.mt);
+    p.out_per_tile = (epi == EPI_SWIGLU) ? p.rows_per_tile / 2 : p.rows_per_tile;
+    p.n_tiles = (N + p.out_per_tile - 1) / p.out_per_tile;
+    const int esz = is_bf16 ? 2 : 4;
+    const int step = GEMV_G * (16 / esz);
+    const int kround = (K + step - 1) / step * step;
+    int kc_max = (int)(GEMV_X_LDS / ((size_t)p.mt * esz)) / step * step;
+    if (kc_max > kround) kc_max = kround;
+    int S = (kround + kc_max - 1) / kc_max;
+    // Split K further until the grid covers the 256 compute units about twice,
+    // keeping at least 4 steps per group.
+    const int target = 512;
+    while ((long)p.n_tiles * S * p.mblocks < target) {
+        const int kc_next = ((kround + S) / (S + 1) + step - 1) / step * step;
+        if (kc_next < 4 * step) break;
+        ++S;
+    }
+    int kc = ((kround + S - 1) / S + step - 1) / step * step;
+    S = (K + kc - 1) / kc;
+    p.kc = kc;
+    p.splits = S;
+    p.threads = GEMV_NW * 64;
+    p.lds_bytes = (size_t)p.mt * kc * esz + (size_t)p.mt * p.rows_per_tile * 4 + (size_t)p.mt * 4;
+    if (S > 1) {
+        const size_t tiles = (size_t)p.n_tiles * p.mblocks;
+        const size_t cnt = (tiles * 4 + 255) / 256 * 256;
+        const size_t part = tiles * S * p.mt * p.rows_per_tile * 4;
+        const size_t ssq = tiles * S * p.mt * 4;
+        p.ws_bytes = cnt + (part + 255) / 256 * 256 + (ssq + 255) / 256 * 256;
+    } else {
+        p.ws_bytes = 0;
+    }
+    return p;
+}
+
+template <typename T, int MT, int EPI, bool NORM>
+static hipError_t launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
+    auto kern = gemv_kernel<T, MT, EPI, NORM>;
+    // Raise the dynamic LDS limit once per instantiation (outside any graph capture
+    // in practice: the first call of a shape is an eager one).
+    static bool lds_raised = false;
+    if (p.lds_bytes > 64 * 1024 && !lds_raised) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        lds_raised = true;
+    }
+    dim3 grid(p.n_tiles, p.splits, p.mblocks);
+    hipLaunchKernelGGL(kern, grid, dim3(p.threads), p.lds_bytes, s, d);
+    return hipGetLastError();
+}
+
+template <typename T, int MT>
+static hipError_t launch_epi(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
+    const bool nrm = d.a.norm != 0;
+    switch (d.a.epi) {
+        case EPI_STORE: return nrm ? launch_t<T, MT, EPI_STORE, true>(d, p, s) : launch_t<T, MT, EPI_STORE, false>(d, p, s);
+        case EPI_PARTIAL: return launch_t<T, MT, EPI_PARTIAL, false>(d, p, s);
+        case EPI_SWIGLU: return nrm ? launch_t<T, MT, EPI_SWIGLU, true>(d, p, s) : launch_t<T, MT, EPI_SWIGLU, false>(d, p, s);
+        case EPI_QKV: return nrm ? launch_t<T, MT, EPI_QKV, true>(d, p, s) : launch_t<T, MT, EPI_QKV, false>(d, p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, void* ws, hipStream_t s) {
+    GemvDev d{};
+    d.a = a;
+    d.kc = p.kc;
+    d.splits = p.splits;
+    d.n_tiles = p.n_tiles;
+    if (p.splits > 1) {
+        const size_t tiles = (size_t)p.n_tiles * p.mblocks;
+        char* b = reinterpret_cast<char*>(ws);
+        const size_t cnt = (tiles * 4 + 255) / 256 * 256;
+        const size_t part = (tiles * p.splits * p.mt * p.rows_per_tile * 4 + 255) / 256 * 256;
+        d.cnt = reinterpret_cast<unsigned*>(b);
+        d.part = reinterpret_cast<float*>(b + cnt);
+        d.ssq = reinterpret_cast<float*>(b + cnt + part);
+    }
+    if (a.is_bf16) {
+        switch (p.mt) {
+            case 1: return launch_epi<uint16_t, 1>(d, p, s);
+            case 2: return launch_epi<uint16_t, 2>(d, p, s);
+            case 4: return launch_epi<uint16_t, 4>(d, p, s);
+            case 8: return launch_epi<uint16_t, 8>(d, p, s);
+            case 16: return launch_epi<uint16_t, 16>(d, p, s);
+        }
+    } else {
+        if (a.epi == EPI_QKV) return hipErrorInvalidValue;
+        switch (p.mt) {
+            case 1: return launch_epi<float, 1>(d, p, s);
+            case 4: return launch_epi<float, 4>(d, p, s);
+            case 16: return launch_epi<float, 16>(d, p, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tpk

@@ -1,0 +1,96 @@
+// Launch interface between the C-ABI host code (api.cpp) and the HIP kernels.
+// Host-side only types: no device code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpk {
+
+enum Epilogue : int {
+    EPI_STORE = 0,    // y[m, n] in the input dtype (column projection)
+    EPI_PARTIAL = 1,  // y[m, n] float32 (row-parallel partial)
+    EPI_SWIGLU = 2,   // y[m, n] = silu(gate) * up in the input dtype
+    EPI_QKV = 3       // q -> y, new k/v -> cache position (decode attention block)
+};
+
+// Thin-M projection (decode): y = epilogue(u @ W^T), u = optional RMSNorm(x).
+struct GemvArgs {
+    const void* x;      // [m, K]
+    const void* w;      // [N, K] (gate rows for EPI_SWIGLU)
+    const void* w_up;   // [N, K] for EPI_SWIGLU
+    const void* gamma;  // [K] or null
+    void* y;            // output
+    void* k_cache;      // EPI_QKV: [m, kv_heads, capacity, d]
+    void* v_cache;
+    int64_t capacity;
+    int64_t pos;        // cache position written (kv_len - 1)
+    int q_cols, kv_cols, head_dim, kv_heads;
+    int m, K, N;        // N: output columns
+    float eps;
+    int is_bf16;
+    int epi;
+    int norm;
+};
+
+struct GemvPlan {
+    int mt;        // tokens per block (1, 2, 4, 8, 16)
+    int mblocks;   // ceil(m / mt)
+    int rows_per_tile;  // weight rows a workgroup covers
+    int out_per_tile;   // outputs a workgroup covers
+    int n_tiles;
+    int kc;        // K elements per split
+    int splits;    // S
+    int threads;
+    size_t lds_bytes;
+    size_t ws_bytes;   // 0 when splits == 1
+};
+
+GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi);
+hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, void* ws, hipStream_t stream);
+
+// Row-wise RMSNorm into a bf16/f32 buffer: u = x * gamma / sqrt(mean(x^2) + eps).
+hipError_t rmsnorm_launch(const void* x, const void* gamma, void* u, int m, int K, float eps, int is_bf16,
+                          hipStream_t stream);
+
+// out = silu(gate) * up, elementwise.
+hipError_t swiglu_launch(const void* gate, const void* up, void* out, int64_t count, int is_bf16,
+                         hipStream_t stream);
+
+// out = sum_r partials[r] (+ residual), rank order.
+struct PartialPtrs { const float* p[8]; };
+hipError_t partial_sum_launch(const PartialPtrs& ptrs, int t, const void* residual, void* out, int64_t count,
+                              int out_bf16, hipStream_t stream);
+
+// Split-KV grouped-query decode attention.
+struct AttnArgs {
+    const void* q;      // [B, q_heads * d]
+    const void* k;      // [B, kv_heads, capacity, d]
+    const void* v;
+    void* out;          // [B, q_heads * d]
+    int64_t capacity;
+    int kv_len;
+    int batch, q_heads, kv_heads, head_dim;
+};
+struct AttnPlan {
+    int chunk;      // keys per workgroup
+    int n_chunks;
+    size_t ws_bytes;
+};
+AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_len);
+hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t stream);
+
+// Prefill projection on bf16 MFMA: y = epilogue(x @ W^T) for large m.
+struct GemmArgs {
+    const void* x;      // [M, K] bf16
+    const void* w;      // [N, K] bf16 (gate rows for EPI_SWIGLU)
+    const void* w_up;   // [N, K] bf16 for EPI_SWIGLU
+    void* y;            // [M, N] bf16 (EPI_STORE, EPI_SWIGLU) or float32 (EPI_PARTIAL)
+    int M, N, K;
+    int epi;
+};
+bool gemm_supported(int M, int N, int K, int epi);
+hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace tpk

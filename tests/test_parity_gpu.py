@@ -1,0 +1,360 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Every workload is drawn by ``workloads`` (seeded, storage-rounded), sliced per
+rank on the GPU side with the library's own planner, run rank by rank on the
+one device, summed on device, and compared with the float64 oracle: max |err|
+/ max |ref| <= 1e-4 for float32 workloads and <= 2e-2 for bf16 workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import megatron_tensor_transformer_amd as tp
+import workloads as W
+from gpu_helpers import TOL, check, dev, host, phys, say
+from oracle import layer as L
+from oracle import sharded as S
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    say(f"device: {torch.cuda.get_device_name(0)}")
+
+
+def empty(shape, dtype):
+    return torch.empty(shape, dtype=dtype, device="cuda")
+
+
+def mlp_rank_phys(inp, p):
+    b, c = p.inter_begin, p.inter_cols
+    return phys(inp["w_gate"][:, b:b + c]), phys(inp["w_up"][:, b:b + c]), phys(inp["w_down"][b:b + c, :])
+
+
+# ---------------------------------------------------------------- tiny MLP, float32, t=2
+
+def test_tiny_mlp_f32():
+    wl = W.WORKLOADS[1]
+    m, H, I, t = wl.tokens[0], wl.hidden, wl.intermediate, wl.t
+    inp = W.mlp_inputs(1, H, I, m, "f32")
+    ref = L.mlp_block(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"])
+    sref = S.sharded_mlp(inp["x"], inp["w_gate"], inp["w_up"], inp["w_down"], t)
+    desc = tp.make_desc(H, I, bytes_per_elem=4)
+    x = dev(inp["x"], "f32")
+    parts, parts_fused = [], []
+    for r in range(t):
+        p = tp.tp_shard_plan(desc, t, r)
+        wg, wu, wd = [dev(a, "f32") for a in mlp_rank_phys(inp, p)]
+        c = p.inter_cols
+        g, u, a, a2 = (empty((m, c), torch.float32) for _ in range(4))
+        tp.tp_column_linear(x, wg, g)
+        tp.tp_column_linear(x, wu, u)
+        tp.tp_swiglu(g, u, a)
+        tp.tp_column_linear(x, wg, a2, w_up=wu)
+        pr, pr2 = empty((m, H), torch.float32), empty((m, H), torch.float32)
+        tp.tp_row_linear_partial(a, wd, pr)
+        tp.tp_row_linear_partial(a2, wd, pr2)
+        torch.cuda.synchronize()
+        rr = sref["ranks"][r]
+        check(f"rank{r} gate", host(g), rr["gate"], TOL["f32"])
+        check(f"rank{r} up", host(u), rr["up"], TOL["f32"])
+        check(f"rank{r} swiglu", host(a), rr["a"], TOL["f32"])
+        check(f"rank{r} fused swiglu", host(a2), rr["a"], TOL["f32"])
+        check(f"rank{r} partial", host(pr), rr["partial"], TOL["f32"])
+        parts.append(pr)
+        parts_fused.append(pr2)
+    out, out2 = empty((m, H), torch.float32), empty((m, H), torch.float32)
+    tp.tp_partial_sum(parts, out)
+    tp.tp_partial_sum(parts_fused, out2)
+    torch.cuda.synchronize()
+    check("sum of partials", host(out), ref["y"], TOL["f32"])
+    check("sum of partials (fused)", host(out2), ref["y"], TOL["f32"])
+
+
+# ---------------------------------------------------------------- Llama-3-8B-shaped MLP decode, bf16, t=4
+
+@pytest.fixture(scope="module")
+def mlp8b():
+    wl = W.WORKLOADS[2]
+    inp = W.mlp_inputs(2, wl.hidden, wl.intermediate, 16, "bf16", "random")
+    desc = tp.make_desc(wl.hidden, wl.intermediate)
+    ranks = []
+    for r in range(wl.t):
+        p = tp.tp_shard_plan(desc, wl.t, r)
+        ranks.append((p, [dev(a, "bf16") for a in mlp_rank_phys(inp, p)]))
+    return wl, inp, desc, ranks
+
+
+@pytest.mark.parametrize("gamma_mode", ["ones", "random"])
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_mlp_decode_bf16(mlp8b, m, gamma_mode):
+    wl, inp, desc, ranks = mlp8b
+    say(f"Llama-3-8B-shaped MLP decode shard m={m} gamma={gamma_mode}")
+    gamma = np.ones(wl.hidden, np.float32) if gamma_mode == "ones" else inp["gamma"]
+    xs = inp["x"][:m]                      # the batches are prefixes of one draw
+    ref = L.mlp_block(xs, inp["w_gate"], inp["w_up"], inp["w_down"], gamma, wl.eps)
+    sref = S.sharded_mlp(xs, inp["w_gate"], inp["w_up"], inp["w_down"], wl.t, gamma, wl.eps)
+    x = dev(xs, "bf16")
+    gam = dev(gamma, "bf16")
+    parts = []
+    for r, (p, (wg, wu, wd)) in enumerate(ranks):
+        part = empty((m, wl.hidden), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, {"mlp_norm": gam, "w_gate": wg, "w_up": wu,
+                                                              "w_down": wd}, x, part)
+        a = empty((m, p.inter_cols), torch.bfloat16)
+        tp.tp_column_linear(x, wg, a, w_up=wu, gamma=gam, eps=wl.eps)
+        torch.cuda.synchronize()
+        check(f"rank{r} swiglu(norm(x))", host(a), sref["ranks"][r]["a"], TOL["bf16"])
+        check(f"rank{r} partial", host(part), sref["ranks"][r]["partial"], TOL["bf16"])
+        parts.append(part)
+    out = empty((m, wl.hidden), torch.float32)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    check("sum of 4 partials", host(out), ref["y"], TOL["bf16"])
+
+
+# ---------------------------------------------------------------- 70B-shaped attention projections, t=4
+
+def qkv_rank_phys(a, p, d):
+    qb, qn, kb, kn = p.q_head_begin, p.q_heads, p.kv_head_begin, p.kv_heads
+    return np.concatenate([phys(a["w_q"][:, qb * d:(qb + qn) * d]), phys(a["w_k"][:, kb * d:(kb + kn) * d]),
+                           phys(a["w_v"][:, kb * d:(kb + kn) * d])], axis=0)
+
+
+def test_attn_projections_bf16():
+    wl = W.WORKLOADS[3]
+    H, nq, nkv, d, t, m = wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t, wl.tokens[0]
+    a = W.attention_inputs(3, H, nq, nkv, d, m, 1, "bf16", with_cache=False)
+    attn_in = W.attn_proj_input(3, m, nq * d, "bf16")
+    ref = L.attn_proj_block(a["x"], attn_in, a["w_q"], a["w_k"], a["w_v"], a["w_o"])
+    desc = tp.make_desc(H, 0, nq, nkv, d)
+    x = dev(a["x"], "bf16")
+    qs, ks, vs, parts = [], [], [], []
+    for r in range(t):
+        p = tp.tp_shard_plan(desc, t, r)
+        assert (p.qkv_cols, p.o_rows) == (2560, 2048)
+        wqkv = dev(qkv_rank_phys(a, p, d), "bf16")
+        y = empty((m, p.qkv_cols), torch.bfloat16)
+        tp.tp_column_linear(x, wqkv, y)
+        wo = dev(phys(a["w_o"][p.q_head_begin * d:(p.q_head_begin + p.q_heads) * d, :]), "bf16")
+        ar = dev(attn_in[:, p.q_head_begin * d:(p.q_head_begin + p.q_heads) * d], "bf16")
+        part = empty((m, H), torch.float32)
+        tp.tp_row_linear_partial(ar, wo, part)
+        torch.cuda.synchronize()
+        yh = host(y)
+        qs.append(yh[:, :p.o_rows])
+        ks.append(yh[:, p.o_rows:p.o_rows + p.kv_heads * d])
+        vs.append(yh[:, p.o_rows + p.kv_heads * d:])
+        parts.append(part)
+    check("Q (concat of 4 column shards)", np.concatenate(qs, 1), ref["q"], TOL["bf16"])
+    check("K (concat)", np.concatenate(ks, 1), ref["k"], TOL["bf16"])
+    check("V (concat)", np.concatenate(vs, 1), ref["v"], TOL["bf16"])
+    out = empty((m, H), torch.float32)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    check("W_o: sum of 4 row partials", host(out), ref["y"], TOL["bf16"])
+
+
+# ---------------------------------------------------------------- 70B-shaped MLP prefill, t=4, 4096 tokens
+
+@pytest.mark.timeout(600)
+def test_mlp_prefill_bf16():
+    wl = W.WORKLOADS[4]
+    H, I, t, M = wl.hidden, wl.intermediate, wl.t, wl.tokens[0]
+    say("drawing the 70B-shaped MLP weights")
+    inp = W.mlp_inputs(4, H, I, M, "bf16")
+    desc = tp.make_desc(H, I)
+    x = dev(inp["x"], "bf16")
+    rows = np.unique(np.concatenate([[0, 1, 2047, 2048, M - 1], np.random.default_rng(4).choice(M, 27, False)]))
+    xs = inp["x"][rows]
+    parts = []
+    for r in range(t):
+        p = tp.tp_shard_plan(desc, t, r)
+        wg, wu, wd = [dev(a, "bf16") for a in mlp_rank_phys(inp, p)]
+        part = empty((M, H), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, {"w_gate": wg, "w_up": wu, "w_down": wd}, x, part)
+        torch.cuda.synchronize()
+        del wg, wu, wd
+        rr = S.rank_mlp(xs, inp["w_gate"], inp["w_up"], inp["w_down"], tp.plan_dict(p))
+        check(f"rank{r} partial (sampled rows)", host(part)[rows], rr["partial"], TOL["bf16"])
+        parts.append(part)
+    out = empty((M, H), torch.float32)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    ref = L.mlp_block(xs, inp["w_gate"], inp["w_up"], inp["w_down"])
+    check("sum of 4 partials (sampled rows)", host(out)[rows], ref["y"], TOL["bf16"])
+
+
+# ---------------------------------------------------------------- 70B-shaped full layer decode, t=8
+
+@pytest.mark.timeout(600)
+def test_full_layer_decode_bf16():
+    wl = W.WORKLOADS[5]
+    H, I, nq, nkv, d, t, B, S_ = wl.hidden, wl.intermediate, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t, \
+        wl.tokens[0], wl.kv_len
+    say("drawing the 70B-shaped layer and its KV cache")
+    a = W.attention_inputs(5, H, nq, nkv, d, B, S_, "bf16", "random")
+    mi = W.mlp_inputs(5, H, I, B, "bf16", "random")
+    w = {"gamma1": a["gamma"], "w_q": a["w_q"], "w_k": a["w_k"], "w_v": a["w_v"], "w_o": a["w_o"],
+         "gamma2": mi["gamma"], "w_gate": mi["w_gate"], "w_up": mi["w_up"], "w_down": mi["w_down"]}
+    desc = tp.make_desc(H, I, nq, nkv, d, n_layers=1, seq_len=S_, batch=B, eps=wl.eps)
+    x = dev(a["x"], "bf16")
+    g1, g2 = dev(a["gamma"], "bf16"), dev(mi["gamma"], "bf16")
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    rank_w, caches, attn_parts = [], [], []
+    for p in plans:
+        kb, kn = p.kv_head_begin, p.kv_heads
+        rw = {"attn_norm": g1, "w_qkv": dev(qkv_rank_phys(a, p, d), "bf16"),
+              "w_o": dev(phys(a["w_o"][p.q_head_begin * d:(p.q_head_begin + p.q_heads) * d, :]), "bf16"),
+              "mlp_norm": g2}
+        rw["w_gate"], rw["w_up"], rw["w_down"] = [dev(q, "bf16") for q in mlp_rank_phys(mi, p)]
+        kc = dev(a["k_cache"][:, kb:kb + kn], "bf16")
+        vc = dev(a["v_cache"][:, kb:kb + kn], "bf16")
+        part = empty((B, H), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_ATTN, rw, x, part, kv={"k": kc, "v": vc, "kv_len": S_})
+        rank_w.append(rw)
+        caches.append((kc, vc))
+        attn_parts.append(part)
+    h = empty((B, H), torch.bfloat16)
+    tp.tp_partial_sum(attn_parts, h, residual=x)
+    mlp_parts = []
+    for p, rw in zip(plans, rank_w):
+        part = empty((B, H), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, rw, h, part)
+        mlp_parts.append(part)
+    out = empty((B, H), torch.bfloat16)
+    tp.tp_partial_sum(mlp_parts, out, residual=h)
+    torch.cuda.synchronize()
+
+    say("oracle: unsharded layer")
+    ref = L.layer(a["x"], w, a["k_cache"], a["v_cache"], S_, nq, nkv, d, wl.eps)
+    for r, p in enumerate(plans):
+        kb, kn = p.kv_head_begin, p.kv_heads
+        kc, vc = caches[r]
+        check(f"rank{r} appended k", host(kc)[:, :, S_ - 1], ref["attn"]["k_cache"][:, kb:kb + kn, S_ - 1],
+              TOL["bf16"])
+        check(f"rank{r} appended v", host(vc)[:, :, S_ - 1], ref["attn"]["v_cache"][:, kb:kb + kn, S_ - 1],
+              TOL["bf16"])
+    sr = S.rank_attention(a["x"], a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], S_, nq, nkv,
+                          d, tp.plan_dict(plans[0]), a["gamma"], wl.eps)
+    check("rank0 attention partial", host(attn_parts[0]), sr["partial"], TOL["bf16"])
+    check("h = x + sum of 8 attention partials", host(h), ref["h"], TOL["bf16"])
+    # the MLP stage against the oracle evaluated at the h the GPU produced
+    mref = L.mlp_block(host(h), w["w_gate"], w["w_up"], w["w_down"], w["gamma2"], wl.eps)
+    mparts = sum(host(q) for q in mlp_parts)
+    check("sum of 8 MLP partials at the GPU's h", mparts, mref["y"], TOL["bf16"])
+    check("layer output", host(out), ref["out"], TOL["bf16"])
+
+
+# ---------------------------------------------------------------- ragged and edge shapes
+
+LINEAR_CASES = [
+    # m, k, n, dtype
+    (1, 8, 1, "bf16"), (3, 264, 130, "bf16"), (5, 4104, 77, "bf16"), (16, 8200, 300, "bf16"),
+    (2, 16384, 64, "bf16"), (9, 1032, 257, "bf16"), (17, 520, 96, "bf16"), (40, 136, 40, "bf16"),
+    (1, 4, 3, "f32"), (7, 260, 33, "f32"), (16, 1028, 129, "f32"), (33, 64, 40, "f32"), (4, 6148, 70, "f32"),
+]
+
+
+@pytest.mark.parametrize("mode", ["col", "col_norm", "swiglu", "swiglu_norm", "row"])
+@pytest.mark.parametrize("case", LINEAR_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_linear_shapes(case, mode):
+    m, k, n, dt = case
+    seed = 100 + (31 * m + 7 * k + n) % 1000
+    x = W.storage_round(W.normal(seed, 0, (m, k)), dt)
+    wp = W.storage_round(W.normal(seed, 1, (n, k), 0.05), dt)     # physical [n, k]
+    wu = W.storage_round(W.normal(seed, 2, (n, k), 0.05), dt)
+    gam = W.storage_round(W.normal(seed, 3, (k,), 0.1, 1.0), dt)
+    norm = mode.endswith("norm")
+    u = L.rmsnorm(x, gam, 1e-5) if norm else x.astype(np.float64)
+    if mode.startswith("swiglu"):
+        ref = L.swiglu(L.linear(u, wp.T), L.linear(u, wu.T))
+    else:
+        ref = L.linear(u, wp.T)
+    tx, tw, twu, tg = dev(x, dt), dev(wp, dt), dev(wu, dt), dev(gam, dt)
+    if mode == "row":
+        y = empty((m, n), torch.float32)
+        tp.tp_row_linear_partial(tx, tw, y)
+    else:
+        y = empty((m, n), torch.bfloat16 if dt == "bf16" else torch.float32)
+        tp.tp_column_linear(tx, tw, y, w_up=twu if mode.startswith("swiglu") else None,
+                            gamma=tg if norm else None)
+    torch.cuda.synchronize()
+    check(f"{mode} m={m} k={k} n={n} {dt}", host(y), ref, TOL[dt])
+
+
+ATTN_CASES = [
+    # batch, q_heads, kv_heads, head_dim, capacity, kv_len
+    (1, 1, 1, 64, 1, 1), (2, 4, 2, 128, 300, 257), (3, 16, 1, 128, 1000, 1000), (4, 8, 8, 64, 5000, 4097),
+    (16, 8, 1, 128, 8192, 8192), (2, 2, 1, 128, 70000, 66000), (5, 4, 4, 128, 256, 255),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_decode_attention_shapes(case):
+    B, qh, kvh, d, cap, kv_len = case
+    seed = 200 + cap
+    q = W.to_bf16(W.normal(seed, 0, (B, qh * d)))
+    k = W.to_bf16(W.normal(seed, 1, (B, kvh, cap, d)))
+    v = W.to_bf16(W.normal(seed, 2, (B, kvh, cap, d)))
+    ref = L.decode_attention(q, k, v, kv_len, qh, kvh, d)
+    out = empty((B, qh * d), torch.bfloat16)
+    tp.tp_decode_attention(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, kv_len, qh)
+    torch.cuda.synchronize()
+    check(f"attention {case}", host(out), ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("t", [1, 3, 8])
+@pytest.mark.parametrize("shape", [(5, 7), (16, 8192), (3, 1)])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("residual", [False, True])
+def test_partial_sum_shapes(t, shape, out_dt, residual):
+    parts = [W.normal(300 + r, 0, shape) for r in range(t)]
+    res = W.storage_round(W.normal(399, 0, shape), out_dt) if residual else None
+    ref = sum(p.astype(np.float64) for p in parts) + (res if residual else 0.0)
+    out = empty(shape, torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    tp.tp_partial_sum([dev(p, "f32") for p in parts], out, residual=dev(res, out_dt) if residual else None)
+    torch.cuda.synchronize()
+    check(f"partial sum t={t} {shape} {out_dt}", host(out), ref, 1e-6 if out_dt == "f32" else 2 ** -8)
+
+
+@pytest.mark.parametrize("count", [(1, 1), (3, 333), (16, 3584)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_swiglu_standalone(count, dt):
+    g = W.storage_round(W.normal(400, 0, count, 3.0), dt)
+    u = W.storage_round(W.normal(400, 1, count), dt)
+    out = empty(count, torch.bfloat16 if dt == "bf16" else torch.float32)
+    tp.tp_swiglu(dev(g, dt), dev(u, dt), out)
+    torch.cuda.synchronize()
+    check(f"swiglu {count} {dt}", host(out), L.swiglu(g, u), TOL[dt])
+
+
+def test_repeatable_and_workspace_reuse():
+    """Same inputs, same workspace, twice: bitwise identical (split-K counters reset)."""
+    m, k, n = 16, 8192, 1280
+    x = dev(W.to_bf16(W.normal(500, 0, (m, k))), "bf16")
+    w = dev(W.to_bf16(W.normal(500, 1, (n, k), 0.02)), "bf16")
+    g = dev(W.to_bf16(W.normal(500, 2, (k,), 0.1, 1.0)), "bf16")
+    ws = tp.workspace(tp.tp_linear_workspace_bytes(m, k, n, tp.TP_BF16, tp.TP_LINEAR_NORM))
+    ys = []
+    for _ in range(3):
+        y = empty((m, n), torch.bfloat16)
+        tp.tp_column_linear(x, w, y, gamma=g, ws=ws)
+        ys.append(y)
+    q = dev(W.to_bf16(W.normal(501, 0, (16, 8 * 128))), "bf16")
+    kc = dev(W.to_bf16(W.normal(501, 1, (16, 1, 8192, 128))), "bf16")
+    vc = dev(W.to_bf16(W.normal(501, 2, (16, 1, 8192, 128))), "bf16")
+    aws = tp.workspace(tp.tp_attention_workspace_bytes(16, 8, 1, 128, 8192))
+    outs = []
+    for _ in range(3):
+        o = empty((16, 8 * 128), torch.bfloat16)
+        tp.tp_decode_attention(q, kc, vc, o, 8192, 8, ws=aws)
+        outs.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    wp, _ = tp._ws(ws)
+    off = wp - ws.data_ptr()
+    assert int(ws[off:off + 256].sum()) == 0, "split-K counters not reset"
