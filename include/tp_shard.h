@@ -34,11 +34,14 @@
  *  - Alignment. Every device pointer must be 16-byte aligned and K a multiple
  *    of 8 (bf16) or 4 (float32), so that rows stream in 128-bit loads.
  *  - Workspace. Entry points with `ws` need device scratch memory of at least
- *    the size the matching *_workspace_bytes function returns, 256-byte
- *    aligned, and zero-filled by the caller once, before its first use. Every
- *    call leaves the workspace's counters at zero again, so it can be reused
- *    without clearing. Calls sharing one workspace must not overlap in time
- *    (same stream, or ordered by events).
+ *    the size the matching *_workspace_bytes function returns (0 means `ws`
+ *    may be NULL), 256-byte aligned. Its first TP_WORKSPACE_HEADER bytes hold
+ *    completion counters that every entry point shares: the caller zero-fills
+ *    them once, before the first use, and every call leaves them zero again.
+ *    Scratch data lives only after the header, so one workspace, sized for the
+ *    largest call, serves calls of any shape in sequence without clearing.
+ *    Calls sharing one workspace must not overlap in time (same stream, or
+ *    ordered by events).
  *  - Errors. Arguments are validated on the host before anything is
  *    enqueued; on failure nothing is enqueued and a tp_status other than
  *    TP_OK is returned. tp_last_error() then gives a thread-local message
@@ -58,6 +61,9 @@ extern "C" {
 #endif
 
 typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+/* Bytes of shared completion counters at the start of every workspace. */
+#define TP_WORKSPACE_HEADER 32768
 
 typedef enum tp_status {
     TP_OK = 0,

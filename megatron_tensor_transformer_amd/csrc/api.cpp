@@ -91,25 +91,35 @@ bool use_gemm(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi) {
     return dt == TP_BF16 && epi != tpk::EPI_QKV && m > kGemvMaxM && tpk::gemm_supported((int)m, (int)n, (int)k, epi);
 }
 
-// Workspace layout of a projection: [normalised activations (GEMM path with
-// norm)][split-K scratch (GEMV path)].
-size_t linear_ws(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
+// Scratch bytes (after the counter header) a projection needs: the normalised
+// activations on the GEMM path with a norm, the split-K slices on the GEMV path.
+size_t linear_scratch(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
     if (use_gemm(m, k, n, dt, epi)) return norm ? round256((size_t)m * k * esize(dt)) : 0;
     return round256(tpk::gemv_plan((int)m, (int)k, (int)n, dt == TP_BF16, epi).ws_bytes);
 }
 
+bool linear_needs_ws(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
+    if (use_gemm(m, k, n, dt, epi)) return norm;
+    return tpk::gemv_plan((int)m, (int)k, (int)n, dt == TP_BF16, epi).splits > 1;
+}
+
+// Whole workspace of a standalone projection: header + scratch, or 0.
+size_t linear_ws(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
+    return linear_needs_ws(m, k, n, dt, epi, norm) ? tpk::WS_HEADER + linear_scratch(m, k, n, dt, epi, norm) : 0;
+}
+
 // Enqueue one projection. x [m,k], w (and w_up) [n,k]; y per epilogue.
+// counters: the workspace header; scratch: this call's scratch region.
 tp_status run_linear(const void* x, const void* w, const void* w_up, const void* gamma, float eps, void* y,
-                     int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, void* ws, size_t ws_bytes,
+                     int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, unsigned* counters, void* scratch,
                      hipStream_t s, const tpk::GemvArgs* qkv = nullptr) {
     const bool norm = gamma != nullptr;
-    TRY(check_ws(ws, ws_bytes, linear_ws(m, k, n, dt, epi, norm)));
     if (use_gemm(m, k, n, dt, epi)) {
         const void* xin = x;
         if (norm) {
-            hipError_t e = tpk::rmsnorm_launch(x, gamma, ws, (int)m, (int)k, eps, 1, s);
+            hipError_t e = tpk::rmsnorm_launch(x, gamma, scratch, (int)m, (int)k, eps, 1, s);
             if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
-            xin = ws;
+            xin = scratch;
         }
         tpk::GemmArgs g{};
         g.x = xin; g.w = w; g.w_up = w_up; g.y = y;
@@ -126,10 +136,13 @@ tp_status run_linear(const void* x, const void* w, const void* w_up, const void*
     a.epi = epi;
     a.norm = norm;
     const tpk::GemvPlan p = tpk::gemv_plan(a.m, a.K, a.N, a.is_bf16, epi);
-    hipError_t e = tpk::gemv_launch(a, p, ws, s);
+    hipError_t e = tpk::gemv_launch(a, p, counters, scratch, s);
     if (e != hipSuccess) return hip_fail(e, "GEMV launch");
     return ok();
 }
+
+unsigned* ws_counters(void* ws) { return reinterpret_cast<unsigned*>(ws); }
+void* ws_scratch(void* ws) { return ws ? reinterpret_cast<char*>(ws) + tpk::WS_HEADER : nullptr; }
 
 tp_status plan_impl(const tp_model_desc* d, int32_t t, int32_t rank, tp_rank_plan* out) {
     if (!d) return fail(TP_ERR_NULL, "desc is NULL");
@@ -192,6 +205,7 @@ tp_status check_plan(const tp_model_desc* d, const tp_rank_plan* p) {
     return TP_OK;
 }
 
+// Layer workspace: [counter header][act1][act2][projection scratch][attention scratch].
 struct LayerWs {
     size_t act1, act2, lin, attn, total;
 };
@@ -202,17 +216,17 @@ LayerWs layer_ws(const tp_model_desc* d, const tp_rank_plan* p, tp_stage stage, 
     if (stage == TP_STAGE_ATTN) {
         w.act1 = round256((size_t)m * p->o_rows * 2);   // q
         w.act2 = round256((size_t)m * p->o_rows * 2);   // attention output
-        const size_t l1 = linear_ws(m, H, p->qkv_cols, dt, tpk::EPI_QKV, true);
-        const size_t l2 = linear_ws(m, p->o_rows, H, dt, tpk::EPI_PARTIAL, false);
+        const size_t l1 = linear_scratch(m, H, p->qkv_cols, dt, tpk::EPI_QKV, true);
+        const size_t l2 = linear_scratch(m, p->o_rows, H, dt, tpk::EPI_PARTIAL, false);
         w.lin = l1 > l2 ? l1 : l2;
         w.attn = round256(tpk::attn_plan((int)m, p->q_heads, p->kv_heads, d->head_dim, (int)d->seq_len).ws_bytes);
     } else {
         w.act1 = round256((size_t)m * p->inter_cols * esize(dt));  // SwiGLU output
-        const size_t l1 = linear_ws(m, H, p->inter_cols, dt, tpk::EPI_SWIGLU, true);
-        const size_t l2 = linear_ws(m, p->inter_cols, H, dt, tpk::EPI_PARTIAL, false);
+        const size_t l1 = linear_scratch(m, H, p->inter_cols, dt, tpk::EPI_SWIGLU, true);
+        const size_t l2 = linear_scratch(m, p->inter_cols, H, dt, tpk::EPI_PARTIAL, false);
         w.lin = l1 > l2 ? l1 : l2;
     }
-    w.total = w.act1 + w.act2 + w.lin + w.attn;
+    w.total = tpk::WS_HEADER + w.act1 + w.act2 + w.lin + w.attn;
     return w;
 }
 
@@ -272,7 +286,9 @@ tp_status tp_column_linear(const void* x, const void* w, const void* w_up, const
         return fail(TP_ERR_ALIAS, "y overlaps an input; use a separate output buffer");
     if (ws && overlaps(ws, ws_bytes, y, ny)) return fail(TP_ERR_ALIAS, "workspace overlaps y");
     const int epi = w_up ? tpk::EPI_SWIGLU : tpk::EPI_STORE;
-    return run_linear(x, w, w_up, gamma, eps, y, m, k, n, dtype, epi, ws, ws_bytes, (hipStream_t)stream);
+    TRY(check_ws(ws, ws_bytes, linear_ws(m, k, n, dtype, epi, gamma != nullptr)));
+    return run_linear(x, w, w_up, gamma, eps, y, m, k, n, dtype, epi, ws_counters(ws), ws_scratch(ws),
+                      (hipStream_t)stream);
 }
 
 tp_status tp_row_linear_partial(const void* a, const void* w, float* partial, int64_t m, int64_t k, int64_t n,
@@ -290,8 +306,9 @@ tp_status tp_row_linear_partial(const void* a, const void* w, float* partial, in
     if (overlaps(partial, np, a, (size_t)m * k * es) || overlaps(partial, np, w, (size_t)n * k * es))
         return fail(TP_ERR_ALIAS, "partial overlaps an input");
     if (ws && overlaps(ws, ws_bytes, partial, np)) return fail(TP_ERR_ALIAS, "workspace overlaps partial");
-    return run_linear(a, w, nullptr, nullptr, 0.f, partial, m, k, n, dtype, tpk::EPI_PARTIAL, ws, ws_bytes,
-                      (hipStream_t)stream);
+    TRY(check_ws(ws, ws_bytes, linear_ws(m, k, n, dtype, tpk::EPI_PARTIAL, false)));
+    return run_linear(a, w, nullptr, nullptr, 0.f, partial, m, k, n, dtype, tpk::EPI_PARTIAL, ws_counters(ws),
+                      ws_scratch(ws), (hipStream_t)stream);
 }
 
 tp_status tp_swiglu(const void* gate, const void* up, void* out, int64_t m, int64_t n, tp_dtype dtype,
@@ -337,7 +354,8 @@ tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* re
 size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                     int64_t kv_len) {
     if (batch < 1 || q_heads < 1 || kv_heads < 1 || q_heads % kv_heads || kv_len < 1) return 0;
-    return round256(tpk::attn_plan((int)batch, q_heads, kv_heads, head_dim, (int)kv_len).ws_bytes);
+    const tpk::AttnPlan p = tpk::attn_plan((int)batch, q_heads, kv_heads, head_dim, (int)kv_len);
+    return p.n_chunks > 1 ? tpk::WS_HEADER + round256(p.ws_bytes) : 0;
 }
 
 static tp_status check_attention(const void* q, const void* k, const void* v, const void* out, int64_t batch,
@@ -371,12 +389,12 @@ tp_status tp_decode_attention(const void* q, const void* k, const void* v, void*
                               void* ws, size_t ws_bytes, void* stream) {
     TRY(check_attention(q, k, v, out, batch, q_heads, kv_heads, head_dim, capacity, kv_len, dtype));
     const tpk::AttnPlan p = tpk::attn_plan((int)batch, q_heads, kv_heads, head_dim, (int)kv_len);
-    TRY(check_ws(ws, ws_bytes, p.ws_bytes));
+    TRY(check_ws(ws, ws_bytes, p.n_chunks > 1 ? tpk::WS_HEADER + round256(p.ws_bytes) : 0));
     tpk::AttnArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out;
     a.capacity = capacity; a.kv_len = (int)kv_len;
     a.batch = (int)batch; a.q_heads = q_heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
-    hipError_t e = tpk::attn_launch(a, p, ws, (hipStream_t)stream);
+    hipError_t e = tpk::attn_launch(a, p, ws_counters(ws), ws_scratch(ws), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     return ok();
 }
@@ -440,7 +458,8 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
                         (long long)desc->seq_len);
         const LayerWs L = layer_ws(desc, plan, stage, m, dtype);
         TRY(check_ws(ws, ws_bytes, L.total));
-        char* b = reinterpret_cast<char*>(ws);
+        char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
+        unsigned* cnt = ws_counters(ws);
         void* qbuf = b;
         void* obuf = b + L.act1;
         void* lin = b + L.act1 + L.act2;
@@ -455,18 +474,17 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         extra.head_dim = desc->head_dim;
         extra.kv_heads = plan->kv_heads;
         TRY(run_linear(in, wts->w_qkv, nullptr, wts->attn_norm, desc->eps, qbuf, m, H, plan->qkv_cols, dtype,
-                       tpk::EPI_QKV, lin, L.lin, s, &extra));
+                       tpk::EPI_QKV, cnt, lin, s, &extra));
         tpk::AttnArgs a{};
         a.q = qbuf; a.k = kv->k; a.v = kv->v; a.out = obuf;
         a.capacity = kv->capacity; a.kv_len = (int)kv->kv_len;
         a.batch = (int)m; a.q_heads = plan->q_heads; a.kv_heads = plan->kv_heads; a.head_dim = desc->head_dim;
-        const tpk::AttnPlan ap = tpk::attn_plan(a.batch, a.q_heads, a.kv_heads, a.head_dim, (int)desc->seq_len);
         const tpk::AttnPlan ap_len = tpk::attn_plan(a.batch, a.q_heads, a.kv_heads, a.head_dim, a.kv_len);
-        if (ap_len.ws_bytes > ap.ws_bytes) return fail(TP_ERR_WORKSPACE, "attention workspace too small");
-        hipError_t e = tpk::attn_launch(a, ap_len, aws, s);
+        if (round256(ap_len.ws_bytes) > L.attn) return fail(TP_ERR_WORKSPACE, "attention workspace too small");
+        hipError_t e = tpk::attn_launch(a, ap_len, cnt, aws, s);
         if (e != hipSuccess) return hip_fail(e, "attention launch");
         return run_linear(obuf, wts->w_o, nullptr, nullptr, 0.f, partial, m, plan->o_rows, H, dtype,
-                          tpk::EPI_PARTIAL, lin, L.lin, s);
+                          tpk::EPI_PARTIAL, cnt, lin, s);
     }
 
     if (plan->inter_cols < 1) return fail(TP_ERR_SHAPE, "desc has no MLP");
@@ -478,13 +496,14 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         return fail(TP_ERR_ALIGN, "inter_cols=%lld not a multiple of %zu", (long long)plan->inter_cols, vec_elems(dtype));
     const LayerWs L = layer_ws(desc, plan, stage, m, dtype);
     TRY(check_ws(ws, ws_bytes, L.total));
-    char* b = reinterpret_cast<char*>(ws);
+    char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
+    unsigned* cnt = ws_counters(ws);
     void* abuf = b;
     void* lin = b + L.act1;
     TRY(run_linear(in, wts->w_gate, wts->w_up, wts->mlp_norm, desc->eps, abuf, m, H, plan->inter_cols, dtype,
-                   tpk::EPI_SWIGLU, lin, L.lin, s));
+                   tpk::EPI_SWIGLU, cnt, lin, s));
     return run_linear(abuf, wts->w_down, nullptr, nullptr, 0.f, partial, m, plan->inter_cols, H, dtype,
-                      tpk::EPI_PARTIAL, lin, L.lin, s);
+                      tpk::EPI_PARTIAL, cnt, lin, s);
 }
 
 }  // extern "C"

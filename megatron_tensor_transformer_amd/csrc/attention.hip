@@ -7,7 +7,8 @@
 // an unnormalised partial with its max and sum in the workspace. The last
 // workgroup of a (sequence, kv head) to finish, found with a counter, merges
 // the chunk partials in chunk order by their log-sum-exp weights and writes
-// the bf16 output; it then resets the counter. Reading K and V once is the
+// the bf16 output. Partials travel through agent-scope coherent stores and
+// loads, so no cache-wide fence is needed. Reading K and V once is the
 // cost; q is staged in LDS and read by broadcast.
 #include "device_common.h"
 #include "kernels.h"
@@ -160,32 +161,27 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
     float* po = d.po + ((size_t)bg * d.n_chunks + c) * GQ * D;
     for (int i = tid; i < GQ * D; i += AT_NT) {
         const int h = i / D, e = i % D;
-        po[i] = red[0][h][e] + red[1][h][e] + red[2][h][e] + red[3][h][e];
+        store_coherent(po + i, red[0][h][e] + red[1][h][e] + red[2][h][e] + red[3][h][e]);
     }
     if (tid < GQ) {
         float* ml = d.pml + (((size_t)bg * d.n_chunks + c) * GQ + tid) * 2;
-        ml[0] = mrun[tid];
-        ml[1] = lrun[tid];
+        store_coherent(ml, mrun[tid]);
+        store_coherent(ml + 1, lrun[tid]);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&d.cnt[bg], 1u) == (unsigned)(d.n_chunks - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+    if (!last_arriver(&d.cnt[bg], (unsigned)d.n_chunks, &s_last)) return;
 
     // merge the chunks in chunk order
     __shared__ float wgt[AT_MAX_CHUNKS][GQ];
     const float* mlb = d.pml + (size_t)bg * d.n_chunks * GQ * 2;
     for (int h = wave; h < GQ; h += 4) {
         float mx = -INFINITY;
-        for (int cc = lane; cc < d.n_chunks; cc += 64) mx = fmaxf(mx, mlb[(cc * GQ + h) * 2]);
+        for (int cc = lane; cc < d.n_chunks; cc += 64) mx = fmaxf(mx, load_coherent(mlb + (cc * GQ + h) * 2));
         mx = group_max<64>(mx);
         float l = 0.f;
         for (int cc = lane; cc < d.n_chunks; cc += 64) {
-            const float w = __expf(mlb[(cc * GQ + h) * 2] - mx);
+            const float w = __expf(load_coherent(mlb + (cc * GQ + h) * 2) - mx);
             wgt[cc][h] = w;
-            l += w * mlb[(cc * GQ + h) * 2 + 1];
+            l += w * load_coherent(mlb + (cc * GQ + h) * 2 + 1);
         }
         l = group_sum<64>(l);
         if (lane == 0) alpha[h] = 1.0f / l;
@@ -195,10 +191,9 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
     for (int i = tid; i < GQ * D; i += AT_NT) {
         const int h = i / D;
         float v = 0.f;
-        for (int cc = 0; cc < d.n_chunks; ++cc) v = fmaf(wgt[cc][h], pob[(size_t)cc * GQ * D + i], v);
+        for (int cc = 0; cc < d.n_chunks; ++cc) v = fmaf(wgt[cc][h], load_coherent(pob + (size_t)cc * GQ * D + i), v);
         out[i] = (uint16_t)f32_to_bf16_bits(v * alpha[h]);
     }
-    if (tid == 0) atomicExch(&d.cnt[bg], 0u);
 }
 
 AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_len) {
@@ -216,13 +211,16 @@ AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_le
         ++passes_per_chunk;
         n_chunks = (passes_total + passes_per_chunk - 1) / passes_per_chunk;
     }
+    if (pairs > WS_MAX_COUNTERS) {   // one counter per (sequence, kv head): no split beyond that
+        passes_per_chunk = passes_total;
+        n_chunks = 1;
+    }
     p.chunk = passes_per_chunk * AT_PASS;
     p.n_chunks = n_chunks;
     if (n_chunks > 1) {
-        const size_t cnt = ((size_t)pairs * 4 + 255) / 256 * 256;
         const size_t ml = ((size_t)pairs * n_chunks * gq * 2 * 4 + 255) / 256 * 256;
         const size_t o = (size_t)pairs * n_chunks * gq * head_dim * 4;
-        p.ws_bytes = cnt + ml + (o + 255) / 256 * 256;
+        p.ws_bytes = ml + (o + 255) / 256 * 256;
     } else {
         p.ws_bytes = 0;
     }
@@ -248,7 +246,7 @@ static hipError_t attn_launch_d(const AttnDev& d, int gq, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t s) {
+hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, unsigned* counters, void* scratch, hipStream_t s) {
     AttnDev d{};
     d.a = a;
     d.chunk = p.chunk;
@@ -256,12 +254,11 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream
     const int gq = a.q_heads / a.kv_heads;
     if (p.n_chunks > 1) {
         const size_t pairs = (size_t)a.batch * a.kv_heads;
-        char* b = reinterpret_cast<char*>(ws);
-        const size_t cnt = (pairs * 4 + 255) / 256 * 256;
+        char* b = reinterpret_cast<char*>(scratch);
         const size_t ml = (pairs * p.n_chunks * gq * 2 * 4 + 255) / 256 * 256;
-        d.cnt = reinterpret_cast<unsigned*>(b);
-        d.pml = reinterpret_cast<float*>(b + cnt);
-        d.po = reinterpret_cast<float*>(b + cnt + ml);
+        d.cnt = counters;
+        d.pml = reinterpret_cast<float*>(b);
+        d.po = reinterpret_cast<float*>(b + ml);
     }
     if (a.head_dim == 64) return attn_launch_d<64>(d, gq, s);
     if (a.head_dim == 128) return attn_launch_d<128>(d, gq, s);

@@ -50,6 +50,103 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// Lane exchange within rows of 16 lanes (DPP). Each control is an involution
+// pairing the lower and upper half of a block: mirror (i <-> 15-i, block 16),
+// half mirror (i <-> 7-i, block 8), quad xor 2 and quad xor 1.
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int ST>
+__device__ __forceinline__ float dpp_stage(float v) {
+    if constexpr (ST == 0) return dpp_mov<DPP_ROW_MIRROR>(v);
+    else if constexpr (ST == 1) return dpp_mov<DPP_ROW_HALF_MIRROR>(v);
+    else if constexpr (ST == 2) return dpp_mov<DPP_QUAD_XOR2>(v);
+    else return dpp_mov<DPP_QUAD_XOR1>(v);
+}
+
+template <int ST, int N>
+__device__ __forceinline__ void rs_stage(float* v, int sub) {
+    if constexpr (ST < 4) {
+        if constexpr (N > 1) {
+            constexpr int H = N / 2;
+            const bool upper = (sub >> (3 - ST)) & 1;
+#pragma unroll
+            for (int j = 0; j < H; ++j) {
+                const float keep = upper ? v[H + j] : v[j];
+                const float send = upper ? v[j] : v[H + j];
+                v[j] = keep + dpp_stage<ST>(send);
+            }
+            rs_stage<ST + 1, H>(v, sub);
+        } else {
+            v[0] += dpp_stage<ST>(v[0]);
+            rs_stage<ST + 1, 1>(v, sub);
+        }
+    }
+}
+
+// Reduce V values over each group of 16 lanes and scatter the sums: stage s
+// pairs the lanes of a block of 16 >> s and keeps half of the remaining values
+// (the upper lane of a pair keeps the upper half). After log2(V) stages (at
+// most 4) each lane holds V/16 sums in v[0 .. V/16) (or, for V < 16, one sum
+// duplicated over 16/V lanes); reduce16_index names them.
+template <int V>
+__device__ __forceinline__ void reduce_scatter16(float* v, int sub) {
+    static_assert(V >= 1 && (V & (V - 1)) == 0, "V must be a power of two");
+    rs_stage<0, V>(v, sub);
+}
+
+// Value index held in slot j of lane `sub` after reduce_scatter16<V>; lanes
+// that hold a duplicate (V < 16) are those with owner == false.
+template <int V>
+__device__ __forceinline__ int reduce16_index(int sub, int j, bool& owner) {
+    int idx = 0, n = V;
+    owner = true;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int bit = (sub >> (3 - st)) & 1;
+        if (n > 1) {
+            n /= 2;
+            idx += bit * n;
+        } else if (bit) {
+            owner = false;
+        }
+    }
+    return idx + j;
+}
+
+// Agent-scope relaxed atomics: coherent per location across the XCDs without
+// the cache-wide writeback/invalidate of an agent-scope fence.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup-level "last one to finish" vote over `total` workgroups sharing a
+// counter. Every thread's coherent stores must be complete before the vote;
+// the caller's threads all call this. Returns true in every thread of the
+// last workgroup, which also resets the counter for the next use.
+__device__ __forceinline__ bool last_arriver(unsigned* counter, unsigned total, int* s_flag) {
+    __builtin_amdgcn_s_waitcnt(0);           // this thread's stores are acknowledged
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == total - 1;
+        if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // 128-bit global load that marks the line as streamed (used once).

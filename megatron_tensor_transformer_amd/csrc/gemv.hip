@@ -13,14 +13,19 @@
 //    accumulators; the activation vector read from LDS is shared by those rows.
 //  - bf16 products use v_dot2 (two multiply-adds per lane per instruction,
 //    float32 accumulation, no unpacking); float32 inputs use fma.
-//  - The G lanes of a group are reduced by a fixed butterfly; results go
-//    through a small LDS tile so the epilogue writes outputs in coalesced
-//    order.
-//  - When K is split over S workgroups, each writes its float32 tile to the
-//    workspace and bumps a per-tile counter; the last to arrive sums the S
-//    slices in split order (deterministic) and runs the epilogue, then resets
-//    the counter. RMSNorm's sum of squares travels the same way, so the
-//    normalisation stays fused: inv_rms multiplies the contraction result.
+//  - Every lane keeps PF steps of weight vectors in flight (a register ring
+//    refilled as each step is consumed), so a workgroup's whole share of a
+//    decode-sized matrix is requested at once.
+//  - The 16 lanes of a group are reduced by a DPP reduce-scatter (row mirror,
+//    half mirror, quad permutes) in a fixed order; each lane ends with its
+//    share of the sums, which go through a small LDS tile so the epilogue
+//    writes outputs in coalesced order.
+//  - When K is split over S workgroups, each publishes its float32 tile with
+//    agent-scope coherent stores and bumps a per-tile counter; the last to
+//    arrive sums the S slices in split order (deterministic), runs the
+//    epilogue and resets the counter. No cache-wide fence is needed. RMSNorm's
+//    sum of squares travels the same way, so the normalisation stays fused:
+//    inv_rms multiplies the contraction result.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,6 +36,8 @@ constexpr int GEMV_NW = 4;     // waves per workgroup
 constexpr size_t GEMV_X_LDS = 64 * 1024;   // LDS budget for the staged activation chunk
 
 template <int MT> struct RowsPerLane { static constexpr int v = MT >= 8 ? 4 : 2; };
+template <int MT> struct Prefetch { static constexpr int v = MT >= 8 ? 4 : 8; };
+static int rows_per_tile(int mt) { return GEMV_NW * (64 / GEMV_G) * (mt >= 8 ? 4 : 2); }
 
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int vec = 8; };
@@ -99,6 +106,7 @@ __device__ __forceinline__ void store_out(void* y, size_t idx, float v, float*) 
 struct GemvDev {
     GemvArgs a;
     int kc, splits, n_tiles;
+    int mb0;           // first m-block of this launch
     float* part;       // [tiles*mblocks][S][MT*RPT]
     float* ssq;        // [tiles*mblocks][S][MT]
     unsigned* cnt;     // [tiles*mblocks]
@@ -111,6 +119,7 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     constexpr int NT = NW * 64;
     constexpr int VEC = Elem<T>::vec;
     constexpr int RWG = RowsPerLane<MT>::v;
+    constexpr int PF = Prefetch<MT>::v;    // steps of weight vectors kept in flight
     constexpr int GROUPS = 64 / G;
     constexpr int RPW = GROUPS * RWG;
     constexpr int RPT = NW * RPW;
@@ -118,6 +127,8 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     constexpr int HALF = RPT / 2;
     constexpr int OUTS = SWI ? HALF : RPT;
     constexpr int STEP = G * VEC;   // K elements one group covers per step
+    constexpr int NV = RWG * MT;    // sums per lane before the group reduction
+    constexpr int NKEEP = NV >= 16 ? NV / 16 : 1;
 
     const GemvArgs& a = d.a;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane / G, sub = lane % G;
-    const int tile = blockIdx.x, split = blockIdx.y, mb = blockIdx.z;
+    const int tile = blockIdx.x, split = blockIdx.y, mb = d.mb0 + blockIdx.z;
     const int K = a.K, N = a.N;
     const int k0 = split * kc;
     const int klen = min(kc, K - k0);
@@ -164,15 +175,20 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
         }
     };
 
-    // Issue the first weight loads before staging the activations: they do
-    // not depend on them, so their latency overlaps the staging.
-    uint4 wa[RWG], wb[RWG];
-    load_w(wa, 0);
+    // Put PF steps of weight loads in flight before staging the activations:
+    // they do not depend on them, so their latency overlaps the staging.
+    uint4 wbuf[PF][RWG];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) load_w(wbuf[u], u);
 
-    // Stage the activation chunk (times gamma) and its sum of squares.
+    // Stage the activation chunk (times gamma) and its sum of squares. Each
+    // wave stages whole rows; all loads of a row are issued before any store.
     const T* x = reinterpret_cast<const T*>(a.x);
     const T* gam = reinterpret_cast<const T*>(a.gamma);
-    for (int mm = wave; mm < MT; mm += NW) {
+#pragma unroll
+    for (int mi = 0; mi < (MT + NW - 1) / NW; ++mi) {
+        const int mm = wave + mi * NW;
+        if (mm >= MT) break;
         float ss = 0.f;
         for (int c = lane; c < kc / VEC; c += 64) {
             const int k = c * VEC;
@@ -199,60 +215,61 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) acc[rg][m] = 0.f;
 
-    auto compute = [&](const uint4* wv, int j) {
-        const int k = (j * G + sub) * VEC;
+    for (int j0 = 0; j0 < steps; j0 += PF) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * kc + k);
+        for (int u = 0; u < PF; ++u) {
+            const int j = j0 + u;
+            if (j < steps) {
+                const int k = (j * G + sub) * VEC;
 #pragma unroll
-            for (int rg = 0; rg < RWG; ++rg) acc[rg][m] = vdot(wv[rg], xv, acc[rg][m], (T*)nullptr);
-        }
-    };
-
-    for (int j = 0; j < steps; j += 2) {
-        if (j + 1 < steps) load_w(wb, j + 1);
-        compute(wa, j);
-        if (j + 1 < steps) {
-            if (j + 2 < steps) load_w(wa, j + 2);
-            compute(wb, j + 1);
+                for (int m = 0; m < MT; ++m) {
+                    const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * kc + k);
+#pragma unroll
+                    for (int rg = 0; rg < RWG; ++rg) acc[rg][m] = vdot(wbuf[u][rg], xv, acc[rg][m], (T*)nullptr);
+                }
+                load_w(wbuf[u], j + PF);
+            }
         }
     }
 
-    // Reduce each row over its G lanes; lanes share out the stores.
+    // Reduce every row over its 16 lanes and scatter the sums over them; each
+    // lane then writes its share of the tile to LDS.
+    float v[NV];
 #pragma unroll
-    for (int rg = 0; rg < RWG; ++rg) {
-        const int rho = wave * RPW + rg * GROUPS + grp;
+    for (int rg = 0; rg < RWG; ++rg)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float v = group_sum<G>(acc[rg][m]);
-            if (((rg * MT + m) % G) == sub) res[m * RPT + rho] = v;
+        for (int m = 0; m < MT; ++m) v[rg * MT + m] = acc[rg][m];
+    reduce_scatter16<NV>(v, sub);
+#pragma unroll
+    for (int j = 0; j < NKEEP; ++j) {
+        bool owner;
+        const int idx = reduce16_index<NV>(sub, j, owner);
+        if (owner) {
+            const int rg = idx / MT, m = idx % MT;
+            res[m * RPT + wave * RPW + rg * GROUPS + grp] = v[j];
         }
     }
     __syncthreads();
 
-    const int tile_id = mb * d.n_tiles + tile;
+    const int tile_id = blockIdx.z * d.n_tiles + tile;
     if (d.splits > 1) {
+        // Publish this split's tile with coherent stores; the last split to
+        // arrive adds the slices in split order.
         float* base = d.part + (size_t)tile_id * d.splits * (MT * RPT);
         float* mine = base + (size_t)split * (MT * RPT);
-        for (int i = tid; i < MT * RPT; i += NT) mine[i] = res[i];
-        if (NORM && tid < MT) d.ssq[((size_t)tile_id * d.splits + split) * MT + tid] = ssl[tid];
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(&d.cnt[tile_id], 1u) == (unsigned)(d.splits - 1));
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
+        for (int i = tid; i < MT * RPT; i += NT) store_coherent(mine + i, res[i]);
+        if (NORM && tid < MT) store_coherent(d.ssq + ((size_t)tile_id * d.splits + split) * MT + tid, ssl[tid]);
+        if (!last_arriver(&d.cnt[tile_id], (unsigned)d.splits, &s_last)) return;
         for (int i = tid; i < MT * RPT; i += NT) {
-            float v = 0.f;
-            for (int s = 0; s < d.splits; ++s) v += base[(size_t)s * (MT * RPT) + i];
-            res[i] = v;
+            float s = 0.f;
+            for (int sp = 0; sp < d.splits; ++sp) s += load_coherent(base + (size_t)sp * (MT * RPT) + i);
+            res[i] = s;
         }
         if (NORM && tid < MT) {
-            float v = 0.f;
-            for (int s = 0; s < d.splits; ++s) v += d.ssq[((size_t)tile_id * d.splits + s) * MT + tid];
-            ssl[tid] = v;
+            float s = 0.f;
+            for (int sp = 0; sp < d.splits; ++sp) s += load_coherent(d.ssq + ((size_t)tile_id * d.splits + sp) * MT + tid);
+            ssl[tid] = s;
         }
-        if (tid == 0) atomicExch(&d.cnt[tile_id], 0u);
         __syncthreads();
     }
 
@@ -292,8 +309,6 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     }
 }
 
-static int rows_per_tile(int mt) { return GEMV_NW * (64 / GEMV_G) * (mt >= 8 ? 4 : 2); }
-
 GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
     GemvPlan p{};
     p.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
@@ -318,16 +333,25 @@ GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
     }
     int kc = ((kround + S - 1) / S + step - 1) / step * step;
     S = (K + kc - 1) / kc;
+    p.mb_per_launch = p.mblocks;
+    if (S > 1 && (size_t)p.n_tiles * p.mblocks > (size_t)WS_MAX_COUNTERS) {
+        // one counter per tile: run the m-blocks in launches that fit the header
+        p.mb_per_launch = WS_MAX_COUNTERS / p.n_tiles;
+        if (p.mb_per_launch < 1) {       // N beyond 2^18 outputs: no split
+            p.mb_per_launch = p.mblocks;
+            kc = kround;
+            S = 1;
+        }
+    }
+    const size_t tiles = (size_t)p.n_tiles * p.mb_per_launch;
     p.kc = kc;
     p.splits = S;
     p.threads = GEMV_NW * 64;
     p.lds_bytes = (size_t)p.mt * kc * esz + (size_t)p.mt * p.rows_per_tile * 4 + (size_t)p.mt * 4;
     if (S > 1) {
-        const size_t tiles = (size_t)p.n_tiles * p.mblocks;
-        const size_t cnt = (tiles * 4 + 255) / 256 * 256;
         const size_t part = tiles * S * p.mt * p.rows_per_tile * 4;
         const size_t ssq = tiles * S * p.mt * 4;
-        p.ws_bytes = cnt + (part + 255) / 256 * 256 + (ssq + 255) / 256 * 256;
+        p.ws_bytes = (part + 255) / 256 * 256 + (ssq + 255) / 256 * 256;
     } else {
         p.ws_bytes = 0;
     }
@@ -341,14 +365,25 @@ static hipError_t launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
     // in practice: the first call of a shape is an eager one).
     static bool lds_raised = false;
     if (p.lds_bytes > 64 * 1024 && !lds_raised) {
+        // the most this instantiation can ask for: the activation budget plus its result tile
+        const int most = (int)(GEMV_X_LDS + (size_t)MT * rows_per_tile(MT) * 4 + MT * 4);
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();   // do not leave the error pending for the caller's next HIP call
+            return e;
+        }
         lds_raised = true;
     }
-    dim3 grid(p.n_tiles, p.splits, p.mblocks);
-    hipLaunchKernelGGL(kern, grid, dim3(p.threads), p.lds_bytes, s, d);
-    return hipGetLastError();
+    for (int mb0 = 0; mb0 < p.mblocks; mb0 += p.mb_per_launch) {
+        GemvDev dl = d;
+        dl.mb0 = mb0;
+        dim3 grid(p.n_tiles, p.splits, min(p.mb_per_launch, p.mblocks - mb0));
+        hipLaunchKernelGGL(kern, grid, dim3(p.threads), p.lds_bytes, s, dl);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <typename T, int MT>
@@ -363,20 +398,19 @@ static hipError_t launch_epi(const GemvDev& d, const GemvPlan& p, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
-hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, void* ws, hipStream_t s) {
+hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters, void* scratch, hipStream_t s) {
     GemvDev d{};
     d.a = a;
     d.kc = p.kc;
     d.splits = p.splits;
     d.n_tiles = p.n_tiles;
     if (p.splits > 1) {
-        const size_t tiles = (size_t)p.n_tiles * p.mblocks;
-        char* b = reinterpret_cast<char*>(ws);
-        const size_t cnt = (tiles * 4 + 255) / 256 * 256;
+        const size_t tiles = (size_t)p.n_tiles * p.mb_per_launch;
+        char* b = reinterpret_cast<char*>(scratch);
         const size_t part = (tiles * p.splits * p.mt * p.rows_per_tile * 4 + 255) / 256 * 256;
-        d.cnt = reinterpret_cast<unsigned*>(b);
-        d.part = reinterpret_cast<float*>(b + cnt);
-        d.ssq = reinterpret_cast<float*>(b + cnt + part);
+        d.cnt = counters;
+        d.part = reinterpret_cast<float*>(b);
+        d.ssq = reinterpret_cast<float*>(b + part);
     }
     if (a.is_bf16) {
         switch (p.mt) {

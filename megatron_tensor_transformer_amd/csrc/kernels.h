@@ -8,6 +8,13 @@
 
 namespace tpk {
 
+// Every workspace starts with a fixed header of split-K / split-KV counters
+// shared by all entry points: each call finds its counters zero and leaves
+// them zero, so one workspace can serve calls of any shape in sequence.
+// Scratch data always lives after the header, never inside it.
+constexpr size_t WS_HEADER = 32768;   // TP_WORKSPACE_HEADER
+constexpr int WS_MAX_COUNTERS = (int)(WS_HEADER / 4);
+
 enum Epilogue : int {
     EPI_STORE = 0,    // y[m, n] in the input dtype (column projection)
     EPI_PARTIAL = 1,  // y[m, n] float32 (row-parallel partial)
@@ -37,6 +44,7 @@ struct GemvArgs {
 struct GemvPlan {
     int mt;        // tokens per block (1, 2, 4, 8, 16)
     int mblocks;   // ceil(m / mt)
+    int mb_per_launch;  // m-blocks per launch, so a launch's tiles fit the counter header
     int rows_per_tile;  // weight rows a workgroup covers
     int out_per_tile;   // outputs a workgroup covers
     int n_tiles;
@@ -44,11 +52,11 @@ struct GemvPlan {
     int splits;    // S
     int threads;
     size_t lds_bytes;
-    size_t ws_bytes;   // 0 when splits == 1
+    size_t ws_bytes;   // scratch bytes after the header; 0 when splits == 1
 };
 
 GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi);
-hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, void* ws, hipStream_t stream);
+hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters, void* scratch, hipStream_t stream);
 
 // Row-wise RMSNorm into a bf16/f32 buffer: u = x * gamma / sqrt(mean(x^2) + eps).
 hipError_t rmsnorm_launch(const void* x, const void* gamma, void* u, int m, int K, float eps, int is_bf16,
@@ -76,10 +84,10 @@ struct AttnArgs {
 struct AttnPlan {
     int chunk;      // keys per workgroup
     int n_chunks;
-    size_t ws_bytes;
+    size_t ws_bytes;   // scratch bytes after the header; 0 when n_chunks == 1
 };
 AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_len);
-hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t stream);
+hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, unsigned* counters, void* scratch, hipStream_t stream);
 
 // Prefill projection on bf16 MFMA: y = epilogue(x @ W^T) for large m.
 struct GemmArgs {

@@ -355,6 +355,30 @@ def test_repeatable_and_workspace_reuse():
     torch.cuda.synchronize()
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    for w_ in (ws, aws):
+        wp, _ = tp._ws(w_)
+        off = wp - w_.data_ptr()
+        assert int(w_[off:off + 32768].sum()) == 0, "counter header not left zero"
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace, sized for the largest call, serves calls of different shapes in turn."""
+    cases = [(16, 8192, 1280, "col"), (16, 1024, 8192, "row"), (4, 4096, 7168, "col"), (16, 3584, 4096, "row"),
+             (1, 8192, 300, "col")]
+    need = max(tp.tp_linear_workspace_bytes(m, k, n, tp.TP_BF16, tp.TP_LINEAR_NORM) for m, k, n, _ in cases)
+    ws = tp.workspace(need)
+    for rep in range(2):
+        for i, (m, k, n, kind) in enumerate(cases):
+            x = W.to_bf16(W.normal(600 + i, 0, (m, k)))
+            w = W.to_bf16(W.normal(600 + i, 1, (n, k), 0.02))
+            if kind == "row":
+                y = empty((m, n), torch.float32)
+                tp.tp_row_linear_partial(dev(x, "bf16"), dev(w, "bf16"), y, ws=ws)
+            else:
+                y = empty((m, n), torch.bfloat16)
+                tp.tp_column_linear(dev(x, "bf16"), dev(w, "bf16"), y, ws=ws)
+            torch.cuda.synchronize()
+            check(f"shared workspace {kind} m={m} k={k} n={n} pass {rep}", host(y), L.linear(x, w.T), TOL["bf16"])
     wp, _ = tp._ws(ws)
     off = wp - ws.data_ptr()
-    assert int(ws[off:off + 256].sum()) == 0, "split-K counters not reset"
+    assert int(ws[off:off + 32768].sum()) == 0, "counter header not left zero"
