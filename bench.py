@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mlp_decode",
                     choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode"])
-    ap.add_argument("--tokens", type=int, default=16)
+    ap.add_argument("--tokens", type=int, default=16, help="headline batch (the workload also times 1 and 4)")
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -129,32 +129,35 @@ def timed_replays(torch, graphs, steps):
     return e0.elapsed_time(e1)
 
 
-def event_time_ms(torch, fn, n):
-    """Average ms per call of fn over n calls, one event pair around each call.
+def event_time_ms(torch, fn, n, reps=5):
+    """Average ms per call of fn: n calls launched back to back between two HIP
+    events on the stream they run on, repeated ``reps`` times.
 
     A spin kernel first keeps the stream busy while every launch is queued, so
-    no event pair waits on the host."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    torch.cuda.synchronize()
-    gpu_hold(torch, 5.0 + 0.05 * n)
-    for i in range(n):
-        starts[i].record()
-        fn(i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    ts = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(ts)), float(np.median(ts)), float(np.min(ts))
+    the timed region never waits on the host. Returns (mean, median, min) over
+    the repetitions of the per-call average."""
+    per = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        gpu_hold(torch, 5.0 + 0.05 * n)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / n)
+    return float(np.mean(per)), float(np.median(per)), float(np.min(per))
 
 
 def bench_mlp_decode(args, torch, tp, W, dev):
     wl = W.WORKLOADS[2]
     H, I, t, M = wl.hidden, wl.intermediate, wl.t, args.tokens
     log(f"[bench] drawing {wl.name}")
-    inp = W.mlp_inputs(2, H, I, M, "bf16", "ones")
+    inp = W.mlp_inputs(2, H, I, max(wl.tokens), "bf16", "ones")
     desc = tp.make_desc(H, I, eps=wl.eps)
     plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
-    x = dev(inp["x"])
+    I_r = plans[0].inter_cols
     gam = dev(inp["gamma"])
     copies = []
     for c in range(args.copies):
@@ -165,16 +168,56 @@ def bench_mlp_decode(args, torch, tp, W, dev):
                           "w_gate": dev(inp["w_gate"][:, b:b + n].T), "w_up": dev(inp["w_up"][:, b:b + n].T),
                           "w_down": dev(inp["w_down"][b:b + n].T)})
         copies.append(ranks)
+    ws = tp.workspace(max(tp.tp_layer_workspace_bytes(desc, p, tp.TP_STAGE_MLP, max(wl.tokens), tp.TP_BF16)
+                          for p in plans))
+    nlaunch = max(len(copies) * t * 16, 64)
+
+    def step_fn(x, parts, out):
+        def step(i):
+            ranks = copies[i % len(copies)]
+            for r, p in enumerate(plans):
+                tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], x, parts[r], ws=ws)
+            tp.tp_partial_sum(parts, out)
+        return step
+
+    # one rank's shard and its dominant kernel, at every batch size of the workload
+    per_batch = {}
+    for m in sorted(set(wl.tokens) | {M}):
+        x = dev(inp["x"][:m])
+        part = torch.empty(m, H, device="cuda")
+        a_out = torch.empty(m, I_r, dtype=torch.bfloat16, device="cuda")
+
+        def shard(i):
+            rw = copies[(i // t) % len(copies)][i % t]
+            tp.tp_layer_shard_forward(desc, plans[i % t], tp.TP_STAGE_MLP, rw, x, part, ws=ws)
+
+        def gateup(i):
+            rw = copies[(i // t) % len(copies)][i % t]
+            tp.tp_column_linear(x, rw["w_gate"], a_out, w_up=rw["w_up"], gamma=gam, eps=wl.eps, ws=ws)
+
+        for i in range(16):
+            shard(i)
+            gateup(i)
+        s_mean, s_med, s_min = event_time_ms(torch, shard, nlaunch)
+        k_mean, k_med, k_min = event_time_ms(torch, gateup, nlaunch)
+        shard_bytes = 3 * I_r * H * 2 + m * H * 2 + H * 2 + m * H * 4
+        gu_bytes = 2 * I_r * H * 2 + m * H * 2 + H * 2 + m * I_r * 2
+        per_batch[m] = {
+            "shard_us": s_mean * 1e3, "shard_us_median": s_med * 1e3, "shard_us_min": s_min * 1e3,
+            "shard_bytes": shard_bytes, "shard_GBps": shard_bytes / (s_mean * 1e-3) / 1e9,
+            "shard_pct_hbm_peak": 100 * shard_bytes / (s_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "tokens_per_s_one_layer_shard": m / (s_mean * 1e-3),
+            "gateup_us": k_mean * 1e3, "gateup_us_median": k_med * 1e3, "gateup_us_min": k_min * 1e3,
+            "gateup_bytes": gu_bytes, "gateup_GBps": gu_bytes / (k_mean * 1e-3) / 1e9,
+        }
+        log(f"[bench] m={m}: rank shard {s_mean * 1e3:.2f} us ({per_batch[m]['shard_GBps']:.0f} GB/s), "
+            f"gate/up {k_mean * 1e3:.2f} us ({per_batch[m]['gateup_GBps']:.0f} GB/s)")
+
+    # the timed step at the headline batch: all t rank shards + the sum of partials
+    x = dev(inp["x"][:M])
     parts = [torch.empty(M, H, device="cuda") for _ in range(t)]
     out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
-    ws = tp.workspace(max(tp.tp_layer_workspace_bytes(desc, p, tp.TP_STAGE_MLP, M, tp.TP_BF16) for p in plans))
-
-    def step(i):
-        ranks = copies[i % len(copies)]
-        for r, p in enumerate(plans):
-            tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], x, parts[r], ws=ws)
-        tp.tp_partial_sum(parts, out)
-
+    step = step_fn(x, parts, out)
     log(f"[bench] warmup {args.warmup} eager steps")
     for i in range(args.warmup):
         step(i)
@@ -187,31 +230,7 @@ def bench_mlp_decode(args, torch, tp, W, dev):
     total_ms = timed_replays(torch, graphs, args.steps)
     ms_step = total_ms / args.steps
 
-    # dominant kernel: fused RMSNorm + gate/up + SwiGLU column projection of one rank
-    a_out = torch.empty(M, plans[0].inter_cols, dtype=torch.bfloat16, device="cuda")
-    lws = tp.workspace(tp.tp_linear_workspace_bytes(M, H, plans[0].inter_cols, tp.TP_BF16,
-                                                    tp.TP_LINEAR_SWIGLU | tp.TP_LINEAR_NORM))
-    nlaunch = max(len(copies) * t * 20, 64)
-
-    def gateup(i):
-        ranks = copies[(i // t) % len(copies)]
-        rw = ranks[i % t]
-        tp.tp_column_linear(x, rw["w_gate"], a_out, w_up=rw["w_up"], gamma=gam, eps=wl.eps, ws=lws)
-
-    for i in range(16):
-        gateup(i)
-    k_mean, k_med, k_min = event_time_ms(torch, gateup, nlaunch)
-    I_r = plans[0].inter_cols
-    gu_bytes = 2 * I_r * H * 2 + M * H * 2 + H * 2 + M * I_r * 2
-    achieved = gu_bytes / (k_mean * 1e-3) / 1e9
-
-    # whole rank shard, for per-shard HBM rate
-    def shard(i):
-        ranks = copies[(i // t) % len(copies)]
-        tp.tp_layer_shard_forward(desc, plans[i % t], tp.TP_STAGE_MLP, ranks[i % t], x, parts[i % t], ws=ws)
-
-    s_mean, s_med, s_min = event_time_ms(torch, shard, nlaunch)
-    shard_bytes = 3 * I_r * H * 2 + M * H * 2 + H * 2 + M * H * 4
+    hb = per_batch[M]
     res = {
         "metric": METRIC,
         "value": M * args.steps / (total_ms * 1e-3),
@@ -228,19 +247,16 @@ def bench_mlp_decode(args, torch, tp, W, dev):
         "config": {"workload": "Llama-3-8B-shaped MLP decode block, all t=4 rank shards + on-device sum of partials",
                    "hidden": H, "intermediate": I, "t": t, "tokens": M, "rmsnorm_eps": wl.eps,
                    "weight_copies_rotated": len(copies)},
-        "per_rank_shard": {"us_mean": s_mean * 1e3, "us_median": s_med * 1e3, "us_min": s_min * 1e3,
-                           "algorithmic_bytes": shard_bytes,
-                           "GBps": shard_bytes / (s_mean * 1e-3) / 1e9,
-                           "pct_hbm_peak": 100 * shard_bytes / (s_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                           "tokens_per_s_one_layer_shard": M / (s_mean * 1e-3)},
-        "roofline": {"kernel": "gemv_kernel (fused RMSNorm + gate/up + SwiGLU column projection, one rank)",
-                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "bytes_per_launch": gu_bytes, "us_mean": k_mean * 1e3, "us_median": k_med * 1e3,
-                     "us_min": k_min * 1e3},
+        "step_GBps": 4 * hb["shard_bytes"] / (ms_step * 1e-3) / 1e9,
+        "per_rank_shard": {str(m): v for m, v in per_batch.items()},
+        "roofline": {"kernel": "gemv_kernel (fused RMSNorm + gate/up + SwiGLU column projection, one rank shard)",
+                     "bound": "hbm", "achieved": hb["gateup_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": hb["gateup_GBps"] / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": hb["gateup_bytes"], "us_mean": hb["gateup_us"],
+                     "us_median": hb["gateup_us_median"], "us_min": hb["gateup_us_min"]},
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline_mlp(inp, t, M, wl.eps, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline_mlp({**inp, "x": inp["x"][:M]}, t, M, wl.eps, args.cpu_seconds)
     return res
 
 

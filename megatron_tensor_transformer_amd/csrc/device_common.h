@@ -15,15 +15,16 @@ __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v <
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// Round to nearest even; NaN stays NaN.
+// float -> bf16 with round-to-nearest-even (one v_cvt_pk_bf16_f32 per pair on gfx950).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    const __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    bf16x2_t v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi on packed bf16 pairs (v_dot2 on gfx950).
@@ -100,6 +101,79 @@ template <int V>
 __device__ __forceinline__ void reduce_scatter16(float* v, int sub) {
     static_assert(V >= 1 && (V & (V - 1)) == 0, "V must be a power of two");
     rs_stage<0, V>(v, sub);
+}
+
+// Cross-row exchange stages for 64-lane reductions. v_permlane32_swap on the
+// pair (x, y) leaves x with its upper 32 lanes replaced by the lower 32 lanes
+// of y, and y with its lower 32 lanes replaced by the upper 32 lanes of x; the
+// sum of the two results is, in lanes 0-31, x plus its partner's x and, in
+// lanes 32-63, y plus its partner's y. permlane16_swap does the same for the
+// 16-lane halves of each 32-lane half. So one swap and one add reduce a pair
+// of values across the exchange with no lane-dependent selects.
+template <int ST>
+__device__ __forceinline__ void xrow_pair(float& x, float& y) {
+    const uint32_t xi = __float_as_uint(x), yi = __float_as_uint(y);
+    uint32_t a, b;
+    if constexpr (ST == 0) {
+        const auto r = __builtin_amdgcn_permlane32_swap(xi, yi, false, false);
+        a = r[0]; b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(xi, yi, false, false);
+        a = r[0]; b = r[1];
+    }
+    x = __uint_as_float(a) + __uint_as_float(b);
+}
+
+template <int ST, int N>
+__device__ __forceinline__ void rs64_stage(float* v, int lane) {
+    if constexpr (ST < 2) {
+        if constexpr (N > 1) {
+            constexpr int H = N / 2;
+#pragma unroll
+            for (int j = 0; j < H; ++j) xrow_pair<ST>(v[j], v[H + j]);
+            rs64_stage<ST + 1, H>(v, lane);
+        } else {
+            float y = v[0];
+            xrow_pair<ST>(v[0], y);
+            rs64_stage<ST + 1, 1>(v, lane);
+        }
+    } else {
+        rs_stage<ST - 2, N>(v, lane & 15);
+    }
+}
+
+// Reduce V values over all 64 lanes and scatter the sums: the two cross-row
+// stages (lane bit 5, then bit 4) use permlane swaps, the four in-row stages
+// (bits 3..0) use DPP. Each lane ends with max(V/64, 1) sums in v[0..);
+// reduce64_index names them.
+template <int V>
+__device__ __forceinline__ void reduce_scatter64(float* v, int lane) {
+    static_assert(V >= 1 && (V & (V - 1)) == 0, "V must be a power of two");
+    rs64_stage<0, V>(v, lane);
+}
+
+template <int V>
+__device__ __forceinline__ int reduce64_index(int lane, int j, bool& owner) {
+    int idx = 0, n = V;
+    owner = true;
+#pragma unroll
+    for (int st = 0; st < 6; ++st) {
+        const int bit = (lane >> (5 - st)) & 1;
+        if (n > 1) {
+            n /= 2;
+            idx += bit * n;
+        } else if (bit) {
+            owner = false;
+        }
+    }
+    return idx + j;
+}
+
+// Sum over the 64 lanes of a wave, every lane receiving it (permlane + DPP).
+__device__ __forceinline__ float wave_sum(float v) {
+    float t[1] = {v};
+    rs64_stage<0, 1>(t, threadIdx.x & 63);
+    return t[0];
 }
 
 // Value index held in slot j of lane `sub` after reduce_scatter16<V>; lanes

@@ -3,23 +3,21 @@
 //
 // Decode reads each weight byte once and does M multiply-adds with it, so the
 // kernel is bound by HBM for small M and close to the VALU limit at M = 16.
-// Layout of the work:
-//  - A workgroup (NW waves) owns a tile of weight rows and one K chunk. The
-//    activation chunk [MT, kc] is staged in LDS once per workgroup (gamma
-//    folded in when RMSNorm is fused) and reused by every row of the tile.
-//  - A wave is split into 64/G groups of G lanes; a group walks one weight row
-//    with 128-bit loads, so each load instruction reads 64/G rows x G*16
-//    contiguous bytes. Each lane handles RWG rows, keeping RWG x MT float32
-//    accumulators; the activation vector read from LDS is shared by those rows.
+// A decode-sized matrix is only a few HBM latencies' worth of bytes, so the
+// design goal is to have every byte requested as early as possible:
+//  - A workgroup (4 waves) owns a tile of weight rows and one K chunk. Each
+//    wave owns RW rows; one load instruction reads 1 KB of one row (64 lanes
+//    x 128 bits), and the plan sizes the chunk so that a lane's whole share
+//    (at most PF vectors per row) is requested at the start, before anything
+//    else happens. No loop carries loads.
+//  - The activation chunk [MT, kc] is staged in LDS once per workgroup (gamma
+//    folded in when RMSNorm is fused) and read by every row of the tile.
 //  - bf16 products use v_dot2 (two multiply-adds per lane per instruction,
 //    float32 accumulation, no unpacking); float32 inputs use fma.
-//  - Every lane keeps PF steps of weight vectors in flight (a register ring
-//    refilled as each step is consumed), so a workgroup's whole share of a
-//    decode-sized matrix is requested at once.
-//  - The 16 lanes of a group are reduced by a DPP reduce-scatter (row mirror,
-//    half mirror, quad permutes) in a fixed order; each lane ends with its
-//    share of the sums, which go through a small LDS tile so the epilogue
-//    writes outputs in coalesced order.
+//  - The 64 lanes of a row are reduced by a reduce-scatter: permlane32/16 swaps
+//    across rows, then DPP within rows, in a fixed order; each lane ends with
+//    its share of the sums, which pass through a small LDS tile so the
+//    epilogue writes outputs in coalesced order.
 //  - When K is split over S workgroups, each publishes its float32 tile with
 //    agent-scope coherent stores and bumps a per-tile counter; the last to
 //    arrive sums the S slices in split order (deterministic), runs the
@@ -31,13 +29,15 @@
 
 namespace tpk {
 
-constexpr int GEMV_G = 16;     // lanes per weight row
-constexpr int GEMV_NW = 4;     // waves per workgroup
 constexpr size_t GEMV_X_LDS = 64 * 1024;   // LDS budget for the staged activation chunk
+constexpr int GEMV_NW = 4;                 // waves per workgroup
 
-template <int MT> struct RowsPerLane { static constexpr int v = MT >= 8 ? 4 : 2; };
-template <int MT> struct Prefetch { static constexpr int v = MT >= 8 ? 4 : 8; };
-static int rows_per_tile(int mt) { return GEMV_NW * (64 / GEMV_G) * (mt >= 8 ? 4 : 2); }
+// Per token-block size: rows per wave (RW) and the most K steps a lane keeps
+// in flight (PF). A step is one 128-bit vector per lane, 64 lanes wide.
+template <int MT> struct RowsPerWave { static constexpr int v = MT >= 8 ? 4 : 2; };
+template <int MT> struct StepsInFlight { static constexpr int v = MT >= 8 ? 4 : 8; };
+static int rows_per_wave(int mt) { return mt >= 8 ? 4 : 2; }
+static int steps_in_flight(int mt) { return mt >= 8 ? 4 : 8; }
 
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> { static constexpr int vec = 8; };
@@ -114,45 +114,42 @@ struct GemvDev {
 
 template <typename T, int MT, int EPI, bool NORM>
 __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
-    constexpr int G = GEMV_G;
     constexpr int NW = GEMV_NW;
     constexpr int NT = NW * 64;
     constexpr int VEC = Elem<T>::vec;
-    constexpr int RWG = RowsPerLane<MT>::v;
-    constexpr int PF = Prefetch<MT>::v;    // steps of weight vectors kept in flight
-    constexpr int GROUPS = 64 / G;
-    constexpr int RPW = GROUPS * RWG;
-    constexpr int RPT = NW * RPW;
+    constexpr int RW = RowsPerWave<MT>::v;
+    constexpr int PF = StepsInFlight<MT>::v;
+    constexpr int RPT = NW * RW;             // weight rows per workgroup
     constexpr bool SWI = (EPI == EPI_SWIGLU);
     constexpr int HALF = RPT / 2;
     constexpr int OUTS = SWI ? HALF : RPT;
-    constexpr int STEP = G * VEC;   // K elements one group covers per step
-    constexpr int NV = RWG * MT;    // sums per lane before the group reduction
-    constexpr int NKEEP = NV >= 16 ? NV / 16 : 1;
+    constexpr int STEP = 64 * VEC;           // K elements of one row per wave instruction
+    constexpr int NV = RW * MT;              // sums per lane before the wave reduction
+    constexpr int NKEEP = NV >= 64 ? NV / 64 : 1;
 
     const GemvArgs& a = d.a;
+    constexpr int XW = PF * STEP;            // staged activation row length (elements)
+    constexpr int RPWV = (MT + NW - 1) / NW; // activation rows a wave stages
     extern __shared__ __align__(16) unsigned char smem[];
-    const int kc = d.kc;
-    T* xs = reinterpret_cast<T*>(smem);
-    float* res = reinterpret_cast<float*>(smem + (size_t)MT * kc * sizeof(T));
-    float* ssl = res + MT * RPT;
+    T* xs = reinterpret_cast<T*>(smem);                                        // [MT][XW]
+    float* res = reinterpret_cast<float*>(smem + (size_t)MT * XW * sizeof(T));  // [MT][RPT]
+    float* ssl = res + MT * RPT;                                               // [MT]
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int grp = lane / G, sub = lane % G;
     const int tile = blockIdx.x, split = blockIdx.y, mb = d.mb0 + blockIdx.z;
     const int K = a.K, N = a.N;
-    const int k0 = split * kc;
-    const int klen = min(kc, K - k0);
+    const int k0 = split * d.kc;
+    const int klen = min(d.kc, K - k0);      // a multiple of VEC, at most XW
     const int m0 = mb * MT;
     const int mvalid = min(MT, a.m - m0);
 
-    // Weight rows of this lane. Rows past N are clamped to a valid row; their
+    // Weight rows of this wave. Rows past N are clamped to a valid row; their
     // results are never stored.
-    const T* wrow[RWG];
+    const T* wrow[RW];
 #pragma unroll
-    for (int rg = 0; rg < RWG; ++rg) {
-        const int rho = wave * RPW + rg * GROUPS + grp;
+    for (int r = 0; r < RW; ++r) {
+        const int rho = wave * RW + r;
         int n;
         const T* base;
         if (SWI) {
@@ -163,90 +160,100 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
             base = reinterpret_cast<const T*>(a.w);
         }
         n = min(n, N - 1);
-        wrow[rg] = base + (size_t)n * K + k0;
+        wrow[r] = base + (size_t)n * K + k0;
     }
-    const int steps = (klen + STEP - 1) / STEP;
 
-    auto load_w = [&](uint4* dst, int j) {
-        const int k = (j * G + sub) * VEC;
-#pragma unroll
-        for (int rg = 0; rg < RWG; ++rg) {
-            dst[rg] = (k < klen) ? load_stream_u4(wrow[rg] + k) : make_uint4(0, 0, 0, 0);
-        }
-    };
-
-    // Put PF steps of weight loads in flight before staging the activations:
-    // they do not depend on them, so their latency overlaps the staging.
-    uint4 wbuf[PF][RWG];
-#pragma unroll
-    for (int u = 0; u < PF; ++u) load_w(wbuf[u], u);
-
-    // Stage the activation chunk (times gamma) and its sum of squares. Each
-    // wave stages whole rows; all loads of a row are issued before any store.
+    // Loads are issued in the order they are needed and without control flow:
+    // activations (and gamma) first, then the lane's whole share of weights.
+    // Offsets past the chunk are clamped to its last vector and the value
+    // zeroed, so every load is in bounds and none is conditional; waiting for
+    // the activations then leaves every weight load in flight.
     const T* x = reinterpret_cast<const T*>(a.x);
     const T* gam = reinterpret_cast<const T*>(a.gamma);
+    const bool stager = (MT >= NW) || (wave < MT);   // waves with activation rows to stage
+    uint4 xr[RPWV][PF];
+    uint4 gr[PF];
+    if (stager) {
 #pragma unroll
-    for (int mi = 0; mi < (MT + NW - 1) / NW; ++mi) {
-        const int mm = wave + mi * NW;
-        if (mm >= MT) break;
-        float ss = 0.f;
-        for (int c = lane; c < kc / VEC; c += 64) {
-            const int k = c * VEC;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (mm < mvalid && k < klen) {
-                v = load_u4(x + (size_t)(m0 + mm) * K + k0 + k);
-                if (NORM) {
-                    ss += vsumsq(v, (T*)nullptr);
-                    v = vscale(v, load_u4(gam + k0 + k), (T*)nullptr);
-                }
+        for (int i = 0; i < RPWV; ++i) {
+            const int mm = wave + i * NW;
+            const int row = m0 + min(mm, mvalid - 1);
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int k = (u * 64 + lane) * VEC;
+                const bool ok = mm < mvalid && k < klen;
+                const uint4 v = load_u4(x + (size_t)row * K + k0 + min(k, klen - VEC));
+                xr[i][u] = ok ? v : make_uint4(0, 0, 0, 0);
             }
-            *reinterpret_cast<uint4*>(xs + (size_t)mm * kc + k) = v;
         }
         if (NORM) {
-            ss = group_sum<64>(ss);
-            if (lane == 0) ssl[mm] = ss;
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const int k = (u * 64 + lane) * VEC;
+                gr[u] = load_u4(gam + k0 + min(k, klen - VEC));
+            }
+        }
+    }
+    uint4 wv[PF][RW];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        const int k = (u * 64 + lane) * VEC;
+        const int kk = min(k, klen - VEC);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const uint4 v = load_stream_u4(wrow[r] + kk);
+            wv[u][r] = k < klen ? v : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    // Stage the activation rows (times gamma) in LDS with their sums of squares.
+    if (stager) {
+#pragma unroll
+        for (int i = 0; i < RPWV; ++i) {
+            const int mm = wave + i * NW;
+            if (mm >= MT) break;
+            float ss = 0.f;
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                uint4 v = xr[i][u];
+                if (NORM) {
+                    ss += vsumsq(v, (T*)nullptr);
+                    v = vscale(v, gr[u], (T*)nullptr);
+                }
+                *reinterpret_cast<uint4*>(xs + (size_t)mm * XW + (u * 64 + lane) * VEC) = v;
+            }
+            if (NORM) {
+                ss = wave_sum(ss);
+                if (lane == 0) ssl[mm] = ss;
+            }
         }
     }
     __syncthreads();
 
-    float acc[RWG][MT];
+    float acc[NV];
 #pragma unroll
-    for (int rg = 0; rg < RWG; ++rg)
+    for (int i = 0; i < NV; ++i) acc[i] = 0.f;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) acc[rg][m] = 0.f;
-
-    for (int j0 = 0; j0 < steps; j0 += PF) {
+    for (int u = 0; u < PF; ++u) {
+        const int k = (u * 64 + lane) * VEC;
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            const int j = j0 + u;
-            if (j < steps) {
-                const int k = (j * G + sub) * VEC;
+        for (int m = 0; m < MT; ++m) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * XW + k);
 #pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const uint4 xv = *reinterpret_cast<const uint4*>(xs + (size_t)m * kc + k);
-#pragma unroll
-                    for (int rg = 0; rg < RWG; ++rg) acc[rg][m] = vdot(wbuf[u][rg], xv, acc[rg][m], (T*)nullptr);
-                }
-                load_w(wbuf[u], j + PF);
-            }
+            for (int r = 0; r < RW; ++r) acc[r * MT + m] = vdot(wv[u][r], xv, acc[r * MT + m], (T*)nullptr);
         }
     }
 
-    // Reduce every row over its 16 lanes and scatter the sums over them; each
-    // lane then writes its share of the tile to LDS.
-    float v[NV];
-#pragma unroll
-    for (int rg = 0; rg < RWG; ++rg)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) v[rg * MT + m] = acc[rg][m];
-    reduce_scatter16<NV>(v, sub);
+    // Reduce every (row, token) sum over the wave's 64 lanes and scatter the
+    // results; each lane writes its share of the tile to LDS.
+    reduce_scatter64<NV>(acc, lane);
 #pragma unroll
     for (int j = 0; j < NKEEP; ++j) {
         bool owner;
-        const int idx = reduce16_index<NV>(sub, j, owner);
+        const int idx = reduce64_index<NV>(lane, j, owner);
         if (owner) {
-            const int rg = idx / MT, m = idx % MT;
-            res[m * RPT + wave * RPW + rg * GROUPS + grp] = v[j];
+            const int r = idx / MT, m = idx % MT;
+            res[m * RPT + wave * RW + r] = acc[j];
         }
     }
     __syncthreads();
@@ -314,40 +321,37 @@ GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
     p.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
     if (!is_bf16 && p.mt != 1 && p.mt != 4) p.mt = (m <= 4) ? 4 : 16;
     p.mblocks = (m + p.mt - 1) / p.mt;
-    p.rows_per_tile = rows_per_tile(p.mt);
+    p.nw = GEMV_NW;
+    p.rows_per_tile = GEMV_NW * rows_per_wave(p.mt);
     p.out_per_tile = (epi == EPI_SWIGLU) ? p.rows_per_tile / 2 : p.rows_per_tile;
     p.n_tiles = (N + p.out_per_tile - 1) / p.out_per_tile;
     const int esz = is_bf16 ? 2 : 4;
-    const int step = GEMV_G * (16 / esz);
+    const int step = 64 * (16 / esz);
     const int kround = (K + step - 1) / step * step;
-    int kc_max = (int)(GEMV_X_LDS / ((size_t)p.mt * esz)) / step * step;
+    // A chunk is at most PF steps (every load of a lane in flight at once) and
+    // its activations must fit the LDS budget.
+    int kc_max = steps_in_flight(p.mt) * step;
+    const int kc_lds = (int)(GEMV_X_LDS / ((size_t)p.mt * esz)) / step * step;
+    if (kc_lds < kc_max) kc_max = kc_lds;
     if (kc_max > kround) kc_max = kround;
-    int S = (kround + kc_max - 1) / kc_max;
-    // Split K further until the grid covers the 256 compute units about twice,
-    // keeping at least 4 steps per group.
-    const int target = 512;
-    while ((long)p.n_tiles * S * p.mblocks < target) {
-        const int kc_next = ((kround + S) / (S + 1) + step - 1) / step * step;
-        if (kc_next < 4 * step) break;
-        ++S;
-    }
-    int kc = ((kround + S - 1) / S + step - 1) / step * step;
-    S = (K + kc - 1) / kc;
+    // Shrink the chunk (more K splits) while the grid is short of about two
+    // workgroups per compute unit, down to two steps per chunk.
+    const long target = 512;
+    int kc = kc_max;
+    while (kc > 2 * step && (long)p.n_tiles * ((kround + kc - 1) / kc) * p.mblocks < target) kc -= step;
+    int S = (K + kc - 1) / kc;
     p.mb_per_launch = p.mblocks;
     if (S > 1 && (size_t)p.n_tiles * p.mblocks > (size_t)WS_MAX_COUNTERS) {
         // one counter per tile: run the m-blocks in launches that fit the header
         p.mb_per_launch = WS_MAX_COUNTERS / p.n_tiles;
-        if (p.mb_per_launch < 1) {       // N beyond 2^18 outputs: no split
-            p.mb_per_launch = p.mblocks;
-            kc = kround;
-            S = 1;
-        }
+        if (p.mb_per_launch < 1) p.mb_per_launch = 1;
     }
     const size_t tiles = (size_t)p.n_tiles * p.mb_per_launch;
     p.kc = kc;
     p.splits = S;
     p.threads = GEMV_NW * 64;
-    p.lds_bytes = (size_t)p.mt * kc * esz + (size_t)p.mt * p.rows_per_tile * 4 + (size_t)p.mt * 4;
+    p.lds_bytes = (size_t)p.mt * steps_in_flight(p.mt) * step * esz + (size_t)p.mt * p.rows_per_tile * 4 +
+                  (size_t)p.mt * 4;
     if (S > 1) {
         const size_t part = tiles * S * p.mt * p.rows_per_tile * 4;
         const size_t ssq = tiles * S * p.mt * 4;
@@ -366,7 +370,7 @@ static hipError_t launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
     static bool lds_raised = false;
     if (p.lds_bytes > 64 * 1024 && !lds_raised) {
         // the most this instantiation can ask for: the activation budget plus its result tile
-        const int most = (int)(GEMV_X_LDS + (size_t)MT * rows_per_tile(MT) * 4 + MT * 4);
+        const int most = (int)p.lds_bytes;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, most);
         if (e != hipSuccess) {
@@ -387,13 +391,18 @@ static hipError_t launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
 }
 
 template <typename T, int MT>
-static hipError_t launch_epi(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
+static hipError_t launch_mt(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
     const bool nrm = d.a.norm != 0;
     switch (d.a.epi) {
-        case EPI_STORE: return nrm ? launch_t<T, MT, EPI_STORE, true>(d, p, s) : launch_t<T, MT, EPI_STORE, false>(d, p, s);
+        case EPI_STORE:
+            return nrm ? launch_t<T, MT, EPI_STORE, true>(d, p, s) : launch_t<T, MT, EPI_STORE, false>(d, p, s);
         case EPI_PARTIAL: return launch_t<T, MT, EPI_PARTIAL, false>(d, p, s);
-        case EPI_SWIGLU: return nrm ? launch_t<T, MT, EPI_SWIGLU, true>(d, p, s) : launch_t<T, MT, EPI_SWIGLU, false>(d, p, s);
-        case EPI_QKV: return nrm ? launch_t<T, MT, EPI_QKV, true>(d, p, s) : launch_t<T, MT, EPI_QKV, false>(d, p, s);
+        case EPI_SWIGLU:
+            return nrm ? launch_t<T, MT, EPI_SWIGLU, true>(d, p, s) : launch_t<T, MT, EPI_SWIGLU, false>(d, p, s);
+        case EPI_QKV:
+            if constexpr (sizeof(T) == 2)
+                return nrm ? launch_t<T, MT, EPI_QKV, true>(d, p, s) : launch_t<T, MT, EPI_QKV, false>(d, p, s);
+            break;
     }
     return hipErrorInvalidValue;
 }
@@ -414,18 +423,18 @@ hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters,
     }
     if (a.is_bf16) {
         switch (p.mt) {
-            case 1: return launch_epi<uint16_t, 1>(d, p, s);
-            case 2: return launch_epi<uint16_t, 2>(d, p, s);
-            case 4: return launch_epi<uint16_t, 4>(d, p, s);
-            case 8: return launch_epi<uint16_t, 8>(d, p, s);
-            case 16: return launch_epi<uint16_t, 16>(d, p, s);
+            case 1: return launch_mt<uint16_t, 1>(d, p, s);
+            case 2: return launch_mt<uint16_t, 2>(d, p, s);
+            case 4: return launch_mt<uint16_t, 4>(d, p, s);
+            case 8: return launch_mt<uint16_t, 8>(d, p, s);
+            case 16: return launch_mt<uint16_t, 16>(d, p, s);
         }
     } else {
         if (a.epi == EPI_QKV) return hipErrorInvalidValue;
         switch (p.mt) {
-            case 1: return launch_epi<float, 1>(d, p, s);
-            case 4: return launch_epi<float, 4>(d, p, s);
-            case 16: return launch_epi<float, 16>(d, p, s);
+            case 1: return launch_mt<float, 1>(d, p, s);
+            case 4: return launch_mt<float, 4>(d, p, s);
+            case 16: return launch_mt<float, 16>(d, p, s);
         }
     }
     return hipErrorInvalidValue;

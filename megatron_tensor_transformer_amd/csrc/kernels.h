@@ -43,6 +43,7 @@ struct GemvArgs {
 
 struct GemvPlan {
     int mt;        // tokens per block (1, 2, 4, 8, 16)
+    int nw;        // waves per workgroup (1 or 4)
     int mblocks;   // ceil(m / mt)
     int mb_per_launch;  // m-blocks per launch, so a launch's tiles fit the counter header
     int rows_per_tile;  // weight rows a workgroup covers
