@@ -72,6 +72,9 @@ __device__ __forceinline__ float dpp_stage(float v) {
     else return dpp_mov<DPP_QUAD_XOR1>(v);
 }
 
+// DPP rotate by 8 within 16 lanes: lane i reads lane i ^ 8.
+constexpr int DPP_ROW_ROR8 = 0x128;
+
 template <int ST, int N>
 __device__ __forceinline__ void rs_stage(float* v, int sub) {
     if constexpr (ST < 4) {
@@ -174,6 +177,32 @@ __device__ __forceinline__ float wave_sum(float v) {
     float t[1] = {v};
     rs64_stage<0, 1>(t, threadIdx.x & 63);
     return t[0];
+}
+
+// Reduce V values over groups of LANES (8 or 16) consecutive lanes, scattering
+// the sums as reduce_scatter16 does (an 8-lane group uses its last 3 stages).
+template <int LANES, int V>
+__device__ __forceinline__ void reduce_scatter_group(float* v, int lane) {
+    static_assert(LANES == 8 || LANES == 16, "groups of 8 or 16 lanes");
+    if constexpr (LANES == 16) rs_stage<0, V>(v, lane & 15);
+    else rs_stage<1, V>(v, lane & 7);
+}
+template <int LANES, int V>
+__device__ __forceinline__ int reduce_group_index(int lane, int j, bool& owner) {
+    const int sub = lane & (LANES - 1);
+    int idx = 0, n = V;
+    owner = true;
+#pragma unroll
+    for (int st = (LANES == 16 ? 0 : 1); st < 4; ++st) {
+        const int bit = (sub >> (3 - st)) & 1;
+        if (n > 1) {
+            n /= 2;
+            idx += bit * n;
+        } else if (bit) {
+            owner = false;
+        }
+    }
+    return idx + j;
 }
 
 // Value index held in slot j of lane `sub` after reduce_scatter16<V>; lanes

@@ -56,9 +56,14 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // Tile order: groups of GM_GROUP_M tile rows sweep the tile columns together,
-    // so the A rows of a group and the B columns in flight stay in L2.
-    const int pid = blockIdx.x;
+    // Workgroups are dispatched to the 8 XCDs round robin; renumber them so
+    // each XCD gets a contiguous run of tiles. Then groups of GM_GROUP_M tile
+    // rows sweep the tile columns together, so the A rows of a group and the
+    // B columns in flight stay in that XCD's L2.
+    const int nblocks = d.tiles_m * d.tiles_n;
+    const int per_xcd = nblocks / 8;
+    int pid = blockIdx.x;
+    if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
     const int per_group = GM_GROUP_M * d.tiles_n;
     const int group = pid / per_group;
     const int first_m = group * GM_GROUP_M;
@@ -70,17 +75,16 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     const int M = d.M, N = d.N, K = d.K;
 
     // Global source of each thread's chunks: chunk c = tid + 256 i covers
-    // row c / 8 and k offset (c % 8) * 8 of the tile.
+    // row c / 8 and k offset (c % 8) * 8 of the tile. Rows past M or N are
+    // clamped to the last row: they only feed accumulator rows or columns that
+    // are never stored, so they need no masking.
     const uint16_t* a_src[GM_CHUNKS];
     const uint16_t* b_src[GM_CHUNKS];
-    bool a_ok[GM_CHUNKS], b_ok[GM_CHUNKS];
 #pragma unroll
     for (int i = 0; i < GM_CHUNKS; ++i) {
         const int c = tid + GM_NT * i;
         const int row = c >> 3, kc = (c & 7) * 8;
-        const int am = m0 + row;
-        a_ok[i] = am < M;
-        a_src[i] = d.x + (size_t)min(am, M - 1) * K + kc;
+        a_src[i] = d.x + (size_t)min(m0 + row, M - 1) * K + kc;
         int bn;
         const uint16_t* base;
         if (SWI) {
@@ -90,18 +94,29 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
             bn = n0 + row;
             base = d.w;
         }
-        b_ok[i] = bn < N;
         b_src[i] = base + (size_t)min(bn, N - 1) * K + kc;
     }
 
     uint4 ra[GM_CHUNKS], rb[GM_CHUNKS];
+    // A whole K tile: straight-line, unmasked loads.
     auto fetch = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < GM_CHUNKS; ++i) {
+            ra[i] = load_u4(a_src[i] + k0);
+            rb[i] = load_u4(b_src[i] + k0);
+        }
+    };
+    // The ragged last K tile: offsets past K are clamped and zeroed.
+    auto fetch_tail = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < GM_CHUNKS; ++i) {
             const int kc = ((tid + GM_NT * i) & 7) * 8;
             const bool kin = k0 + kc < K;
-            ra[i] = (a_ok[i] && kin) ? load_u4(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-            rb[i] = (b_ok[i] && kin) ? load_u4(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+            const int off = kin ? k0 : K - 8 - kc;
+            const uint4 va = load_u4(a_src[i] + off);
+            const uint4 vb = load_u4(b_src[i] + off);
+            ra[i] = kin ? va : make_uint4(0, 0, 0, 0);
+            rb[i] = kin ? vb : make_uint4(0, 0, 0, 0);
         }
     };
     auto stash = [&](int buf) {
@@ -135,12 +150,9 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     }
 
     const int KT = (K + GM_BK - 1) / GM_BK;
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) fetch((kt + 1) * GM_BK);
+    const int KT_full = K / GM_BK;           // tiles with every k inside K
+
+    auto compute = [&](int buf) {
         const uint16_t* a = As + buf * GM_BM * GM_LDK;
         const uint16_t* b = Bs + buf * GM_BN * GM_LDK;
 #pragma unroll
@@ -156,9 +168,21 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[i], fb[j], acc[i][j]);
         }
-        if (kt + 1 < KT) stash(buf ^ 1);
+    };
+
+    if (KT_full > 0) fetch(0);
+    else fetch_tail(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT_full) fetch((kt + 1) * GM_BK);
+        else fetch_tail((kt + 1) * GM_BK);
+        compute(buf);
+        stash(buf ^ 1);
         __syncthreads();
     }
+    compute((KT - 1) & 1);
 
     // Epilogue.
     const int col_l = lane & 31;
