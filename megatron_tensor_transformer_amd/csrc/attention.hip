@@ -1,104 +1,141 @@
 // Grouped-query decode attention over the heads one rank owns, split over the
 // cached keys ("split-KV").
 //
-// Grid: (key chunks, kv heads, sequences). A workgroup takes the GQ query
-// heads that share one kv head and one chunk of keys, walks the chunk in
-// passes of 256 keys with a running (max, sum, output) per head, and leaves
-// an unnormalised partial with its max and sum in the workspace. The last
-// workgroup of a (sequence, kv head) to finish, found with a counter, merges
-// the chunk partials in chunk order by their log-sum-exp weights and writes
-// the bf16 output. Partials travel through agent-scope coherent stores and
-// loads, so no cache-wide fence is needed. Reading K and V once is the
-// cost; q is staged in LDS and read by broadcast.
+// Grid: (key chunks, kv heads, sequences). A workgroup (4 waves) takes the GQ
+// query heads that share one kv head and one chunk of keys, walks the chunk
+// in passes of 256 keys (64 per wave) with a running (max, sum, output) per
+// head, and leaves an unnormalised partial with its max and sum.
+//
+// Memory is read coalesced: a key's row of D bf16 is read by D/8 lanes with
+// one 128-bit load each, so one wave instruction covers 64/(D/8) whole keys.
+// A wave requests its pass's K and V rows before any arithmetic.
+//  - Scores: each lane dots its 8 dimensions of a key with the same 8
+//    dimensions of every head of the group (v_dot2), then a DPP
+//    reduce-scatter over the key's lanes leaves each lane with one head's
+//    score.
+//  - Probabilities go to LDS as packed bf16 pairs of consecutive keys; the
+//    value pass forms (V[j][d], V[j+1][d]) pairs with one v_perm each and
+//    accumulates with v_dot2, two keys per instruction. The running sum adds
+//    the same rounded probabilities the values are weighted with.
+//  - The key groups of a wave are reduced with permlane swaps, the 4 waves
+//    through LDS.
+// When the keys are split over several chunks, a second small kernel (one
+// workgroup per sequence, kv head and query head) merges the chunk partials
+// in chunk order by their log-sum-exp weights and writes the bf16 output; the
+// kernel boundary makes the partials visible, so no counters or fences are
+// needed.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace tpk {
 
-constexpr int AT_NT = 256;       // threads; one key per thread while scoring
-constexpr int AT_PASS = 256;     // keys per pass
+constexpr int AT_NT = 256;       // threads
+constexpr int AT_PASS = 256;     // keys per pass (64 per wave)
 constexpr int AT_MAX_CHUNKS = 128;
 
 struct AttnDev {
     AttnArgs a;
     int chunk, n_chunks;
-    unsigned* cnt;   // [B * kv_heads]
     float* pml;      // [B * kv_heads][n_chunks][GQ][2] (max, sum)
     float* po;       // [B * kv_heads][n_chunks][GQ][D]
 };
 
 template <int D, int GQ>
 __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
-    constexpr int QD = D / 4;          // threads per V row (4 dims each)
-    constexpr int KG = AT_NT / QD;     // key groups in the PV phase
+    constexpr int LPK = D / 8;             // lanes per key row
+    constexpr int KPW = 64 / LPK;          // keys per wave instruction
+    constexpr int KW = AT_PASS / 4;        // keys per wave per pass
+    constexpr int NK = KW / KPW;           // K rows a lane loads per pass
+    constexpr int NP = KW / 2 / KPW;       // V row pairs a lane loads per pass
+    constexpr bool PREFETCH_V = GQ <= 8;   // keep V loads in flight during the scores
+    constexpr int NO = GQ * 8;             // output accumulators per lane
     const AttnArgs& a = d.a;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kq = lane / LPK, dq = lane % LPK;
     const int bg = b * a.kv_heads + g;
     const int jbeg = c * d.chunk;
     const int jend = min(jbeg + d.chunk, a.kv_len);
 
-    __shared__ uint32_t qs[GQ][D / 2];
-    __shared__ float ps[GQ][AT_PASS];
+    __shared__ float sc[GQ][AT_PASS];                          // scores
+    __shared__ __align__(16) uint32_t pp[AT_PASS / 2][GQ];     // probabilities of key pairs, packed bf16
     __shared__ float mrun[GQ], lrun[GQ], alpha[GQ];
     __shared__ float red[4][GQ][D];
-    __shared__ int s_last;
 
-    const uint32_t* q = reinterpret_cast<const uint32_t*>(a.q) + ((size_t)b * a.q_heads + (size_t)g * GQ) * (D / 2);
-    for (int i = tid; i < GQ * D / 2; i += AT_NT) qs[i / (D / 2)][i % (D / 2)] = q[i];
+    // this lane's 8 dimensions of every query head of the group
+    uint4 qv[GQ];
+    {
+        const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.q_heads + (size_t)g * GQ) * D;
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) qv[h] = load_u4(q + (size_t)h * D + dq * 8);
+    }
     if (tid < GQ) { mrun[tid] = -INFINITY; lrun[tid] = 0.f; }
-    __syncthreads();
 
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (size_t)bg * a.capacity * D;
     const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + (size_t)bg * a.capacity * D;
     const float scale = 1.0f / sqrtf((float)D);
-    const int dq = tid % QD, kg = tid / QD;
-    float o[GQ][4];
+    float o[NO];
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
+    for (int i = 0; i < NO; ++i) o[i] = 0.f;
 
     for (int j0 = jbeg; j0 < jend; j0 += AT_PASS) {
-        const int nk = min(AT_PASS, jend - j0);
-        // scores: thread tid scores key j0 + tid for every head of the group
-        float s[GQ];
+        const int kw0 = j0 + wave * KW;              // this wave's first key
+        // K rows (and V row pairs) of the pass, clamped to the last valid key.
+        uint4 kr[NK];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) s[h] = 0.f;
-        if (tid < nk) {
-            const uint4* kr = reinterpret_cast<const uint4*>(kbase + (size_t)(j0 + tid) * D);
-            uint4 kv[D / 8];
+        for (int i = 0; i < NK; ++i) {
+            const int key = min(kw0 + i * KPW + kq, jend - 1);
+            kr[i] = load_stream_u4(kbase + (size_t)key * D + dq * 8);
+        }
+        uint4 va[NP], vb[NP];
+        auto load_v = [&]() {
 #pragma unroll
-            for (int v = 0; v < D / 8; ++v) kv[v] = load_stream_u4(kr + v);
+            for (int i = 0; i < NP; ++i) {
+                const int key = kw0 + 2 * (i * KPW + kq);
+                va[i] = load_stream_u4(vbase + (size_t)min(key, jend - 1) * D + dq * 8);
+                vb[i] = load_stream_u4(vbase + (size_t)min(key + 1, jend - 1) * D + dq * 8);
+            }
+        };
+        if (PREFETCH_V) load_v();
+
+        // scores
 #pragma unroll
-            for (int v = 0; v < D / 8; ++v) {
+        for (int i = 0; i < NK; ++i) {
+            float s[GQ];
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    const uint4 qv = *reinterpret_cast<const uint4*>(&qs[h][4 * v]);
-                    s[h] = dot2_bf16(kv[v].x, qv.x, s[h]);
-                    s[h] = dot2_bf16(kv[v].y, qv.y, s[h]);
-                    s[h] = dot2_bf16(kv[v].z, qv.z, s[h]);
-                    s[h] = dot2_bf16(kv[v].w, qv.w, s[h]);
-                }
+            for (int h = 0; h < GQ; ++h) {
+                float t = dot2_bf16(kr[i].x, qv[h].x, 0.f);
+                t = dot2_bf16(kr[i].y, qv[h].y, t);
+                t = dot2_bf16(kr[i].z, qv[h].z, t);
+                s[h] = dot2_bf16(kr[i].w, qv[h].w, t);
+            }
+            reduce_scatter_group<LPK, GQ>(s, lane);
+            const int lk = wave * KW + i * KPW + kq;            // key within the pass
+#pragma unroll
+            for (int j = 0; j < (GQ > LPK ? GQ / LPK : 1); ++j) {
+                bool owner;
+                const int h = reduce_group_index<LPK, GQ>(lane, j, owner);
+                if (owner) sc[h][lk] = (j0 + lk < jend) ? s[j] * scale : -INFINITY;
             }
         }
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) ps[h][tid] = (tid < nk) ? s[h] * scale : -INFINITY;
+        if (!PREFETCH_V) load_v();
         __syncthreads();
 
-        // per-head running max and sum; probabilities relative to the new max
+        // running max and sum per head; probabilities relative to the new max
         for (int h = wave; h < GQ; h += 4) {
             float mx = -INFINITY;
-            for (int i = lane; i < AT_PASS; i += 64) mx = fmaxf(mx, ps[h][i]);
+            for (int i = lane; i < AT_PASS; i += 64) mx = fmaxf(mx, sc[h][i]);
             mx = group_max<64>(mx);
             const float mnew = fmaxf(mrun[h], mx);
             float sum = 0.f;
-            for (int i = lane; i < AT_PASS; i += 64) {
-                const float p = __expf(ps[h][i] - mnew);
-                ps[h][i] = p;
-                sum += p;
+            for (int i = lane; i < AT_PASS / 2; i += 64) {
+                const float p0 = __expf(sc[h][2 * i] - mnew);
+                const float p1 = __expf(sc[h][2 * i + 1] - mnew);
+                const uint32_t pk = pack_bf16x2(p0, p1);
+                pp[i][h] = pk;
+                sum += bf16lo(pk) + bf16hi(pk);
             }
-            sum = group_sum<64>(sum);
+            sum = wave_sum(sum);
             if (lane == 0) {
                 const float al = __expf(mrun[h] - mnew);
                 alpha[h] = al;
@@ -108,43 +145,70 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
         }
         __syncthreads();
 
-        // PV: thread (kg, dq) accumulates dims 4dq..4dq+3 over keys kg, kg+KG, ...
+        // values: two keys per v_dot2
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
             const float al = alpha[h];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[h][e] *= al;
+            for (int e = 0; e < 8; ++e) o[h * 8 + e] *= al;
         }
-        for (int j = kg; j < nk; j += KG) {
-            const uint2 vv = *reinterpret_cast<const uint2*>(vbase + (size_t)(j0 + j) * D + 4 * dq);
-            const float v0 = bf16lo(vv.x), v1 = bf16hi(vv.x), v2 = bf16lo(vv.y), v3 = bf16hi(vv.y);
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                const float p = ps[h][j];
-                o[h][0] = fmaf(p, v0, o[h][0]);
-                o[h][1] = fmaf(p, v1, o[h][1]);
-                o[h][2] = fmaf(p, v2, o[h][2]);
-                o[h][3] = fmaf(p, v3, o[h][3]);
+        for (int i = 0; i < NP; ++i) {
+            const int lp = (wave * KW) / 2 + i * KPW + kq;      // key pair within the pass
+            uint32_t pw[GQ];
+            if constexpr (GQ >= 4) {
+#pragma unroll
+                for (int h4 = 0; h4 < GQ; h4 += 4) {
+                    const uint4 t = *reinterpret_cast<const uint4*>(&pp[lp][h4]);
+                    pw[h4] = t.x; pw[h4 + 1] = t.y; pw[h4 + 2] = t.z; pw[h4 + 3] = t.w;
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) pw[h] = pp[lp][h];
+            }
+            const uint32_t* A = &va[i].x;
+            const uint32_t* Bv = &vb[i].x;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t lo = __builtin_amdgcn_perm(Bv[t], A[t], 0x05040100u);   // (V[j][2t],   V[j+1][2t])
+                const uint32_t hi = __builtin_amdgcn_perm(Bv[t], A[t], 0x07060302u);   // (V[j][2t+1], V[j+1][2t+1])
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) {
+                    o[h * 8 + 2 * t] = dot2_bf16(pw[h], lo, o[h * 8 + 2 * t]);
+                    o[h * 8 + 2 * t + 1] = dot2_bf16(pw[h], hi, o[h * 8 + 2 * t + 1]);
+                }
             }
         }
         __syncthreads();
     }
 
-    // reduce the key groups: lanes of a wave first, then the 4 waves via LDS
+    // Reduce over the key groups of the wave (lanes with the same dq). For
+    // D = 128 the groups differ in lane bits 4 and 5 (two permlane stages);
+    // for D = 64 also in bit 3 (a DPP stage first).
+    constexpr int N0 = (LPK == 8) ? NO / 2 : NO;
+    if constexpr (LPK == 8) {
+        const bool upper = (lane >> 3) & 1;
 #pragma unroll
-    for (int h = 0; h < GQ; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float v = o[h][e];
-#pragma unroll
-            for (int off = QD; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-            o[h][e] = v;
+        for (int j = 0; j < NO / 2; ++j) {
+            const float kp = upper ? o[NO / 2 + j] : o[j];
+            const float sd = upper ? o[j] : o[NO / 2 + j];
+            o[j] = kp + dpp_mov<DPP_ROW_ROR8>(sd);
         }
-    if (lane < QD) {
+    }
 #pragma unroll
-        for (int h = 0; h < GQ; ++h)
+    for (int j = 0; j < N0 / 2; ++j) xrow_pair<0>(o[j], o[N0 / 2 + j]);      // lane bit 5
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave][h][4 * dq + e] = o[h][e];
+    for (int j = 0; j < N0 / 4; ++j) xrow_pair<1>(o[j], o[N0 / 4 + j]);      // lane bit 4
+    // slot j of this lane now holds flat index base + j (flat index = head * 8 + element)
+    {
+        int base = ((lane >> 5) & 1) * (N0 / 2) + ((lane >> 4) & 1) * (N0 / 4);
+        if constexpr (LPK == 8) base += ((lane >> 3) & 1) * (NO / 2);
+#pragma unroll
+        for (int j = 0; j < N0 / 4; ++j) {
+            const int idx = base + j;
+            const int h = idx / 8, e = idx % 8;
+            red[wave][h][dq * 8 + e] = o[j];
+        }
     }
     __syncthreads();
 
@@ -161,39 +225,77 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
     float* po = d.po + ((size_t)bg * d.n_chunks + c) * GQ * D;
     for (int i = tid; i < GQ * D; i += AT_NT) {
         const int h = i / D, e = i % D;
-        store_coherent(po + i, red[0][h][e] + red[1][h][e] + red[2][h][e] + red[3][h][e]);
+        po[i] = red[0][h][e] + red[1][h][e] + red[2][h][e] + red[3][h][e];
     }
     if (tid < GQ) {
         float* ml = d.pml + (((size_t)bg * d.n_chunks + c) * GQ + tid) * 2;
-        store_coherent(ml, mrun[tid]);
-        store_coherent(ml + 1, lrun[tid]);
+        ml[0] = mrun[tid];
+        ml[1] = lrun[tid];
     }
-    if (!last_arriver(&d.cnt[bg], (unsigned)d.n_chunks, &s_last)) return;
+}
 
-    // merge the chunks in chunk order
-    __shared__ float wgt[AT_MAX_CHUNKS][GQ];
-    const float* mlb = d.pml + (size_t)bg * d.n_chunks * GQ * 2;
-    for (int h = wave; h < GQ; h += 4) {
-        float mx = -INFINITY;
-        for (int cc = lane; cc < d.n_chunks; cc += 64) mx = fmaxf(mx, load_coherent(mlb + (cc * GQ + h) * 2));
-        mx = group_max<64>(mx);
-        float l = 0.f;
-        for (int cc = lane; cc < d.n_chunks; cc += 64) {
-            const float w = __expf(load_coherent(mlb + (cc * GQ + h) * 2) - mx);
-            wgt[cc][h] = w;
-            l += w * load_coherent(mlb + (cc * GQ + h) * 2 + 1);
-        }
-        l = group_sum<64>(l);
-        if (lane == 0) alpha[h] = 1.0f / l;
+// Merge of the chunk partials of one (sequence, kv head, query head): weights
+// exp(m_c - max) in chunk order, out = sum_c w_c o_c / sum_c w_c l_c. One
+// thread per dimension; the partials of all chunks are requested in batches.
+template <int D, int GQ>
+__global__ __launch_bounds__(D) void attn_merge_kernel(AttnDev d) {
+    const AttnArgs& a = d.a;
+    const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int e = threadIdx.x;
+    const int bg = b * a.kv_heads + g;
+    const int nc = d.n_chunks;
+    __shared__ float wgt[AT_MAX_CHUNKS];
+    __shared__ float red[D / 64];
+    __shared__ float s_max, s_inv;
+    const float* mlb = d.pml + (size_t)bg * nc * GQ * 2;
+    // chunk maxima (nc <= AT_MAX_CHUNKS <= 2 D): each thread reads up to two
+    float m0 = -INFINITY, m1 = -INFINITY;
+    if (e < nc) m0 = mlb[((size_t)e * GQ + h) * 2];
+    if (e + D < nc) m1 = mlb[((size_t)(e + D) * GQ + h) * 2];
+    float mx = group_max<64>(fmaxf(m0, m1));
+    if ((e & 63) == 0) red[e >> 6] = mx;
+    __syncthreads();
+    if (e == 0) {
+        float t = red[0];
+        for (int w = 1; w < D / 64; ++w) t = fmaxf(t, red[w]);
+        s_max = t;
     }
     __syncthreads();
-    const float* pob = d.po + (size_t)bg * d.n_chunks * GQ * D;
-    for (int i = tid; i < GQ * D; i += AT_NT) {
-        const int h = i / D;
-        float v = 0.f;
-        for (int cc = 0; cc < d.n_chunks; ++cc) v = fmaf(wgt[cc][h], load_coherent(pob + (size_t)cc * GQ * D + i), v);
-        out[i] = (uint16_t)f32_to_bf16_bits(v * alpha[h]);
+    const float M = s_max;
+    float l = 0.f;
+    if (e < nc) {
+        const float w = __expf(m0 - M);
+        wgt[e] = w;
+        l += w * mlb[((size_t)e * GQ + h) * 2 + 1];
     }
+    if (e + D < nc) {
+        const float w = __expf(m1 - M);
+        wgt[e + D] = w;
+        l += w * mlb[((size_t)(e + D) * GQ + h) * 2 + 1];
+    }
+    l = wave_sum(l);
+    __syncthreads();
+    if ((e & 63) == 0) red[e >> 6] = l;
+    __syncthreads();
+    if (e == 0) {
+        float t = 0.f;
+        for (int w = 0; w < D / 64; ++w) t += red[w];
+        s_inv = 1.0f / t;
+    }
+    __syncthreads();
+    const float* pob = d.po + (size_t)bg * nc * GQ * D + (size_t)h * D + e;
+    constexpr int UNR = 16;
+    float acc = 0.f;
+    for (int c0 = 0; c0 < nc; c0 += UNR) {
+        float v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) v[u] = pob[(size_t)min(c0 + u, nc - 1) * GQ * D];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+            if (c0 + u < nc) acc = fmaf(wgt[c0 + u], v[u], acc);
+    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.q_heads + (size_t)g * GQ + h) * D;
+    out[e] = (uint16_t)f32_to_bf16_bits(acc * s_inv);
 }
 
 AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_len) {
@@ -201,7 +303,7 @@ AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_le
     const int gq = q_heads / kv_heads;
     const long pairs = (long)batch * kv_heads;
     // chunks of whole passes; aim for about two workgroups per compute unit
-    int passes_total = (kv_len + AT_PASS - 1) / AT_PASS;
+    const int passes_total = (kv_len + AT_PASS - 1) / AT_PASS;
     int want = (int)((512 + pairs - 1) / pairs);
     if (want < 1) want = 1;
     if (want > passes_total) want = passes_total;
@@ -210,10 +312,6 @@ AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_le
     while (n_chunks > AT_MAX_CHUNKS) {
         ++passes_per_chunk;
         n_chunks = (passes_total + passes_per_chunk - 1) / passes_per_chunk;
-    }
-    if (pairs > WS_MAX_COUNTERS) {   // one counter per (sequence, kv head): no split beyond that
-        passes_per_chunk = passes_total;
-        n_chunks = 1;
     }
     p.chunk = passes_per_chunk * AT_PASS;
     p.n_chunks = n_chunks;
@@ -231,6 +329,9 @@ template <int D, int GQ>
 static hipError_t attn_launch_t(const AttnDev& d, hipStream_t s) {
     dim3 grid(d.n_chunks, d.a.kv_heads, d.a.batch);
     hipLaunchKernelGGL((attn_decode_kernel<D, GQ>), grid, dim3(AT_NT), 0, s, d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || d.n_chunks == 1) return e;
+    hipLaunchKernelGGL((attn_merge_kernel<D, GQ>), dim3(GQ, d.a.kv_heads, d.a.batch), dim3(D), 0, s, d);
     return hipGetLastError();
 }
 
@@ -246,7 +347,8 @@ static hipError_t attn_launch_d(const AttnDev& d, int gq, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, unsigned* counters, void* scratch, hipStream_t s) {
+hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, unsigned* /*counters: unused*/, void* scratch,
+                       hipStream_t s) {
     AttnDev d{};
     d.a = a;
     d.chunk = p.chunk;
@@ -256,7 +358,6 @@ hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, unsigned* counters,
         const size_t pairs = (size_t)a.batch * a.kv_heads;
         char* b = reinterpret_cast<char*>(scratch);
         const size_t ml = (pairs * p.n_chunks * gq * 2 * 4 + 255) / 256 * 256;
-        d.cnt = counters;
         d.pml = reinterpret_cast<float*>(b);
         d.po = reinterpret_cast<float*>(b + ml);
     }

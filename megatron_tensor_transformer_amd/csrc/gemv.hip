@@ -24,8 +24,7 @@
 //    epilogue and resets the counter. No cache-wide fence is needed. RMSNorm's
 //    sum of squares travels the same way, so the normalisation stays fused:
 //    inv_rms multiplies the contraction result.
-#include "device_common.h"
-#include "kernels.h"
+#include "gemv_tile.h"
 
 namespace tpk {
 
@@ -59,59 +58,6 @@ __device__ __forceinline__ float vdot(const uint4& w, const uint4& x, float acc,
     return acc;
 }
 
-// Sum of squares of a vector and the vector scaled by gamma (rounded back to T).
-__device__ __forceinline__ float vsumsq(const uint4& v, uint16_t*) {
-    float s = 0.f;
-    const uint32_t* p = &v.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float a = bf16lo(p[i]), b = bf16hi(p[i]);
-        s = fmaf(a, a, s);
-        s = fmaf(b, b, s);
-    }
-    return s;
-}
-__device__ __forceinline__ float vsumsq(const uint4& v, float*) {
-    const uint32_t* p = &v.x;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(__uint_as_float(p[i]), __uint_as_float(p[i]), s);
-    return s;
-}
-__device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, uint16_t*) {
-    uint4 r;
-    const uint32_t* a = &v.x;
-    const uint32_t* b = &g.x;
-    uint32_t* o = &r.x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(bf16lo(a[i]) * bf16lo(b[i]), bf16hi(a[i]) * bf16hi(b[i]));
-    return r;
-}
-__device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, float*) {
-    uint4 r;
-    r.x = __float_as_uint(__uint_as_float(v.x) * __uint_as_float(g.x));
-    r.y = __float_as_uint(__uint_as_float(v.y) * __uint_as_float(g.y));
-    r.z = __float_as_uint(__uint_as_float(v.z) * __uint_as_float(g.z));
-    r.w = __float_as_uint(__uint_as_float(v.w) * __uint_as_float(g.w));
-    return r;
-}
-
-__device__ __forceinline__ void store_out(void* y, size_t idx, float v, uint16_t*) {
-    reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
-}
-__device__ __forceinline__ void store_out(void* y, size_t idx, float v, float*) {
-    reinterpret_cast<float*>(y)[idx] = v;
-}
-
-struct GemvDev {
-    GemvArgs a;
-    int kc, splits, n_tiles;
-    int mb0;           // first m-block of this launch
-    float* part;       // [tiles*mblocks][S][MT*RPT]
-    float* ssq;        // [tiles*mblocks][S][MT]
-    unsigned* cnt;     // [tiles*mblocks]
-};
-
 template <typename T, int MT, int EPI, bool NORM>
 __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     constexpr int NW = GEMV_NW;
@@ -122,7 +68,6 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     constexpr int RPT = NW * RW;             // weight rows per workgroup
     constexpr bool SWI = (EPI == EPI_SWIGLU);
     constexpr int HALF = RPT / 2;
-    constexpr int OUTS = SWI ? HALF : RPT;
     constexpr int STEP = 64 * VEC;           // K elements of one row per wave instruction
     constexpr int NV = RW * MT;              // sums per lane before the wave reduction
     constexpr int NKEEP = NV >= 64 ? NV / 64 : 1;
@@ -258,65 +203,10 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     }
     __syncthreads();
 
-    const int tile_id = blockIdx.z * d.n_tiles + tile;
-    if (d.splits > 1) {
-        // Publish this split's tile with coherent stores; the last split to
-        // arrive adds the slices in split order.
-        float* base = d.part + (size_t)tile_id * d.splits * (MT * RPT);
-        float* mine = base + (size_t)split * (MT * RPT);
-        for (int i = tid; i < MT * RPT; i += NT) store_coherent(mine + i, res[i]);
-        if (NORM && tid < MT) store_coherent(d.ssq + ((size_t)tile_id * d.splits + split) * MT + tid, ssl[tid]);
-        if (!last_arriver(&d.cnt[tile_id], (unsigned)d.splits, &s_last)) return;
-        for (int i = tid; i < MT * RPT; i += NT) {
-            float s = 0.f;
-            for (int sp = 0; sp < d.splits; ++sp) s += load_coherent(base + (size_t)sp * (MT * RPT) + i);
-            res[i] = s;
-        }
-        if (NORM && tid < MT) {
-            float s = 0.f;
-            for (int sp = 0; sp < d.splits; ++sp) s += load_coherent(d.ssq + ((size_t)tile_id * d.splits + sp) * MT + tid);
-            ssl[tid] = s;
-        }
-        __syncthreads();
-    }
-
-    // Epilogue.
-    for (int i = tid; i < mvalid * OUTS; i += NT) {
-        const int m = i / OUTS, o = i - m * OUTS;
-        const float inv = NORM ? 1.0f / sqrtf(ssl[m] / (float)K + a.eps) : 1.0f;
-        const int row = m0 + m;
-        if (SWI) {
-            const int n = tile * HALF + o;
-            if (n < N) {
-                const float g = res[m * RPT + o] * inv;
-                const float u = res[m * RPT + HALF + o] * inv;
-                store_out(a.y, (size_t)row * N + n, silu_f32(g) * u, (T*)nullptr);
-            }
-        } else {
-            const int n = tile * RPT + o;
-            if (n >= N) continue;
-            const float v = res[m * RPT + o] * inv;
-            if (EPI == EPI_PARTIAL) {
-                reinterpret_cast<float*>(a.y)[(size_t)row * N + n] = v;
-            } else if (EPI == EPI_STORE) {
-                store_out(a.y, (size_t)row * N + n, v, (T*)nullptr);
-            } else {  // EPI_QKV
-                if (n < a.q_cols) {
-                    store_out(a.y, (size_t)row * a.q_cols + n, v, (T*)nullptr);
-                } else {
-                    const int r = n - a.q_cols;
-                    const bool is_k = r < a.kv_cols;
-                    const int rr = is_k ? r : r - a.kv_cols;
-                    const int g = rr / a.head_dim, e = rr - g * a.head_dim;
-                    const size_t idx = (((size_t)row * a.kv_heads + g) * a.capacity + a.pos) * a.head_dim + e;
-                    store_out(is_k ? a.k_cache : a.v_cache, idx, v, (T*)nullptr);
-                }
-            }
-        }
-    }
+    gemv_finish<T, MT, RPT, EPI, NORM, NT>(d, res, ssl, &s_last, tile, split, m0, mvalid);
 }
 
-GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
+GemvPlan gemv_plan_dot2(int m, int K, int N, int is_bf16, int epi) {
     GemvPlan p{};
     p.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
     if (!is_bf16 && p.mt != 1 && p.mt != 4) p.mt = (m <= 4) ? 4 : 16;
@@ -360,6 +250,13 @@ GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
         p.ws_bytes = 0;
     }
     return p;
+}
+
+GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi) {
+    // bf16 blocks of several tokens go to the matrix cores; a token or two
+    // (and float32) stay on v_dot2 / fma
+    if (is_bf16 && m >= GEMV_MFMA_MIN_M) return gemv_plan_mfma(m, K, N, epi);
+    return gemv_plan_dot2(m, K, N, is_bf16, epi);
 }
 
 template <typename T, int MT, int EPI, bool NORM>
@@ -421,6 +318,7 @@ hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters,
         d.part = reinterpret_cast<float*>(b);
         d.ssq = reinterpret_cast<float*>(b + part);
     }
+    if (p.mfma) return a.is_bf16 ? gemv_mfma_launch(d, p, s) : hipErrorInvalidValue;
     if (a.is_bf16) {
         switch (p.mt) {
             case 1: return launch_mt<uint16_t, 1>(d, p, s);

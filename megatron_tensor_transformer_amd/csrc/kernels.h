@@ -42,6 +42,7 @@ struct GemvArgs {
 };
 
 struct GemvPlan {
+    int mfma;      // 1: matrix-core kernel (bf16, 16-token blocks), 0: v_dot2 / fma kernel
     int mt;        // tokens per block (1, 2, 4, 8, 16)
     int nw;        // waves per workgroup (1 or 4)
     int mblocks;   // ceil(m / mt)
@@ -56,7 +57,11 @@ struct GemvPlan {
     size_t ws_bytes;   // scratch bytes after the header; 0 when splits == 1
 };
 
-GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi);
+// Smallest bf16 token count that goes to the matrix-core kernel.
+constexpr int GEMV_MFMA_MIN_M = 5;
+GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi);        // picks one of the two below
+GemvPlan gemv_plan_dot2(int m, int K, int N, int is_bf16, int epi);
+GemvPlan gemv_plan_mfma(int m, int K, int N, int epi);                // bf16 only
 hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters, void* scratch, hipStream_t stream);
 
 // Row-wise RMSNorm into a bf16/f32 buffer: u = x * gamma / sqrt(mean(x^2) + eps).
