@@ -23,9 +23,13 @@
 //    the workgroup, so activation reads are a quarter of the weight bytes;
 //    each wave stages its own 16 weight rows. Rows are padded by 16 bytes so
 //    the operand reads of 16 rows hit distinct banks.
-//  - K is split over at most about four workgroups per tile; results (lane:
-//    one weight row, four tokens) go to an LDS tile, and the split-K merge
-//    and the epilogues are those of the v_dot2 kernel.
+//  - K is split over at most about four workgroups per tile. Unsplit, the
+//    results (lane: one weight row, four tokens) go through an LDS tile to the
+//    epilogue shared with the v_dot2 kernel. Split, each workgroup writes its
+//    float32 slice with plain stores and a small merge kernel (one workgroup
+//    per tile) adds the slices in split order and runs that epilogue: no
+//    counter vote, whose memory round trips would sit at the end of the
+//    projection kernel.
 #include "gemv_tile.h"
 
 namespace tpk {
@@ -56,7 +60,6 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_mfma_kernel(GemvDev d) {
     __shared__ __align__(16) uint16_t xl[SK_MT * SK_PITCH];
     __shared__ float res[SK_MT * SK_RPT];
     __shared__ float ssl[SK_MT];
-    __shared__ int s_last;
 
     const GemvArgs& a = d.a;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,12 +167,65 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_mfma_kernel(GemvDev d) {
             if ((lane & 31) == 0) ssl[t0 + 8 * i] = v;
         }
     }
+    if (d.splits > 1) {
+        if (NORM) __syncthreads();             // ssl written by the stagers
+        // This split's slice goes out with plain stores; the merge kernel that
+        // follows on the stream adds the slices and runs the epilogue.
+        const int tile_id = blockIdx.z * d.n_tiles + tile;
+        float* mine = d.part + ((size_t)tile_id * d.splits + split) * (SK_MT * SK_RPT);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * kg + j < mvalid) mine[(4 * kg + j) * SK_RPT + wave * 16 + col] = acc[j];
+        if (NORM && tid < mvalid) d.ssq[((size_t)tile_id * d.splits + split) * SK_MT + tid] = ssl[tid];
+        return;
+    }
     // lane holds tokens 4 kg + j of row wave * 16 + col
 #pragma unroll
     for (int j = 0; j < 4; ++j) res[(4 * kg + j) * SK_RPT + wave * 16 + col] = acc[j];
     __syncthreads();
+    gemv_epilogue<uint16_t, SK_MT, SK_RPT, EPI, NORM, NT>(a, res, ssl, tile, m0, mvalid);
+}
 
-    gemv_finish<uint16_t, SK_MT, SK_RPT, EPI, NORM, NT>(d, res, ssl, &s_last, tile, split, m0, mvalid);
+// Split-K merge: one workgroup per output tile adds the tile's slices in
+// split order (a thread requests the slices of its outputs together) and runs
+// the epilogue.
+template <int EPI, bool NORM>
+__global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
+    constexpr int NT = 256, PER = SK_MT * SK_RPT / NT, UNR = 8;
+    __shared__ float res[SK_MT * SK_RPT];
+    __shared__ float ssl[SK_MT];
+    const int tid = threadIdx.x, tile = blockIdx.x, mb = d.mb0 + blockIdx.z;
+    const int m0 = mb * SK_MT;
+    const int mvalid = min(SK_MT, d.a.m - m0);
+    const int S = d.splits;
+    const int tile_id = blockIdx.z * d.n_tiles + tile;
+    const float* base = d.part + (size_t)tile_id * S * (SK_MT * SK_RPT);
+    const int live = mvalid * SK_RPT;
+    float acc[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) acc[p] = 0.f;
+    for (int sp0 = 0; sp0 < S; sp0 += UNR) {
+        float v[PER][UNR];
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                v[p][u] = base[(size_t)min(sp0 + u, S - 1) * (SK_MT * SK_RPT) + min(tid + p * NT, live - 1)];
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+#pragma unroll
+            for (int u = 0; u < UNR; ++u)
+                if (sp0 + u < S) acc[p] += v[p][u];
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) res[tid + p * NT] = acc[p];
+    if (NORM && tid < mvalid) {
+        float t = 0.f;
+        for (int sp = 0; sp < S; ++sp) t += d.ssq[((size_t)tile_id * S + sp) * SK_MT + tid];
+        ssl[tid] = t;
+    }
+    __syncthreads();
+    gemv_epilogue<uint16_t, SK_MT, SK_RPT, EPI, NORM, NT>(d.a, res, ssl, tile, m0, mvalid);
 }
 
 GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
@@ -187,11 +243,7 @@ GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
     int kc = SK_SUB;
     while (kc < SK_MAX_STAGES * SK_SUB && (K + kc - 1) / kc > 4) kc *= 2;
     const int S = (K + kc - 1) / kc;
-    p.mb_per_launch = p.mblocks;
-    if (S > 1 && (size_t)p.n_tiles * p.mblocks > (size_t)WS_MAX_COUNTERS) {
-        p.mb_per_launch = WS_MAX_COUNTERS / p.n_tiles;
-        if (p.mb_per_launch < 1) p.mb_per_launch = 1;
-    }
+    p.mb_per_launch = p.mblocks;                // the merge uses no counters
     p.kc = kc;
     p.splits = S;
     p.threads = SK_NW * 64;
@@ -214,6 +266,11 @@ static hipError_t mfma_launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t
         hipLaunchKernelGGL((gemv_mfma_kernel<EPI, NORM, NST>), grid, dim3(p.threads), 0, s, dl);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (p.splits > 1) {
+            hipLaunchKernelGGL((gemv_mfma_merge_kernel<EPI, NORM>), dim3(p.n_tiles, 1, grid.z), dim3(256), 0, s, dl);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

@@ -64,6 +64,53 @@ __device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, float*) 
     return r;
 }
 
+// The epilogue of one output tile: res[m][RPT] are the full K sums of the
+// tile's rows for tokens m < mvalid (for SwiGLU the gate rows first, then the
+// up rows of the same outputs), ssl[m] the activations' sums of squares when
+// RMSNorm is fused.
+template <typename T, int MT, int RPT, int EPI, bool NORM, int NT>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, const float* res, const float* ssl, int tile, int m0,
+                                              int mvalid) {
+    constexpr bool SWI = (EPI == EPI_SWIGLU);
+    constexpr int HALF = RPT / 2;
+    constexpr int OUTS = SWI ? HALF : RPT;
+    const int tid = threadIdx.x;
+    const int N = a.N;
+    for (int i = tid; i < mvalid * OUTS; i += NT) {
+        const int m = i / OUTS, o = i - m * OUTS;
+        const float inv = NORM ? 1.0f / sqrtf(ssl[m] / (float)a.K + a.eps) : 1.0f;
+        const int row = m0 + m;
+        if (SWI) {
+            const int n = tile * HALF + o;
+            if (n < N) {
+                const float g = res[m * RPT + o] * inv;
+                const float u = res[m * RPT + HALF + o] * inv;
+                store_out(a.y, (size_t)row * N + n, silu_f32(g) * u, (T*)nullptr);
+            }
+        } else {
+            const int n = tile * RPT + o;
+            if (n >= N) continue;
+            const float v = res[m * RPT + o] * inv;
+            if (EPI == EPI_PARTIAL) {
+                reinterpret_cast<float*>(a.y)[(size_t)row * N + n] = v;
+            } else if (EPI == EPI_STORE) {
+                store_out(a.y, (size_t)row * N + n, v, (T*)nullptr);
+            } else {  // EPI_QKV
+                if (n < a.q_cols) {
+                    store_out(a.y, (size_t)row * a.q_cols + n, v, (T*)nullptr);
+                } else {
+                    const int r = n - a.q_cols;
+                    const bool is_k = r < a.kv_cols;
+                    const int rr = is_k ? r : r - a.kv_cols;
+                    const int g = rr / a.head_dim, e = rr - g * a.head_dim;
+                    const size_t idx = (((size_t)row * a.kv_heads + g) * a.capacity + a.pos) * a.head_dim + e;
+                    store_out(is_k ? a.k_cache : a.v_cache, idx, v, (T*)nullptr);
+                }
+            }
+        }
+    }
+}
+
 // res[MT][RPT] holds this workgroup's sums of its K chunk (rows of the tile in
 // the order the epilogue expects: for SwiGLU the gate rows, then the up rows
 // of the same outputs), ssl[MT] its sums of squares of the activations when
@@ -73,12 +120,8 @@ __device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, float*) 
 template <typename T, int MT, int RPT, int EPI, bool NORM, int NT>
 __device__ __forceinline__ void gemv_finish(const GemvDev& d, float* res, float* ssl, int* s_last, int tile,
                                             int split, int m0, int mvalid) {
-    constexpr bool SWI = (EPI == EPI_SWIGLU);
-    constexpr int HALF = RPT / 2;
-    constexpr int OUTS = SWI ? HALF : RPT;
     const GemvArgs& a = d.a;
     const int tid = threadIdx.x;
-    const int N = a.N;
     const int tile_id = blockIdx.z * d.n_tiles + tile;
     if (d.splits > 1) {
         float* base = d.part + (size_t)tile_id * d.splits * (MT * RPT);
@@ -121,39 +164,7 @@ __device__ __forceinline__ void gemv_finish(const GemvDev& d, float* res, float*
         __syncthreads();
     }
 
-    for (int i = tid; i < mvalid * OUTS; i += NT) {
-        const int m = i / OUTS, o = i - m * OUTS;
-        const float inv = NORM ? 1.0f / sqrtf(ssl[m] / (float)a.K + a.eps) : 1.0f;
-        const int row = m0 + m;
-        if (SWI) {
-            const int n = tile * HALF + o;
-            if (n < N) {
-                const float g = res[m * RPT + o] * inv;
-                const float u = res[m * RPT + HALF + o] * inv;
-                store_out(a.y, (size_t)row * N + n, silu_f32(g) * u, (T*)nullptr);
-            }
-        } else {
-            const int n = tile * RPT + o;
-            if (n >= N) continue;
-            const float v = res[m * RPT + o] * inv;
-            if (EPI == EPI_PARTIAL) {
-                reinterpret_cast<float*>(a.y)[(size_t)row * N + n] = v;
-            } else if (EPI == EPI_STORE) {
-                store_out(a.y, (size_t)row * N + n, v, (T*)nullptr);
-            } else {  // EPI_QKV
-                if (n < a.q_cols) {
-                    store_out(a.y, (size_t)row * a.q_cols + n, v, (T*)nullptr);
-                } else {
-                    const int r = n - a.q_cols;
-                    const bool is_k = r < a.kv_cols;
-                    const int rr = is_k ? r : r - a.kv_cols;
-                    const int g = rr / a.head_dim, e = rr - g * a.head_dim;
-                    const size_t idx = (((size_t)row * a.kv_heads + g) * a.capacity + a.pos) * a.head_dim + e;
-                    store_out(is_k ? a.k_cache : a.v_cache, idx, v, (T*)nullptr);
-                }
-            }
-        }
-    }
+    gemv_epilogue<T, MT, RPT, EPI, NORM, NT>(a, res, ssl, tile, m0, mvalid);
 }
 
 }  // namespace tpk
