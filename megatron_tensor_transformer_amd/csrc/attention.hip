@@ -236,9 +236,12 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
 
 // Merge of the chunk partials of one (sequence, kv head, query head): weights
 // exp(m_c - max) in chunk order, out = sum_c w_c o_c / sum_c w_c l_c. One
-// thread per dimension; the partials of all chunks are requested in batches.
+// thread per dimension. The chunk maxima and sums and the first MR chunks'
+// partial outputs are requested together, so the merge costs one memory
+// round trip for up to MR chunks.
 template <int D, int GQ>
 __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDev d) {
+    constexpr int MR = 32;
     const AttnArgs& a = d.a;
     const int h = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int e = threadIdx.x;
@@ -248,10 +251,16 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDev d) {
     __shared__ float red[D / 64];
     __shared__ float s_max, s_inv;
     const float* mlb = d.pml + (size_t)bg * nc * GQ * 2;
-    // chunk maxima (nc <= AT_MAX_CHUNKS <= 2 D): each thread reads up to two
-    float m0 = -INFINITY, m1 = -INFINITY;
-    if (e < nc) m0 = mlb[((size_t)e * GQ + h) * 2];
-    if (e + D < nc) m1 = mlb[((size_t)(e + D) * GQ + h) * 2];
+    const float* pob = d.po + (size_t)bg * nc * GQ * D + (size_t)h * D + e;
+    // chunk maxima and sums (nc <= AT_MAX_CHUNKS <= 2 D): each thread reads up to two of each
+    const int c0 = min(e, nc - 1), c1 = min(e + D, nc - 1);
+    const float m0r = mlb[((size_t)c0 * GQ + h) * 2], l0r = mlb[((size_t)c0 * GQ + h) * 2 + 1];
+    const float m1r = mlb[((size_t)c1 * GQ + h) * 2], l1r = mlb[((size_t)c1 * GQ + h) * 2 + 1];
+    float v[MR];
+#pragma unroll
+    for (int u = 0; u < MR; ++u) v[u] = pob[(size_t)min(u, nc - 1) * GQ * D];
+    const float m0 = e < nc ? m0r : -INFINITY;
+    const float m1 = e + D < nc ? m1r : -INFINITY;
     float mx = group_max<64>(fmaxf(m0, m1));
     if ((e & 63) == 0) red[e >> 6] = mx;
     __syncthreads();
@@ -266,12 +275,12 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDev d) {
     if (e < nc) {
         const float w = __expf(m0 - M);
         wgt[e] = w;
-        l += w * mlb[((size_t)e * GQ + h) * 2 + 1];
+        l += w * l0r;
     }
     if (e + D < nc) {
         const float w = __expf(m1 - M);
         wgt[e + D] = w;
-        l += w * mlb[((size_t)(e + D) * GQ + h) * 2 + 1];
+        l += w * l1r;
     }
     l = wave_sum(l);
     __syncthreads();
@@ -283,17 +292,11 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDev d) {
         s_inv = 1.0f / t;
     }
     __syncthreads();
-    const float* pob = d.po + (size_t)bg * nc * GQ * D + (size_t)h * D + e;
-    constexpr int UNR = 16;
     float acc = 0.f;
-    for (int c0 = 0; c0 < nc; c0 += UNR) {
-        float v[UNR];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) v[u] = pob[(size_t)min(c0 + u, nc - 1) * GQ * D];
-#pragma unroll
-        for (int u = 0; u < UNR; ++u)
-            if (c0 + u < nc) acc = fmaf(wgt[c0 + u], v[u], acc);
-    }
+    for (int u = 0; u < MR; ++u)
+        if (u < nc) acc = fmaf(wgt[u], v[u], acc);
+    for (int c = MR; c < nc; ++c) acc = fmaf(wgt[c], pob[(size_t)c * GQ * D], acc);
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.q_heads + (size_t)g * GQ + h) * D;
     out[e] = (uint16_t)f32_to_bf16_bits(acc * s_inv);
 }
