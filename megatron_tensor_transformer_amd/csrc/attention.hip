@@ -2,23 +2,30 @@
 // cached keys ("split-KV").
 //
 // Grid: (key chunks, kv heads, sequences). A workgroup (4 waves) takes the GQ
-// query heads that share one kv head and one chunk of keys, walks the chunk
-// in passes of 256 keys (64 per wave) with a running (max, sum, output) per
-// head, and leaves an unnormalised partial with its max and sum.
+// query heads that share one kv head and one chunk of keys, in passes of 128
+// keys; each wave owns 32 keys of every pass and keeps its own running max,
+// sum and output per head, so the waves never synchronise inside the chunk.
 //
 // Memory is read coalesced: a key's row of D bf16 is read by D/8 lanes with
-// one 128-bit load each, so one wave instruction covers 64/(D/8) whole keys.
-// A wave requests its pass's K and V rows before any arithmetic.
-//  - Scores: each lane dots its 8 dimensions of a key with the same 8
-//    dimensions of every head of the group (v_dot2), then a DPP
-//    reduce-scatter over the key's lanes leaves each lane with one head's
-//    score.
-//  - Probabilities go to LDS as packed bf16 pairs of consecutive keys; the
-//    value pass forms (V[j][d], V[j+1][d]) pairs with one v_perm each and
-//    accumulates with v_dot2, two keys per instruction. The running sum adds
-//    the same rounded probabilities the values are weighted with.
-//  - The key groups of a wave are reduced with permlane swaps, the 4 waves
-//    through LDS.
+// one 128-bit load each, so one wave instruction covers 64/(D/8) whole keys,
+// and a wave requests its pass's K rows, then its V rows, before anything
+// else.
+//  - Scores are a [keys x D] x [D x heads] contraction and go to the matrix
+//    cores (v_mfma_f32_16x16x32_bf16, heads padded to 16 with zero queries).
+//    The K rows pass through a wave-private LDS tile (rows padded by 16
+//    bytes) on their way to the operand registers: read in the operand
+//    layout straight from HBM they would stream at a fraction of the rate.
+//    A lane then holds one head's scores for four keys of each 16-key block.
+//  - The softmax runs in registers: maxima and sums over the four lanes of a
+//    head are two permlane swaps each. Probabilities are rounded to bf16 and
+//    the running sum adds exactly the rounded values the outputs are weighted
+//    with.
+//  - Values: probabilities go to LDS as packed bf16 pairs of consecutive keys;
+//    the value pass forms (V[j][d], V[j+1][d]) pairs with one v_perm each and
+//    accumulates two keys per v_dot2.
+//  - At the end of the chunk each wave reduces its outputs over its key
+//    groups (permlane swaps, DPP), and the four waves are merged by their
+//    log-sum-exp weights through LDS.
 // When the keys are split over several chunks, a second small kernel (one
 // workgroup per sequence, kv head and query head) merges the chunk partials
 // in chunk order by their log-sum-exp weights and writes the bf16 output; the
@@ -29,8 +36,12 @@
 
 namespace tpk {
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int AT_NT = 256;       // threads
-constexpr int AT_PASS = 256;     // keys per pass (64 per wave)
+constexpr int AT_KW = 32;        // keys per wave per pass
+constexpr int AT_PASS = 4 * AT_KW;   // keys per workgroup pass
 constexpr int AT_MAX_CHUNKS = 128;
 
 struct AttnDev {
@@ -40,47 +51,75 @@ struct AttnDev {
     float* po;       // [B * kv_heads][n_chunks][GQ][D]
 };
 
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// op over the lanes l, l ^ 16, l ^ 32, l ^ 48: each permlane swap of a value
+// with itself leaves, between the two results, the lane's own value and its
+// partner's in every lane, so op(a, b) combines them with no selects.
+__device__ __forceinline__ float max_over_kg(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum_over_kg(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 template <int D, int GQ>
 __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
     constexpr int LPK = D / 8;             // lanes per key row
     constexpr int KPW = 64 / LPK;          // keys per wave instruction
-    constexpr int KW = AT_PASS / 4;        // keys per wave per pass
-    constexpr int NK = KW / KPW;           // K rows a lane loads per pass
-    constexpr int NP = KW / 2 / KPW;       // V row pairs a lane loads per pass
-    constexpr bool PREFETCH_V = GQ <= 8;   // keep V loads in flight during the scores
+    constexpr int NK = AT_KW / KPW;        // K rows a lane loads per pass
+    constexpr int NP = AT_KW / 2 / KPW;    // V row pairs a lane loads per pass
     constexpr int NO = GQ * 8;             // output accumulators per lane
+    constexpr int KP = D + 8;              // K tile row pitch (elements)
+    constexpr int DS = D / 32;             // MFMA steps over d
+    constexpr int KB = AT_KW / 16;         // 16-key blocks per wave per pass
+    constexpr int NPAIR = AT_KW / 2;
+    static_assert(AT_KW * KP * 2 >= GQ * D * 4, "the end-of-chunk reduction reuses the K tile");
     const AttnArgs& a = d.a;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int kq = lane / LPK, dq = lane % LPK;
+    const int kq = lane / LPK, dq = lane % LPK;        // load / value-pass role
+    const int hc = lane & 15, kg = lane >> 4;          // score role: head hc, keys 4 kg .. 4 kg + 3 of a block
     const int bg = b * a.kv_heads + g;
     const int jbeg = c * d.chunk;
     const int jend = min(jbeg + d.chunk, a.kv_len);
 
-    __shared__ float sc[GQ][AT_PASS];                          // scores
-    __shared__ __align__(16) uint32_t pp[AT_PASS / 2][GQ];     // probabilities of key pairs, packed bf16
-    __shared__ float mrun[GQ], lrun[GQ], alpha[GQ];
-    __shared__ float red[4][GQ][D];
+    __shared__ __align__(16) uint16_t kt[4][AT_KW * KP];       // K tiles; at the end, each wave's outputs
+    __shared__ __align__(16) uint32_t pp[4][NPAIR][16];        // probabilities of key pairs, packed bf16
+    __shared__ float alpha_w[4][16];
+    __shared__ float m_w[4][16], l_w[4][16];
 
-    // this lane's 8 dimensions of every query head of the group
-    uint4 qv[GQ];
+    // query fragments: head hc, elements 32 s + 8 kg .. + 7 (zero for padding heads)
+    uint4 qf[DS];
     {
         const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.q_heads + (size_t)g * GQ) * D;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) qv[h] = load_u4(q + (size_t)h * D + dq * 8);
+        for (int s = 0; s < DS; ++s) {
+            const uint4 v = load_u4(q + (size_t)min(hc, GQ - 1) * D + s * 32 + kg * 8);
+            qf[s] = hc < GQ ? v : make_uint4(0, 0, 0, 0);
+        }
     }
-    if (tid < GQ) { mrun[tid] = -INFINITY; lrun[tid] = 0.f; }
-
     const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + (size_t)bg * a.capacity * D;
     const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + (size_t)bg * a.capacity * D;
     const float scale = 1.0f / sqrtf((float)D);
+    uint16_t* ktw = kt[wave];
+    float mrun = -INFINITY, lrun = 0.f;                // of head hc, this wave's keys
     float o[NO];
 #pragma unroll
     for (int i = 0; i < NO; ++i) o[i] = 0.f;
 
     for (int j0 = jbeg; j0 < jend; j0 += AT_PASS) {
-        const int kw0 = j0 + wave * KW;              // this wave's first key
-        // K rows (and V row pairs) of the pass, clamped to the last valid key.
+        const int kw0 = j0 + wave * AT_KW;             // this wave's first key
+        // K rows, then V row pairs, clamped to the last valid key.
         uint4 kr[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
@@ -88,83 +127,79 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
             kr[i] = load_stream_u4(kbase + (size_t)key * D + dq * 8);
         }
         uint4 va[NP], vb[NP];
-        auto load_v = [&]() {
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int key = kw0 + 2 * (i * KPW + kq);
-                va[i] = load_stream_u4(vbase + (size_t)min(key, jend - 1) * D + dq * 8);
-                vb[i] = load_stream_u4(vbase + (size_t)min(key + 1, jend - 1) * D + dq * 8);
-            }
-        };
-        if (PREFETCH_V) load_v();
+        for (int i = 0; i < NP; ++i) {
+            const int key = kw0 + 2 * (i * KPW + kq);
+            va[i] = load_stream_u4(vbase + (size_t)min(key, jend - 1) * D + dq * 8);
+            vb[i] = load_stream_u4(vbase + (size_t)min(key + 1, jend - 1) * D + dq * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i) *reinterpret_cast<uint4*>(ktw + (i * KPW + kq) * KP + dq * 8) = kr[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // scores
+        // scores: block kb, lane holds head hc for keys 16 kb + 4 kg + r
+        f32x4_t sc[KB];
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            float s[GQ];
+        for (int kb = 0; kb < KB; ++kb) {
+            sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                float t = dot2_bf16(kr[i].x, qv[h].x, 0.f);
-                t = dot2_bf16(kr[i].y, qv[h].y, t);
-                t = dot2_bf16(kr[i].z, qv[h].z, t);
-                s[h] = dot2_bf16(kr[i].w, qv[h].w, t);
-            }
-            reduce_scatter_group<LPK, GQ>(s, lane);
-            const int lk = wave * KW + i * KPW + kq;            // key within the pass
-#pragma unroll
-            for (int j = 0; j < (GQ > LPK ? GQ / LPK : 1); ++j) {
-                bool owner;
-                const int h = reduce_group_index<LPK, GQ>(lane, j, owner);
-                if (owner) sc[h][lk] = (j0 + lk < jend) ? s[j] * scale : -INFINITY;
+            for (int s = 0; s < DS; ++s) {
+                const uint4 kf = *reinterpret_cast<const uint4*>(ktw + (kb * 16 + hc) * KP + s * 32 + kg * 8);
+                sc[kb] = mfma16(kf, qf[s], sc[kb]);
             }
         }
-        if (!PREFETCH_V) load_v();
-        __syncthreads();
-
-        // running max and sum per head; probabilities relative to the new max
-        for (int h = wave; h < GQ; h += 4) {
-            float mx = -INFINITY;
-            for (int i = lane; i < AT_PASS; i += 64) mx = fmaxf(mx, sc[h][i]);
-            mx = group_max<64>(mx);
-            const float mnew = fmaxf(mrun[h], mx);
-            float sum = 0.f;
-            for (int i = lane; i < AT_PASS / 2; i += 64) {
-                const float p0 = __expf(sc[h][2 * i] - mnew);
-                const float p1 = __expf(sc[h][2 * i + 1] - mnew);
-                const uint32_t pk = pack_bf16x2(p0, p1);
-                pp[i][h] = pk;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool valid = kw0 + kb * 16 + 4 * kg + r < jend;
+                sc[kb][r] = valid ? sc[kb][r] * scale : -INFINITY;
+                mx = fmaxf(mx, sc[kb][r]);
+            }
+        mx = max_over_kg(mx);
+        const float mnew = fmaxf(mrun, mx);
+        const float mref = mnew == -INFINITY ? 0.f : mnew;    // a wave may see no valid key yet
+        const float al = __expf(mrun - mref);
+        float sum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const uint32_t pk = pack_bf16x2(__expf(sc[kb][2 * r2] - mref), __expf(sc[kb][2 * r2 + 1] - mref));
                 sum += bf16lo(pk) + bf16hi(pk);
+                pp[wave][kb * 8 + 2 * kg + r2][hc] = pk;
             }
-            sum = wave_sum(sum);
-            if (lane == 0) {
-                const float al = __expf(mrun[h] - mnew);
-                alpha[h] = al;
-                lrun[h] = lrun[h] * al + sum;
-                mrun[h] = mnew;
-            }
-        }
-        __syncthreads();
+        sum = sum_over_kg(sum);
+        lrun = lrun * al + sum;
+        mrun = mnew;
+        if (kg == 0) alpha_w[wave][hc] = al;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // values: two keys per v_dot2
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
-            const float al = alpha[h];
+            const float ah = alpha_w[wave][h];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[h * 8 + e] *= al;
+            for (int e = 0; e < 8; ++e) o[h * 8 + e] *= ah;
         }
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            const int lp = (wave * KW) / 2 + i * KPW + kq;      // key pair within the pass
+            const int lp = i * KPW + kq;                // key pair within the wave's keys
             uint32_t pw[GQ];
             if constexpr (GQ >= 4) {
 #pragma unroll
                 for (int h4 = 0; h4 < GQ; h4 += 4) {
-                    const uint4 t = *reinterpret_cast<const uint4*>(&pp[lp][h4]);
+                    const uint4 t = *reinterpret_cast<const uint4*>(&pp[wave][lp][h4]);
                     pw[h4] = t.x; pw[h4 + 1] = t.y; pw[h4 + 2] = t.z; pw[h4 + 3] = t.w;
                 }
             } else {
 #pragma unroll
-                for (int h = 0; h < GQ; ++h) pw[h] = pp[lp][h];
+                for (int h = 0; h < GQ; ++h) pw[h] = pp[wave][lp][h];
             }
             const uint32_t* A = &va[i].x;
             const uint32_t* Bv = &vb[i].x;
@@ -179,7 +214,9 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
                 }
             }
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
     // Reduce over the key groups of the wave (lanes with the same dq). For
@@ -200,6 +237,7 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
 #pragma unroll
     for (int j = 0; j < N0 / 4; ++j) xrow_pair<1>(o[j], o[N0 / 4 + j]);      // lane bit 4
     // slot j of this lane now holds flat index base + j (flat index = head * 8 + element)
+    float* ow = reinterpret_cast<float*>(kt[wave]);                          // [GQ][D] of this wave
     {
         int base = ((lane >> 5) & 1) * (N0 / 2) + ((lane >> 4) & 1) * (N0 / 4);
         if constexpr (LPK == 8) base += ((lane >> 3) & 1) * (NO / 2);
@@ -207,30 +245,38 @@ __global__ __launch_bounds__(AT_NT) void attn_decode_kernel(AttnDev d) {
         for (int j = 0; j < N0 / 4; ++j) {
             const int idx = base + j;
             const int h = idx / 8, e = idx % 8;
-            red[wave][h][dq * 8 + e] = o[j];
+            ow[h * D + dq * 8 + e] = o[j];
         }
+    }
+    if (kg == 0) {
+        m_w[wave][hc] = mrun;
+        l_w[wave][hc] = lrun;
     }
     __syncthreads();
 
+    // Merge the four waves: weights exp(m_w - max), in wave order.
     uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * a.q_heads + (size_t)g * GQ) * D;
-    if (d.n_chunks == 1) {
-        for (int i = tid; i < GQ * D; i += AT_NT) {
-            const int h = i / D, e = i % D;
-            const float v = red[0][h][e] + red[1][h][e] + red[2][h][e] + red[3][h][e];
-            out[i] = (uint16_t)f32_to_bf16_bits(v / lrun[h]);
-        }
-        return;
-    }
-
     float* po = d.po + ((size_t)bg * d.n_chunks + c) * GQ * D;
     for (int i = tid; i < GQ * D; i += AT_NT) {
-        const int h = i / D, e = i % D;
-        po[i] = red[0][h][e] + red[1][h][e] + red[2][h][e] + red[3][h][e];
-    }
-    if (tid < GQ) {
-        float* ml = d.pml + (((size_t)bg * d.n_chunks + c) * GQ + tid) * 2;
-        ml[0] = mrun[tid];
-        ml[1] = lrun[tid];
+        const int h = i / D;
+        const float M = fmaxf(fmaxf(m_w[0][h], m_w[1][h]), fmaxf(m_w[2][h], m_w[3][h]));
+        float acc = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float wt = m_w[w][h] == -INFINITY ? 0.f : __expf(m_w[w][h] - M);
+            acc += wt * reinterpret_cast<const float*>(kt[w])[i];
+            l += wt * l_w[w][h];
+        }
+        if (d.n_chunks == 1) {
+            out[i] = (uint16_t)f32_to_bf16_bits(acc / l);
+        } else {
+            po[i] = acc;
+            if (i % D == 0) {
+                float* ml = d.pml + (((size_t)bg * d.n_chunks + c) * GQ + h) * 2;
+                ml[0] = M;
+                ml[1] = l;
+            }
+        }
     }
 }
 
