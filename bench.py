@@ -615,6 +615,10 @@ def bench_layer_decode(ctx):
     config = {"workload": f"70B-shaped full layer decode, all t={t} rank shards (attention and MLP stages) + "
                           f"on-device sums with residual", "hidden": H, "intermediate": I, "q_heads": nq,
               "kv_heads": nkv, "head_dim": d, "t": t, "batch": B, "kv_len": S_}
+    # A model, not a measurement: the t-GPU decode step predicted from this
+    # one-GPU layer time (all t shards run in turn) for 80 such layers.
+    from megatron_tensor_transformer_amd import step_model
+    extra["step_model_80_layers"] = step_model.predict(ms_step * 1e-3, layers=80, hidden=H, tokens=B, max_t=t)
     res = result(ctx, B * args.steps / (total_ms * 1e-3), "tokens/s", ms_step, config, extra)
     if not args.no_cpu:
         from oracle import sharded as S
