@@ -15,6 +15,10 @@ Readings the pages leave open:
   softmax over the kv_len cached keys, no mask and no rotary embedding. The new
   token's k and v overwrite cache position kv_len - 1 before attending. Query
   head h reads kv head floor(h / (n_q / n_kv)) (grouped-query attention).
+- Prefill attention: a block of S new tokens at positions kv_len - S ..
+  kv_len - 1, whose k and v are already in the cache; the token at position p
+  attends to positions 0..p (causal), with the same scale, grouping and no
+  rotary embedding. A prompt from scratch is kv_len = S.
 - The full layer is pre-norm with residual adds: h = x + attn(norm1(x)),
   out = h + mlp(norm2(h)); ``residual=False`` gives the pages' literal flow.
 - No biases.
@@ -94,6 +98,31 @@ def decode_attention(q, k_cache, v_cache, kv_len: int, n_q: int, n_kv: int, d: i
             p = softmax((keys @ q[b, h]) * scale)       # [kv_len]
             out[b, h] = p @ vals
     return out.reshape(B, n_q * d)
+
+
+def prefill_attention(q, k_cache, v_cache, kv_len: int, n_q: int, n_kv: int, d: int) -> np.ndarray:
+    """Causal grouped-query attention for a block of new tokens.
+
+    q [B, S, n_q * d] for the tokens at positions kv_len - S .. kv_len - 1;
+    caches [B, n_kv, capacity, d] hold k, v for positions 0..kv_len-1. The
+    token at position p attends to positions 0..p. Returns [B, S, n_q * d].
+    """
+    q = f64(q)
+    B, S = q.shape[0], q.shape[1]
+    q = q.reshape(B, S, n_q, d)
+    group = n_q // n_kv
+    scale = 1.0 / np.sqrt(d)
+    pos = (kv_len - S) + np.arange(S)                    # position of each query
+    allowed = np.arange(kv_len)[None, :] <= pos[:, None]  # [S, kv_len]
+    out = np.zeros((B, S, n_q, d))
+    for b in range(B):
+        for h in range(n_q):
+            g = h // group
+            keys = f64(k_cache[b, g, :kv_len])
+            vals = f64(v_cache[b, g, :kv_len])
+            s = np.where(allowed, (q[b, :, h] @ keys.T) * scale, -np.inf)
+            out[b, :, h] = softmax(s) @ vals
+    return out.reshape(B, S, n_q * d)
 
 
 def append_kv(k_cache, v_cache, k_new, v_new, kv_len: int, n_kv: int, d: int):

@@ -74,3 +74,34 @@ def decode_attention(q, k_cache, v_cache, kv_len, n_q, n_kv, d):
                 row.append(acc)
         out.append(row)
     return out
+
+
+def prefill_attention(q, k_cache, v_cache, kv_len, n_q, n_kv, d):
+    """q [B][S][n_q*d] at positions kv_len-S..kv_len-1; caches [B][n_kv][cap][d]; out [B][S][n_q*d]."""
+    group = n_q // n_kv
+    out = []
+    for b in range(len(q)):
+        S = len(q[b])
+        rows = []
+        for i in range(S):
+            pos = kv_len - S + i
+            row = []
+            for h in range(n_q):
+                g = h // group
+                scores = []
+                for j in range(pos + 1):
+                    s = 0.0
+                    for e in range(d):
+                        s += float(q[b][i][h * d + e]) * float(k_cache[b][g][j][e])
+                    scores.append(s / math.sqrt(d))
+                mx = max(scores)
+                w = [math.exp(s - mx) for s in scores]
+                tot = sum(w)
+                for e in range(d):
+                    acc = 0.0
+                    for j in range(pos + 1):
+                        acc += w[j] / tot * float(v_cache[b][g][j][e])
+                    row.append(acc)
+            rows.append(row)
+        out.append(rows)
+    return out

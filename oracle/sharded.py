@@ -123,6 +123,30 @@ def rank_attention(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len: int, n_q: in
     return {"q": q, "k": k, "v": v, "k_cache": kc, "v_cache": vc, "o": o, "partial": partial}
 
 
+def rank_prefill_attention(q_rank, k_rank, v_rank, kv_len: int, n_q: int, n_kv: int, d: int,
+                           p: dict) -> np.ndarray:
+    """One rank's causal prefill attention on its owned heads.
+
+    q_rank [B, S, q_heads * d] (the rank's q columns); k_rank, v_rank
+    [B, kv_heads, capacity, d] (the rank's kv heads). Query i of the block sits
+    at position kv_len - S + i and sees the first kv_len - S + i + 1 keys.
+    """
+    qb, qn = p["q_head_begin"], p["q_heads"]
+    kb = p["kv_head_begin"]
+    q = _f(q_rank)
+    B, S = q.shape[0], q.shape[1]
+    q = q.reshape(B, S, qn, d)
+    group = n_q // n_kv
+    o = np.zeros((B, S, qn, d))
+    for b in range(B):
+        for i in range(S):
+            seen = kv_len - S + i + 1
+            for hl in range(qn):
+                j = (qb + hl) // group - kb           # local kv head
+                o[b, i, hl] = _attend(q[b, i, hl][None, :], _f(k_rank[b, j, :seen]), _f(v_rank[b, j, :seen]), d)[0]
+    return o.reshape(B, S, qn * d)
+
+
 def sharded_layer(x, w: Dict[str, Optional[np.ndarray]], k_cache, v_cache, kv_len: int, n_q: int,
                   n_kv: int, d: int, t: int, eps: float = 1e-5, residual: bool = True) -> Dict[str, object]:
     """All t ranks of the attention stage, sum, then all t ranks of the MLP stage, sum."""

@@ -227,6 +227,64 @@ def pin_attention_special_cases(decode_attention):
     assert np.max(np.abs(o - 1.0)) < 1e-14
 
 
+def pin_prefill_attention(prefill_attention, decode_attention):
+    """Causal prefill attention: brute force on tiny inputs, the first token's
+    output is its own value, the last row is decode attention over the same
+    keys, identical keys give running means, and a chunk of the block equals
+    the same rows of the whole block."""
+    B, n_q, n_kv, d, cap = 2, 4, 2, 3, 9
+    rng = np.random.default_rng(21)
+    K = rng.standard_normal((B, n_kv, cap, d))
+    V = rng.standard_normal((B, n_kv, cap, d))
+    for S, kv_len in [(1, 1), (3, 3), (4, 6), (5, 9)]:
+        q = rng.standard_normal((B, S, n_q * d))
+        ref = np.array(naive.prefill_attention(q.tolist(), K.tolist(), V.tolist(), kv_len, n_q, n_kv, d))
+        got = prefill_attention(q, K, V, kv_len, n_q, n_kv, d)
+        assert relerr(got, ref) < 1e-13, (S, kv_len)
+        # the last query attends to every key: decode attention
+        last = decode_attention(q[:, -1], K, V, kv_len, n_q, n_kv, d)
+        assert relerr(got[:, -1], last) < 1e-13, (S, kv_len)
+    # a prompt from scratch: token 0 sees only itself
+    S = 6
+    q = rng.standard_normal((B, S, n_q * d))
+    o = prefill_attention(q, K, V, S, n_q, n_kv, d).reshape(B, S, n_q, d)
+    for h in range(n_q):
+        assert np.allclose(o[:, 0, h], V[:, h // 2, 0], rtol=0, atol=1e-15)
+    # identical keys: the token at position p averages values 0..p
+    Kc = np.repeat(K[:, :, :1], cap, axis=2)
+    o = prefill_attention(q, Kc, V, S, n_q, n_kv, d).reshape(B, S, n_q, d)
+    for i in range(S):
+        for h in range(n_q):
+            assert np.allclose(o[:, i, h], V[:, h // 2, :i + 1].mean(axis=1), rtol=0, atol=1e-14)
+    # positions after a query are never read: poison them for the first rows
+    Kx, Vx = K.copy(), V.copy()
+    Kx[:, :, 3:] = np.nan; Vx[:, :, 3:] = np.nan
+    o = prefill_attention(q[:, :3], Kx, Vx, 3, n_q, n_kv, d)
+    assert np.all(np.isfinite(o))
+    # chunked prefill: the last 2 rows of a 6-token block, given the same caches
+    full = prefill_attention(q, K, V, S, n_q, n_kv, d)
+    part = prefill_attention(q[:, 4:], K, V, S, n_q, n_kv, d)
+    assert relerr(part, full[:, 4:]) < 1e-14
+
+
+def pin_rank_prefill(rank_prefill_attention, prefill_attention, rank_plan, ModelDesc):
+    """Each rank's owned heads, from its own kv heads, equal the unsharded heads."""
+    B, S, n_q, n_kv, d, cap, kv_len = 2, 4, 8, 4, 3, 7, 6
+    rng = np.random.default_rng(22)
+    q = rng.standard_normal((B, S, n_q * d))
+    K = rng.standard_normal((B, n_kv, cap, d))
+    V = rng.standard_normal((B, n_kv, cap, d))
+    full = prefill_attention(q, K, V, kv_len, n_q, n_kv, d)
+    for t in (1, 2, 4):
+        desc = ModelDesc(hidden=n_q * d, intermediate=0, n_q_heads=n_q, n_kv_heads=n_kv, head_dim=d)
+        for r in range(t):
+            p = rank_plan(desc, t, r)
+            qs = slice(p["q_head_begin"] * d, (p["q_head_begin"] + p["q_heads"]) * d)
+            ks = slice(p["kv_head_begin"], p["kv_head_begin"] + p["kv_heads"])
+            got = rank_prefill_attention(q[:, :, qs], K[:, ks], V[:, ks], kv_len, n_q, n_kv, d, p)
+            assert relerr(got, full[:, :, qs]) < 1e-13, (t, r)
+
+
 # ---------------------------------------------------------------- decomposition invariants
 
 def pin_column_concat_naive(column_shard, rank_plan, ModelDesc):

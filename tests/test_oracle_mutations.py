@@ -23,6 +23,11 @@ def _all_layer_pins():
     P.pin_layer_vs_naive(L.layer)
 
 
+def _all_prefill_pins():
+    P.pin_prefill_attention(L.prefill_attention, L.decode_attention)
+    P.pin_rank_prefill(S.rank_prefill_attention, L.prefill_attention, plan.rank_plan, plan.ModelDesc)
+
+
 def _all_sharded_pins():
     P.pin_silu(S._silu)
     P.pin_rmsnorm(lambda x, g, eps: S._norm(x, g, eps))
@@ -43,6 +48,38 @@ def _all_plan_pins():
 _orig_rank_plan = plan.rank_plan
 _orig_attention = L.decode_attention
 _orig_rank_attention = S.rank_attention
+_orig_prefill = L.prefill_attention
+_orig_rank_prefill = S.rank_prefill_attention
+
+
+def _prefill_strict_mask(q, k, v, kv_len, n_q, n_kv, d):
+    # each token attends to positions before it but not itself (first row undefined -> use key 0 only)
+    q = np.asarray(q, np.float64)
+    B, S = q.shape[:2]
+    out = np.zeros((B, S, n_q * d))
+    for i in range(S):
+        seen = max(kv_len - S + i, 1)
+        out[:, i] = _orig_attention(q[:, i], k, v, seen, n_q, n_kv, d)
+    return out
+
+
+def _prefill_no_mask(q, k, v, kv_len, n_q, n_kv, d):
+    q = np.asarray(q, np.float64)
+    B, S = q.shape[:2]
+    return np.stack([_orig_attention(q[:, i], k, v, kv_len, n_q, n_kv, d) for i in range(S)], axis=1)
+
+
+def _prefill_positions_from_zero(q, k, v, kv_len, n_q, n_kv, d):
+    # treats the block as starting at position 0 even when kv_len > S
+    return _orig_prefill(q, k, v, np.shape(q)[1], n_q, n_kv, d)
+
+
+def _rank_prefill_global_kv(q, k, v, kv_len, n_q, n_kv, d, p):
+    # uses the global kv head index into the rank's local kv slice
+    p2 = dict(p)
+    p2["kv_head_begin"] = 0
+    return _orig_rank_prefill(q, k, v, kv_len, n_q, n_kv, d, p2) if p["kv_head_begin"] == 0 else \
+        _orig_rank_prefill(q, np.roll(k, 1, axis=1), np.roll(v, 1, axis=1), kv_len, n_q, n_kv, d, p)
 
 
 def _plan_shift_heads(desc, t, rank):
@@ -113,6 +150,10 @@ MUTATIONS = {
     "attention_no_scale": (L, "decode_attention", _attention_no_scale, _all_layer_pins),
     "attention_drops_last_key": (L, "decode_attention", _attention_short, _all_layer_pins),
     "append_wrong_slot": (L, "append_kv", _append_wrong_slot, _all_layer_pins),
+    "prefill_strict_mask": (L, "prefill_attention", _prefill_strict_mask, _all_prefill_pins),
+    "prefill_no_mask": (L, "prefill_attention", _prefill_no_mask, _all_prefill_pins),
+    "prefill_positions_from_zero": (L, "prefill_attention", _prefill_positions_from_zero, _all_prefill_pins),
+    "rank_prefill_wrong_kv_head": (S, "rank_prefill_attention", _rank_prefill_global_kv, _all_prefill_pins),
     # decomposition
     "sum_drops_last_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
         [np.asarray(p, float) for p in parts[:-1]] or [np.zeros_like(parts[0])], axis=0)

@@ -75,3 +75,11 @@ def test_layer_literal_flow():
 
 def test_layer_vs_naive():
     P.pin_layer_vs_naive(L.layer)
+
+
+def test_prefill_attention():
+    P.pin_prefill_attention(L.prefill_attention, L.decode_attention)
+
+
+def test_rank_prefill_attention():
+    P.pin_rank_prefill(S.rank_prefill_attention, L.prefill_attention, plan.rank_plan, plan.ModelDesc)
