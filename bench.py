@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mlp_decode",
-                    choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode"])
+                    choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of the timed step (default: the workload's)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true")
@@ -101,7 +101,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
     bench = {"mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
-             "layer_decode": bench_layer_decode}[args.workload]
+             "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill}[args.workload]
     if args.calibrate_copy:
         calibrate_copy(torch)
     res = bench(ctx)
@@ -636,6 +636,84 @@ def bench_layer_decode(ctx):
                                "kind": "oracle",
                                "sample": f"{n} float64 passes of rank 0's shard (attention + MLP stages) over the "
                                          f"batch of {B}, {el:.1f} s; scaled by 1/{t} for the {t} ranks of a step"}
+    return res
+
+
+
+def causal_flops(batch, seq, kv_len, q_heads, d):
+    """Multiply-adds x 2 of causal attention: the token at position p scores and weights p + 1 keys."""
+    p0 = kv_len - seq
+    seen = seq * (p0 + 1) + seq * (seq - 1) // 2          # sum over the block of (p + 1)
+    return 4.0 * d * batch * q_heads * seen
+
+
+def bench_attn_prefill(ctx):
+    torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
+    wl = W.WORKLOADS[6]
+    nq, nkv, d, t, kv_len = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t, wl.kv_len
+    M = args.tokens or wl.tokens[0]
+    B = 2
+    S_ = M // B
+    log(f"[bench] drawing {wl.name}")
+    inp = W.prefill_attention_inputs(6, B, S_, nq, nkv, d, kv_len, "bf16")
+    desc = tp.make_desc(wl.hidden, 0, nq, nkv, d, n_layers=1, seq_len=kv_len, batch=B)
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    q_all = inp["q"].reshape(B, S_, nq, d)
+    ranks = []
+    for p in plans:
+        qb, qn, kb, kn = p.q_head_begin, p.q_heads, p.kv_head_begin, p.kv_heads
+        ranks.append({"q": ctx.dev(q_all[:, :, qb:qb + qn].reshape(B, S_, qn * d)),
+                      "k": ctx.dev(inp["k_cache"][:, kb:kb + kn]), "v": ctx.dev(inp["v_cache"][:, kb:kb + kn]),
+                      "o": torch.empty(B, S_, qn * d, dtype=torch.bfloat16, device="cuda")})
+    p0 = plans[0]
+
+    def step(i):
+        for r, p in enumerate(plans):
+            rw = ranks[r]
+            tp.tp_prefill_attention(rw["q"], rw["k"], rw["v"], rw["o"], kv_len, p.q_heads)
+
+    def one(i):
+        rw = ranks[i % t]
+        tp.tp_prefill_attention(rw["q"], rw["k"], rw["v"], rw["o"], kv_len, p0.q_heads)
+
+    for i in range(2 * t):
+        one(i)
+    at = event_time_ms(torch, one, 4 * t)
+    fl = causal_flops(B, S_, kv_len, p0.q_heads, d)
+    tf = fl / (at[0] * 1e-3) / 1e12
+    log(f"[bench] prefill attention {at[0] * 1e3:.1f} us ({tf:.0f} TFLOP/s)")
+    total_ms = time_steps(ctx, step, 1)
+    ms_step = total_ms / args.steps
+    tflops = t * fl * args.steps / (total_ms * 1e-3) / 1e12
+    extra = {
+        "tokens_per_s": M * args.steps / (total_ms * 1e-3),
+        "pct_mfma_peak": 100 * tflops / BF16_PEAK_TFLOPS,
+        "per_rank": {"attention_us": at[0] * 1e3, "causal_flops": fl},
+        "roofline": {"kernel": "attn_prefill_kernel (causal GQA prefill attention, one rank shard)",
+                     "bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / BF16_PEAK_TFLOPS, "traffic": counted_traffic(f"prefill_attention_m{M}"),
+                     "flops_per_launch": fl, "us_mean": at[0] * 1e3, "us_median": at[1] * 1e3,
+                     "us_min": at[2] * 1e3},
+    }
+    config = {"workload": f"70B-shaped causal prefill attention, all t={t} rank shards (each {p0.q_heads} q heads "
+                          f"on {p0.kv_heads} kv head)", "q_heads": nq, "kv_heads": nkv, "head_dim": d, "t": t,
+              "batch": B, "seq": S_, "kv_len": kv_len}
+    res = result(ctx, tflops, "TFLOP/s", ms_step, config, extra)
+    if not args.no_cpu:
+        from oracle import sharded as S
+        pd = tp.plan_dict(p0)
+        n_tail = 32
+        qs = inp["q"][:1, S_ - n_tail:].reshape(1, n_tail, nq, d)[:, :, p0.q_head_begin:p0.q_head_begin + p0.q_heads]
+        qs = qs.reshape(1, n_tail, p0.q_heads * d)
+        kr = inp["k_cache"][:1, p0.kv_head_begin:p0.kv_head_begin + p0.kv_heads]
+        vr = inp["v_cache"][:1, p0.kv_head_begin:p0.kv_head_begin + p0.kv_heads]
+        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
+        n, el = repeat_for(args.cpu_seconds, lambda: S.rank_prefill_attention(qs, kr, vr, kv_len, nq, nkv, d, pd))
+        sfl = causal_flops(1, n_tail, kv_len, p0.q_heads, d)
+        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} float64 passes of rank 0's shard over the last {n_tail} tokens of "
+                                         f"sequence 0 (each sees about {kv_len} keys), {el:.1f} s"}
     return res
 
 

@@ -207,6 +207,28 @@ tp_status tp_decode_attention(const void* q, const void* k, const void* v, void*
                               int32_t q_heads, int32_t kv_heads, int32_t head_dim, int64_t capacity,
                               int64_t kv_len, tp_dtype dtype, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * tp_prefill_attention - causal attention over the heads this rank owns for
+ * a block of seq new tokens ("Tensor parallel scaling curves", section "What
+ * tensor parallelism actually splits": local attention on owned heads, no
+ * communication; causal masking is the standard decoder rule, token at
+ * position p sees positions 0..p). Token i of sequence b sits at position
+ * p = kv_len - seq + i and its k, v are already in the caches. For owned
+ * query head h with kv head g = h / (q_heads / kv_heads):
+ *   o[b, i, h] = sum_j softmax_j(q[b, i, h] . K[b, g, j] / sqrt(d)) V[b, g, j],
+ *   j = 0 .. p.
+ * q      device [batch, seq, q_heads * d] bf16
+ * k, v   device [batch, kv_heads, capacity, d] bf16 caches
+ * out    device [batch, seq, q_heads * d] bf16; must not overlap q or the caches
+ * d must be 64 or 128, q_heads / kv_heads one of 1, 2, 4, 8, 16, batch and
+ * kv_heads at most 65535 (TP_ERR_SHAPE); 1 <= seq <= kv_len <= capacity
+ * (TP_ERR_KV). bf16 only
+ * (TP_ERR_DTYPE). Needs no workspace.
+ */
+tp_status tp_prefill_attention(const void* q, const void* k, const void* v, void* out, int64_t batch,
+                               int64_t seq, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
+                               int64_t capacity, int64_t kv_len, tp_dtype dtype, void* stream);
+
 typedef enum tp_stage { TP_STAGE_ATTN = 0, TP_STAGE_MLP = 1 } tp_stage;
 
 /* One rank's weights for one layer, all device pointers, stored [out, in]. */

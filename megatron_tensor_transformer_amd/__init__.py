@@ -36,7 +36,7 @@ STATUS = ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_
 
 EXPORTS = ["tp_shard_plan", "tp_linear_workspace_bytes", "tp_column_linear", "tp_swiglu",
            "tp_row_linear_partial", "tp_partial_sum", "tp_attention_workspace_bytes", "tp_decode_attention",
-           "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_status_name", "tp_last_error"]
+           "tp_prefill_attention", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_status_name", "tp_last_error"]
 
 
 class tp_model_desc(ctypes.Structure):
@@ -75,6 +75,7 @@ _SIGS = {
     "tp_partial_sum": (_I32, [ctypes.POINTER(_P), _I32, _P, _P, _I64, _I64, _I32, _P]),
     "tp_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I64]),
     "tp_decode_attention": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P, _SZ, _P]),
+    "tp_prefill_attention": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P]),
     "tp_layer_workspace_bytes": (_SZ, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
                                        _I64, _I32]),
     "tp_layer_shard_forward": (_I32, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
@@ -222,6 +223,16 @@ def tp_decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: 
     wp, wn = _ws(ws)
     _check(lib.tp_decode_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, q_heads, kv_heads, d, cap, kv_len,
                                    _dtype_code(q), wp, wn, _stream(stream)))
+    return out
+
+
+def tp_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, kv_len: int,
+                         q_heads: int, stream=None) -> torch.Tensor:
+    """q, out [B, S, q_heads*d]; k, v [B, kv_heads, capacity, d]; tokens at kv_len-S .. kv_len-1."""
+    B, kv_heads, cap, d = k.shape
+    S = q.shape[1]
+    _check(lib.tp_prefill_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, q_heads, kv_heads, d, cap, kv_len,
+                                    _dtype_code(q), _stream(stream)))
     return out
 
 

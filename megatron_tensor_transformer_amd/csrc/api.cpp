@@ -399,6 +399,39 @@ tp_status tp_decode_attention(const void* q, const void* k, const void* v, void*
     return ok();
 }
 
+tp_status tp_prefill_attention(const void* q, const void* k, const void* v, void* out, int64_t batch, int64_t seq,
+                               int32_t q_heads, int32_t kv_heads, int32_t head_dim, int64_t capacity, int64_t kv_len,
+                               tp_dtype dtype, void* stream) {
+    if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "prefill attention supports bf16 only");
+    TRY(check_ptr(q, "q"));
+    TRY(check_ptr(k, "k"));
+    TRY(check_ptr(v, "v"));
+    TRY(check_ptr(out, "out"));
+    if (batch < 1 || batch > 65535) return fail(TP_ERR_SHAPE, "batch=%lld outside 1..65535", (long long)batch);
+    if (q_heads < 1 || kv_heads < 1 || kv_heads > 65535) return fail(TP_ERR_SHAPE, "bad head counts");
+    if (q_heads % kv_heads) return fail(TP_ERR_INDIVISIBLE, "q_heads=%d not a multiple of kv_heads=%d", q_heads, kv_heads);
+    const int gq = q_heads / kv_heads;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8 && gq != 16)
+        return fail(TP_ERR_SHAPE, "q_heads/kv_heads=%d must be 1, 2, 4, 8 or 16", gq);
+    if (head_dim != 64 && head_dim != 128) return fail(TP_ERR_SHAPE, "head_dim=%d must be 64 or 128", head_dim);
+    if (capacity < 1 || capacity > (int64_t(1) << 24)) return fail(TP_ERR_SHAPE, "capacity outside 1..2^24");
+    if (kv_len < 1 || kv_len > capacity)
+        return fail(TP_ERR_KV, "kv_len=%lld outside 1..capacity=%lld", (long long)kv_len, (long long)capacity);
+    if (seq < 1 || seq > kv_len)
+        return fail(TP_ERR_KV, "seq=%lld outside 1..kv_len=%lld", (long long)seq, (long long)kv_len);
+    const size_t nq = (size_t)batch * seq * q_heads * head_dim * 2;
+    const size_t nc = (size_t)batch * kv_heads * capacity * head_dim * 2;
+    if (overlaps(out, nq, q, nq) || overlaps(out, nq, k, nc) || overlaps(out, nq, v, nc))
+        return fail(TP_ERR_ALIAS, "out overlaps q or the caches");
+    tpk::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.capacity = capacity; a.kv_len = (int)kv_len;
+    a.batch = (int)batch; a.seq = (int)seq; a.q_heads = q_heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
+    hipError_t e = tpk::prefill_attn_launch(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+    return ok();
+}
+
 size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage, int64_t m,
                                 tp_dtype dtype) {
     if (!desc || !plan || m < 1 || (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP)) return 0;

@@ -1,0 +1,414 @@
+// Causal grouped-query attention for a block of new tokens (prefill).
+//
+// The S tokens of a sequence sit at positions kv_len - S .. kv_len - 1 and
+// their k, v are already in the cache; the token at position p attends to
+// positions 0..p with scores scaled by 1/sqrt(D), and query head h reads kv
+// head h / GQ.
+//
+// Work split. A query block is 64 rows: 64 / GQ consecutive tokens x the GQ
+// heads of one kv head, so every K and V block staged for it serves all of
+// them. Causality makes late query blocks see many more keys than early
+// ones, so a workgroup takes two query blocks of one (sequence, kv head),
+// i and n - 1 - i, one after the other: every workgroup then walks about the
+// same number of keys and the grid ends together. Inside a query block the 8
+// waves split the work 2 x 4: wave w owns rows 32 (w % 2) .. + 31 (two MFMA
+// column tiles of 16) and keys 32 (w / 2) .. + 31 of every 128-key block,
+// with its own running softmax state; the four key quarters of a row are
+// merged by their log-sum-exp weights through LDS at the end.
+//  - Scores are computed transposed, S^T = K Q^T, on
+//    v_mfma_f32_16x16x32_bf16: a lane then holds one query row's scores for
+//    four keys of each 16-key tile, so the softmax of a row needs only its
+//    own lane and the three lanes that share its column (two permlane swaps),
+//    and the probabilities already form the B operand of O^T = V^T P^T
+//    (a lane's 8 k-values are keys 4kg..4kg+3 of the wave's two key tiles;
+//    the V^T operand reads the same 8 keys).
+//  - K and V go through LDS in blocks of 128 keys, double buffered: the next
+//    block's rows are loaded into registers while the current block is
+//    multiplied, then written to the other buffer; one barrier per block.
+//    V is stored transposed (V^T[d][key]); the transpose pairs two keys of
+//    one column with one v_perm per dword, and key pairs are XOR-swizzled by
+//    d / 8 so that both the transposing stores and the operand reads spread
+//    over the LDS banks.
+//  - The online softmax (running max and sum per row, in the base-2 domain
+//    with the 1/sqrt(D) scale folded into one multiply-add) runs in
+//    registers. The reference maximum is raised only when a score exceeds it
+//    by more than 2^PF_SLACK, so most blocks skip the rescale of the
+//    accumulators. Probabilities are rounded to bf16 and the running sum
+//    adds exactly the rounded values (one v_dot2 with (1, 1) per key pair).
+//  - Causality: a query block walks key blocks up to its last token's
+//    position; only blocks that reach past its first token's position are
+//    masked, and a wave skips a quarter that lies wholly past every row.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int PF_NT = 512;       // threads (8 waves)
+constexpr int PF_ROWS = 64;      // query rows per query block
+constexpr int PF_BK = 128;       // keys per block
+constexpr int PF_KW = 32;        // keys per wave per block
+constexpr int NBUF = 2;          // K/V block buffers in LDS
+constexpr float PF_SLACK = 8.0f; // log2 of the largest unnormalised probability
+constexpr float PF_LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4_t mfma16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+
+// Maxima of finite or -inf scores. Written out because fmaxf quiets NaN
+// inputs first, which costs an extra instruction per operand here.
+__device__ __forceinline__ float pf_max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float pf_max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// op over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one MFMA
+// column): between the two results of a swap with itself every lane holds its
+// own value and its partner's, so op(a, b) needs no lane selects.
+__device__ __forceinline__ float pf_max4(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = pf_max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return pf_max2(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float pf_sum4(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Key-pair column of V^T row d in LDS: pairs are XOR-swizzled by bits of
+// d / 8 moved to pair-index bits 1, 2 and 4. Bits 0 and 3 stay put, so a
+// lane's two 4-key runs (pairs kp, kp + 1 and kp + 8, kp + 9) stay
+// contiguous and 8 pairs apart.
+__device__ __forceinline__ int vt_pair(int kp, int d) {
+    const int g = (d >> 3) & 7;
+    return kp ^ (((g & 3) << 1) | ((g & 4) << 2));
+}
+
+template <int D, int GQ>
+__global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
+    constexpr int DC = D / 8;                      // 16-byte chunks per row
+    constexpr int KPITCH = D + 8;                  // K tile row pitch (elements)
+    constexpr int VPITCH = PF_BK + 8;              // V^T tile row pitch (elements)
+    constexpr int KUNITS = PF_BK * DC;             // K chunks per block
+    constexpr int VUNITS = (PF_BK / 2) * DC;       // V (key pair, chunk) units per block
+    constexpr int KU = KUNITS / PF_NT;
+    constexpr int VU = VUNITS / PF_NT;
+    constexpr int DS = D / 32;                     // MFMA steps over d for the scores
+    constexpr int DT = D / 16;                     // 16-wide d tiles of the output
+    constexpr int TOK = PF_ROWS / GQ;              // tokens per query block
+    constexpr int KTILE = PF_BK * KPITCH;          // elements
+    constexpr int VTILE = D * VPITCH;
+    constexpr int BUF = KTILE + VTILE;
+    constexpr int NV = DT * 8 + 4;                 // floats a lane publishes in the merge
+    static_assert(KUNITS % PF_NT == 0 && VUNITS % PF_NT == 0, "blocks must split evenly over the threads");
+    static_assert(2 * 3 * NV * 64 * 4 <= NBUF * BUF * 2, "merge area exceeds the tiles");
+
+    __shared__ __align__(16) uint16_t smem[NBUF * BUF];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave & 1, kq = wave >> 1;      // row group, key quarter
+    const int col = lane & 15, kg = lane >> 4;
+    const int heads = a.kv_heads * a.batch;
+    const int pair = (int)(blockIdx.x / heads);
+    const int g = (int)(blockIdx.x % heads) % a.kv_heads, b = (int)(blockIdx.x % heads) / a.kv_heads;
+    const int S = a.seq, kv_len = a.kv_len;
+    const int p0 = kv_len - S;                      // position of token 0 of the block
+    const int nqb = (S + TOK - 1) / TOK;
+
+    const size_t head_off = ((size_t)b * a.kv_heads + g) * a.capacity * D;
+    const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k) + head_off;
+    const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v) + head_off;
+    const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
+    uint16_t* obase = reinterpret_cast<uint16_t*>(a.out);
+    const float c = PF_LOG2E / sqrtf((float)D);     // scores to the base-2 domain
+
+    // Block loads: K chunk u -> key u / DC, chunk u % DC; V unit u -> keys
+    // 2 (u / DC) and 2 (u / DC) + 1, chunk u % DC. Keys past kv_len are clamped
+    // (their scores are masked).
+    uint4 kr[KU], va[VU], vb[VU];
+    auto load_block = [&](int kb) {
+        const int key0 = kb * PF_BK;
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            const int u = j * PF_NT + tid;
+            const int key = min(key0 + u / DC, kv_len - 1);
+            kr[j] = load_u4(kbase + (size_t)key * D + (u % DC) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int u = j * PF_NT + tid;
+            const int key = key0 + 2 * (u / DC);
+            va[j] = load_u4(vbase + (size_t)min(key, kv_len - 1) * D + (u % DC) * 8);
+            vb[j] = load_u4(vbase + (size_t)min(key + 1, kv_len - 1) * D + (u % DC) * 8);
+        }
+    };
+    auto store_block = [&](int buf) {
+        uint16_t* ks = smem + buf * BUF;
+        uint16_t* vt = ks + KTILE;
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            const int u = j * PF_NT + tid;
+            *reinterpret_cast<uint4*>(&ks[(u / DC) * KPITCH + (u % DC) * 8]) = kr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int u = j * PF_NT + tid;
+            const int kp = u / DC, d0 = (u % DC) * 8;
+            const int kps = vt_pair(kp, d0);        // d0 .. d0 + 7 share d / 8
+            const uint32_t* A = &va[j].x;
+            const uint32_t* B = &vb[j].x;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                // (V[2kp][d], V[2kp+1][d]) for d = d0 + 2t and d0 + 2t + 1
+                *reinterpret_cast<uint32_t*>(&vt[(d0 + 2 * t) * VPITCH + 2 * kps]) =
+                    __builtin_amdgcn_perm(B[t], A[t], 0x05040100u);
+                *reinterpret_cast<uint32_t*>(&vt[(d0 + 2 * t + 1) * VPITCH + 2 * kps]) =
+                    __builtin_amdgcn_perm(B[t], A[t], 0x07060302u);
+            }
+        }
+    };
+
+    const int kp_lane = kq * 16 + kg * 2;           // first key pair of the lane's run
+    // Query blocks pair and nqb - 1 - pair (once when they coincide).
+    for (int ph = 0; ph < 2; ++ph) {
+        const int qblk = ph == 0 ? pair : nqb - 1 - pair;
+        if (ph == 1 && qblk == pair) break;
+        const int i0 = qblk * TOK;                  // first token of the query block
+        const int ilast = min(i0 + TOK, S) - 1;
+        const int nblk = (p0 + ilast) / PF_BK + 1;  // blocks up to the last token's position
+        const int nfull = (p0 + i0 + 1) / PF_BK;    // blocks every row sees whole
+        const int plast = p0 + ilast;
+
+        // This lane's two query rows (one per column tile): token and head.
+        int tok[2], pos[2];
+        uint4 qf[2][DS];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int r = rg * 32 + rt * 16 + col;
+            tok[rt] = i0 + r / GQ;
+            pos[rt] = p0 + tok[rt];
+            const int hq = g * GQ + r % GQ;
+            const uint16_t* qrow = qbase + (((size_t)b * S + min(tok[rt], S - 1)) * a.q_heads + hq) * D;
+#pragma unroll
+            for (int s = 0; s < DS; ++s) qf[rt][s] = load_u4(qrow + s * 32 + kg * 8);
+        }
+
+        float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+        f32x4_t ot[DT][2];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        load_block(0);
+        store_block(0);
+        // Every load issued so far (the query fragments included) has landed,
+        // so the waits inside the loop only ever cover the next block's loads.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+
+        // One block for this wave: its 32 keys x its 32 rows.
+        auto block = [&](int kb, int buf, bool masked) {
+            const uint16_t* kt = smem + buf * BUF + kq * PF_KW * KPITCH;
+            const uint16_t* vtb = smem + buf * BUF + KTILE;
+
+            // S^T tiles: keys 32 kq + 16 t .. + 15 of the block x this wave's
+            // rows; four independent accumulation chains.
+            f32x4_t st[2][2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) st[t][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < DS; ++s) {
+                uint4 kf[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    kf[t] = *reinterpret_cast<const uint4*>(&kt[(t * 16 + col) * KPITCH + s * 32 + kg * 8]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int rt = 0; rt < 2; ++rt) st[t][rt] = mfma16x32(kf[t], qf[rt][s], st[t][rt]);
+            }
+
+            __builtin_amdgcn_sched_barrier(0);
+
+            // Online softmax; the lane holds keys 32 kq + 16 t + 4 kg + j.
+            float mx[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                if (masked) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int key = kb * PF_BK + kq * PF_KW + t * 16 + kg * 4 + j;
+                            if (key > pos[rt]) st[t][rt][j] = -INFINITY;
+                        }
+                }
+                const float m8 = pf_max3(pf_max3(st[0][rt][0], st[0][rt][1], st[0][rt][2]),
+                                         pf_max3(st[0][rt][3], st[1][rt][0], st[1][rt][1]),
+                                         pf_max2(st[1][rt][2], st[1][rt][3]));
+                mx[rt] = pf_max4(m8) * c;
+            }
+            const bool grow = mx[0] > mrun[0] + PF_SLACK || mx[1] > mrun[1] + PF_SLACK;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const float mnew = fmaxf(mrun[rt], mx[rt]);
+                    const float al = __builtin_amdgcn_exp2f(mrun[rt] - (mnew == -INFINITY ? 0.f : mnew));
+                    mrun[rt] = mnew;
+                    lrun[rt] *= al;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ot[dt][rt][j] *= al;
+                }
+            }
+            uint4 pk[2];
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const float mref = mrun[rt] == -INFINITY ? 0.f : mrun[rt];
+                float sum = 0.f;
+                uint32_t pw[2][2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][rt][2 * h2], c, -mref));
+                        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][rt][2 * h2 + 1], c, -mref));
+                        const uint32_t p = pack_bf16x2(e0, e1);
+                        sum = dot2_bf16(p, 0x3f803f80u, sum);
+                        pw[t][h2] = p;
+                    }
+                lrun[rt] += pf_sum4(sum);
+                pk[rt] = make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // O^T += V^T P^T: V^T rows d, the same 8 keys per lane as the probabilities.
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = dt * 16 + col;
+                const uint16_t* vrow = &vtb[d * VPITCH + 2 * vt_pair(kp_lane, d)];
+                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+                const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = mfma16x32(vf, pk[rt], ot[dt][rt]);
+            }
+        };
+
+        auto step = [&](int kb, bool masked) {
+            const int buf = kb & 1;
+            if (kb + 1 < nblk) load_block(kb + 1);
+            // a quarter wholly past the last token's position holds no visible key
+            if (!masked || kb * PF_BK + kq * PF_KW <= plast) block(kb, buf, masked);
+            if (kb + 1 < nblk) store_block(buf ^ 1);
+            __syncthreads();
+        };
+        // Blocks every row sees whole, then the diagonal ones, in two loops so
+        // that each has a single body.
+        int kb = 0;
+        for (; kb < nfull; ++kb) step(kb, false);
+        for (; kb < nblk; ++kb) step(kb, true);
+
+        // Merge the key quarters: waves of quarters 1..3 publish (m, l, O^T),
+        // the quarter-0 wave of each row group combines and writes the output.
+        // Layout [row group][quarter - 1][value][lane]: lane-contiguous.
+        float* mgbase = reinterpret_cast<float*>(smem) + rg * 3 * NV * 64;
+        if (kq != 0) {
+            float* mg = mgbase + (kq - 1) * NV * 64;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                mg[(2 * rt) * 64 + lane] = mrun[rt];
+                mg[(2 * rt + 1) * 64 + lane] = lrun[rt];
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mg[(4 + (dt * 2 + rt) * 4 + j) * 64 + lane] = ot[dt][rt][j];
+            }
+        }
+        __syncthreads();
+        if (kq == 0) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                float mq[3], w[3];
+                float m = mrun[rt];                   // finite: key 0 is in quarter 0
+#pragma unroll
+                for (int e = 0; e < 3; ++e) {
+                    mq[e] = mgbase[(e * NV + 2 * rt) * 64 + lane];
+                    m = fmaxf(m, mq[e]);
+                }
+                const float w0 = __builtin_amdgcn_exp2f(mrun[rt] - m);
+                float l = lrun[rt] * w0;
+#pragma unroll
+                for (int e = 0; e < 3; ++e) {
+                    w[e] = __builtin_amdgcn_exp2f(mq[e] - m);
+                    l += mgbase[(e * NV + 2 * rt + 1) * 64 + lane] * w[e];
+                }
+                const float inv = 1.0f / l;
+                if (tok[rt] < S) {
+                    const int r = rg * 32 + rt * 16 + col;
+                    const int hq = g * GQ + r % GQ;
+                    uint16_t* orow = obase + (((size_t)b * S + tok[rt]) * a.q_heads + hq) * D;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        float o[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            float acc = ot[dt][rt][j] * w0;
+#pragma unroll
+                            for (int e = 0; e < 3; ++e)
+                                acc += mgbase[(e * NV + 4 + (dt * 2 + rt) * 4 + j) * 64 + lane] * w[e];
+                            o[j] = acc * inv;
+                        }
+                        *reinterpret_cast<uint2*>(orow + dt * 16 + kg * 4) =
+                            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+                    }
+                }
+            }
+        }
+        __syncthreads();                            // the next query block reuses the tiles
+    }
+}
+
+template <int D>
+static hipError_t prefill_launch_d(const PrefillArgs& a, int gq, hipStream_t s) {
+    const int tok = PF_ROWS / gq;
+    const int64_t nqb = (a.seq + tok - 1) / tok;
+    const int64_t blocks = (nqb + 1) / 2 * a.kv_heads * a.batch;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    dim3 grid((unsigned)blocks);
+    switch (gq) {
+        case 1: hipLaunchKernelGGL((attn_prefill_kernel<D, 1>), grid, dim3(PF_NT), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((attn_prefill_kernel<D, 2>), grid, dim3(PF_NT), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((attn_prefill_kernel<D, 4>), grid, dim3(PF_NT), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((attn_prefill_kernel<D, 8>), grid, dim3(PF_NT), 0, s, a); break;
+        case 16: hipLaunchKernelGGL((attn_prefill_kernel<D, 16>), grid, dim3(PF_NT), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t prefill_attn_launch(const PrefillArgs& a, hipStream_t s) {
+    const int gq = a.q_heads / a.kv_heads;
+    if (a.head_dim == 64) return prefill_launch_d<64>(a, gq, s);
+    if (a.head_dim == 128) return prefill_launch_d<128>(a, gq, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tpk

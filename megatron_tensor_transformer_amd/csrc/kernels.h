@@ -107,4 +107,16 @@ struct GemmArgs {
 bool gemm_supported(int M, int N, int K, int epi);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
 
+// Causal grouped-query attention over a block of seq new tokens (bf16).
+struct PrefillArgs {
+    const void* q;      // [batch, seq, q_heads * d]
+    const void* k;      // [batch, kv_heads, capacity, d]
+    const void* v;
+    void* out;          // [batch, seq, q_heads * d]
+    int64_t capacity;
+    int kv_len;         // token i of the block sits at position kv_len - seq + i
+    int batch, seq, q_heads, kv_heads, head_dim;
+};
+hipError_t prefill_attn_launch(const PrefillArgs& a, hipStream_t stream);
+
 }  // namespace tpk

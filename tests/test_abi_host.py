@@ -195,6 +195,26 @@ def test_attention_validation():
     assert tp.tp_attention_workspace_bytes(16, 8, 1, 128, 8192) > 0
 
 
+def prefill(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=2, S=2048, qh=8, kvh=1, d=128, cap=2048,
+            L=2048, dt=tp.TP_BF16):
+    return rejected(tp.lib.tp_prefill_attention(q, k, v, out, B, S, qh, kvh, d, cap, L, dt, None))
+
+
+def test_prefill_attention_validation():
+    assert prefill(dt=tp.TP_F32) == "TP_ERR_DTYPE"
+    assert prefill(v=None) == "TP_ERR_NULL"
+    assert prefill(out=A + 192 * MB + 4) == "TP_ERR_ALIGN"
+    assert prefill(S=0) == "TP_ERR_KV"
+    assert prefill(S=2049) == "TP_ERR_KV"            # more new tokens than keys
+    assert prefill(L=2049) == "TP_ERR_KV"            # beyond the cache
+    assert prefill(d=96) == "TP_ERR_SHAPE"
+    assert prefill(qh=32, kvh=1) == "TP_ERR_SHAPE"   # 32 q heads per kv head
+    assert prefill(qh=9, kvh=2) == "TP_ERR_INDIVISIBLE"
+    assert prefill(B=70000) == "TP_ERR_SHAPE"
+    assert prefill(out=A + 64 * MB + 256) == "TP_ERR_ALIAS"
+    assert prefill(out=A + 4 * MB) == "TP_ERR_ALIAS"  # inside q
+
+
 def test_layer_validation():
     d = tp.make_desc(8192, 28672, 64, 8, 128, seq_len=8192, batch=16)
     p = tp.tp_shard_plan(d, 8, 3)

@@ -306,6 +306,51 @@ def test_decode_attention_shapes(case):
     check(f"attention {case}", host(out), ref, TOL["bf16"])
 
 
+PREFILL_CASES = [
+    # batch, q_heads, kv_heads, head_dim, capacity, seq, kv_len
+    (1, 1, 1, 64, 1, 1, 1),            # one token, one key
+    (1, 1, 1, 128, 5, 1, 5),           # one new token after four cached ones (a decode step)
+    (2, 4, 2, 128, 300, 257, 257),     # prompt from scratch, ragged last block
+    (3, 2, 2, 64, 130, 130, 130),      # GQ 1: 128 tokens per workgroup, two query blocks
+    (1, 16, 1, 64, 600, 100, 555),     # GQ 16: 8 tokens per workgroup, long cached prefix
+    (2, 8, 4, 64, 1000, 77, 1000),     # GQ 2, chunk at the end of a full cache
+    (2, 8, 1, 128, 3000, 200, 2900),   # 70B t=8 head shard, chunked prefill
+    (1, 4, 4, 128, 64, 64, 64),        # GQ 1 with several kv heads, one key block
+    (2, 8, 1, 128, 2048, 2048, 2048),  # 70B t=8 head shard at batch 2 x 2048 tokens
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_prefill_attention_shapes(case):
+    B, qh, kvh, d, cap, S, kv_len = case
+    seed = 300 + cap + S
+    q = W.to_bf16(W.normal(seed, 0, (B, S, qh * d)))
+    k = W.to_bf16(W.normal(seed, 1, (B, kvh, cap, d)))
+    v = W.to_bf16(W.normal(seed, 2, (B, kvh, cap, d)))
+    ref = L.prefill_attention(q, k, v, kv_len, qh, kvh, d)
+    out = torch.full((B, S, qh * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tp.tp_prefill_attention(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, kv_len, qh)
+    torch.cuda.synchronize()
+    check(f"prefill attention {case}", host(out), ref, TOL["bf16"])
+
+
+def test_prefill_last_token_matches_decode():
+    """The last token of a prefill block attends to every cached key, as decode does."""
+    B, qh, kvh, d, cap, S, kv_len = 4, 8, 1, 128, 1024, 96, 1000
+    q = W.to_bf16(W.normal(41, 0, (B, S, qh * d)))
+    k = dev(W.to_bf16(W.normal(41, 1, (B, kvh, cap, d))), "bf16")
+    v = dev(W.to_bf16(W.normal(41, 2, (B, kvh, cap, d))), "bf16")
+    tq = dev(q, "bf16")
+    pre = empty((B, S, qh * d), torch.bfloat16)
+    tp.tp_prefill_attention(tq, k, v, pre, kv_len, qh)
+    dec = empty((B, qh * d), torch.bfloat16)
+    tp.tp_decode_attention(tq[:, S - 1].contiguous(), k, v, dec, kv_len, qh)
+    torch.cuda.synchronize()
+    ref = L.decode_attention(q[:, S - 1], host(k), host(v), kv_len, qh, kvh, d)
+    check("prefill last token", host(pre)[:, S - 1], ref, TOL["bf16"])
+    check("decode of the same token", host(dec), ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("t", [1, 3, 8])
 @pytest.mark.parametrize("shape", [(5, 7), (16, 8192), (3, 1)])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])

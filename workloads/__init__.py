@@ -3,7 +3,7 @@
 This module is the only code that both the CPU oracle and the HIP path's tests
 use. It holds no arithmetic of the layer itself: it draws normal variates from
 a seeded generator, rounds them to the storage precision the GPU receives, and
-records the shapes of the five measured workloads.
+records the shapes of the measured workloads.
 
 Seeding: every tensor is drawn from ``numpy.random.default_rng([workload_id,
 tensor_id])`` with ``standard_normal(dtype=float32)`` and then scaled by its
@@ -23,7 +23,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 # Tensor ids (second seed word).
-X, GAMMA1, W_Q, W_K, W_V, W_O, GAMMA2, W_GATE, W_UP, W_DOWN, K_CACHE, V_CACHE, ATTN_IN = range(13)
+X, GAMMA1, W_Q, W_K, W_V, W_O, GAMMA2, W_GATE, W_UP, W_DOWN, K_CACHE, V_CACHE, ATTN_IN, Q_PREFILL = range(14)
 
 WEIGHT_STD = 0.02
 
@@ -107,6 +107,9 @@ WORKLOADS: Dict[int, Workload] = {
     5: Workload(5, "70B-shaped full layer decode shard, bf16, t=8, batch 16, KV 8192",
                 "bf16", hidden=8192, intermediate=28672, t=8, tokens=(16,), n_q_heads=64, n_kv_heads=8,
                 head_dim=128, kv_len=8192, norm=True),
+    6: Workload(6, "70B-shaped causal prefill attention shard, bf16, t=8, batch 2 x 2048 tokens",
+                "bf16", hidden=8192, intermediate=0, t=8, tokens=(4096,), n_q_heads=64, n_kv_heads=8,
+                head_dim=128, kv_len=2048),
 }
 
 
@@ -155,3 +158,13 @@ def attention_inputs(workload_id: int, hidden: int, n_q: int, n_kv: int, d: int,
 def attn_proj_input(workload_id: int, m: int, cols: int, dtype: str) -> np.ndarray:
     """Synthetic attention output fed to W_o when no attention runs in between."""
     return storage_round(normal(workload_id, ATTN_IN, (m, cols)), dtype)
+
+
+def prefill_attention_inputs(workload_id: int, batch: int, seq: int, n_q: int, n_kv: int, d: int,
+                             capacity: int, dtype: str) -> Dict[str, np.ndarray]:
+    """q [B, seq, n_q d] for a block of new tokens; K/V caches [B, n_kv, capacity, d]; all N(0, 1)."""
+    return {
+        "q": storage_round(normal(workload_id, Q_PREFILL, (batch, seq, n_q * d)), dtype),
+        "k_cache": storage_round(normal(workload_id, K_CACHE, (batch, n_kv, capacity, d)), dtype),
+        "v_cache": storage_round(normal(workload_id, V_CACHE, (batch, n_kv, capacity, d)), dtype),
+    }
