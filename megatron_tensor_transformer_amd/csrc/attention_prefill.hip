@@ -22,13 +22,17 @@
 //    and the probabilities already form the B operand of O^T = V^T P^T
 //    (a lane's 8 k-values are keys 4kg..4kg+3 of the wave's two key tiles;
 //    the V^T operand reads the same 8 keys).
-//  - K and V go through LDS in blocks of 128 keys, double buffered: the next
-//    block's rows are loaded into registers while the current block is
-//    multiplied, then written to the other buffer; one barrier per block.
-//    V is stored transposed (V^T[d][key]); the transpose pairs two keys of
-//    one column with one v_perm per dword, and key pairs are XOR-swizzled by
-//    d / 8 so that both the transposing stores and the operand reads spread
-//    over the LDS banks.
+//  - K and V go through LDS in blocks of 128 keys, double buffered, one
+//    barrier per block: while a block is multiplied, the next block's V comes
+//    into registers, to be written to the other stage transposed
+//    (V^T[d][key]) after the work, and its K goes straight from global
+//    memory into the other stage (global_load_lds, chunks XOR-swizzled by
+//    row) once this block's LDS reads are issued.
+//    The transpose pairs two keys of one column with one v_perm per dword,
+//    and key pairs are XOR-swizzled by d / 8 so that both the transposing
+//    stores and the operand reads spread over the LDS banks. Each wave reads
+//    its K fragments of a block at once, ahead of the score products, and
+//    its V fragments behind them, ahead of the softmax.
 //  - The online softmax (running max and sum per row, in the base-2 domain
 //    with the 1/sqrt(D) scale folded into one multiply-add) runs in
 //    registers. The reference maximum is raised only when a score exceeds it
@@ -50,7 +54,6 @@ constexpr int PF_NT = 512;       // threads (8 waves)
 constexpr int PF_ROWS = 64;      // query rows per query block
 constexpr int PF_BK = 128;       // keys per block
 constexpr int PF_KW = 32;        // keys per wave per block
-constexpr int NBUF = 2;          // K/V block buffers in LDS
 constexpr float PF_SLACK = 8.0f; // log2 of the largest unnormalised probability
 constexpr float PF_LOG2E = 1.4426950408889634f;
 
@@ -97,26 +100,38 @@ __device__ __forceinline__ int vt_pair(int kp, int d) {
     return kp ^ (((g & 3) << 1) | ((g & 4) << 2));
 }
 
+// Position of K chunk lc (16 bytes) of key row r in the unpadded K tile: the
+// chunk index is XOR-swizzled with bits of the row, so that the 16 rows a
+// quarter-wave reads for one MFMA operand fall into distinct LDS banks.
+template <int D>
+__device__ __forceinline__ int k_chunk(int r, int lc) {
+    return lc ^ (D == 128 ? (r & 15) : ((r >> 1) & 7));
+}
+
+__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
 template <int D, int GQ>
 __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     constexpr int DC = D / 8;                      // 16-byte chunks per row
-    constexpr int KPITCH = D + 8;                  // K tile row pitch (elements)
     constexpr int VPITCH = PF_BK + 8;              // V^T tile row pitch (elements)
-    constexpr int KUNITS = PF_BK * DC;             // K chunks per block
+    constexpr int KDMA = PF_BK * D * 2 / 1024 / 8; // 1 KB transfers per wave per K block
     constexpr int VUNITS = (PF_BK / 2) * DC;       // V (key pair, chunk) units per block
-    constexpr int KU = KUNITS / PF_NT;
     constexpr int VU = VUNITS / PF_NT;
     constexpr int DS = D / 32;                     // MFMA steps over d for the scores
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
     constexpr int TOK = PF_ROWS / GQ;              // tokens per query block
-    constexpr int KTILE = PF_BK * KPITCH;          // elements
+    constexpr int KTILE = PF_BK * D;               // elements
     constexpr int VTILE = D * VPITCH;
-    constexpr int BUF = KTILE + VTILE;
     constexpr int NV = DT * 8 + 4;                 // floats a lane publishes in the merge
-    static_assert(KUNITS % PF_NT == 0 && VUNITS % PF_NT == 0, "blocks must split evenly over the threads");
-    static_assert(2 * 3 * NV * 64 * 4 <= NBUF * BUF * 2, "merge area exceeds the tiles");
+    static_assert(VUNITS % PF_NT == 0 && KDMA >= 1, "blocks must split evenly over the threads");
+    static_assert(4 * NV * 64 * 4 <= 2 * (KTILE + VTILE) * 2, "merge area exceeds the tiles");
 
-    __shared__ __align__(16) uint16_t smem[NBUF * BUF];
+    // Two stages, each a K tile then a V^T tile.
+    constexpr int BUF = KTILE + VTILE;
+    __shared__ __align__(16) uint16_t smem[2 * BUF];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = wave & 1, kq = wave >> 1;      // row group, key quarter
@@ -135,34 +150,38 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     uint16_t* obase = reinterpret_cast<uint16_t*>(a.out);
     const float c = PF_LOG2E / sqrtf((float)D);     // scores to the base-2 domain
 
-    // Block loads: K chunk u -> key u / DC, chunk u % DC; V unit u -> keys
-    // 2 (u / DC) and 2 (u / DC) + 1, chunk u % DC. Keys past kv_len are clamped
-    // (their scores are masked).
-    uint4 kr[KU], va[VU], vb[VU];
-    auto load_block = [&](int kb) {
+    // K block: wave transfer i covers tile bytes [(i * 8 + wave) KB, + 1 KB),
+    // lane L the 16 bytes at L * 16 in it: row e / D, physical chunk
+    // (e % D) / 8, which holds logical chunk k_chunk(row, physical).
+    int klast = kv_len - 1;                         // last valid key; loads clamp to it
+    int krow[KDMA], kcol[KDMA];
+#pragma unroll
+    for (int i = 0; i < KDMA; ++i) {
+        const int e = (i * 8 + wave) * 512 + lane * 8;
+        krow[i] = e / D;
+        kcol[i] = k_chunk<D>(krow[i], (e % D) / 8) * 8;
+    }
+    auto load_k = [&](int kb, uint16_t* kdst) {
         const int key0 = kb * PF_BK;
 #pragma unroll
-        for (int j = 0; j < KU; ++j) {
-            const int u = j * PF_NT + tid;
-            const int key = min(key0 + u / DC, kv_len - 1);
-            kr[j] = load_u4(kbase + (size_t)key * D + (u % DC) * 8);
-        }
+        for (int i = 0; i < KDMA; ++i)
+            dma16(kbase + (size_t)min(key0 + krow[i], klast) * D + kcol[i], kdst + (i * 8 + wave) * 512);
+    };
+    // V unit u -> keys 2 (u / DC) and 2 (u / DC) + 1, chunk u % DC, through
+    // registers (the tile is stored transposed). Keys past kv_len are
+    // clamped; their scores are masked.
+    uint4 va[VU], vb[VU];
+    auto load_v = [&](int kb) {
+        const int key0 = kb * PF_BK;
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
             const int u = j * PF_NT + tid;
             const int key = key0 + 2 * (u / DC);
-            va[j] = load_u4(vbase + (size_t)min(key, kv_len - 1) * D + (u % DC) * 8);
-            vb[j] = load_u4(vbase + (size_t)min(key + 1, kv_len - 1) * D + (u % DC) * 8);
+            va[j] = load_u4(vbase + (size_t)min(key, klast) * D + (u % DC) * 8);
+            vb[j] = load_u4(vbase + (size_t)min(key + 1, klast) * D + (u % DC) * 8);
         }
     };
-    auto store_block = [&](int buf) {
-        uint16_t* ks = smem + buf * BUF;
-        uint16_t* vt = ks + KTILE;
-#pragma unroll
-        for (int j = 0; j < KU; ++j) {
-            const int u = j * PF_NT + tid;
-            *reinterpret_cast<uint4*>(&ks[(u / DC) * KPITCH + (u % DC) * 8]) = kr[j];
-        }
+    auto store_v = [&](uint16_t* vt) {
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
             const int u = j * PF_NT + tid;
@@ -186,6 +205,9 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     for (int ph = 0; ph < 2; ++ph) {
         const int qblk = ph == 0 ? pair : nqb - 1 - pair;
         if (ph == 1 && qblk == pair) break;
+        // Opaque per query block: keeps the compiler from hoisting the first
+        // block's load addresses out of this loop and holding them throughout.
+        asm volatile("" : "+s"(klast));
         const int i0 = qblk * TOK;                  // first token of the query block
         const int ilast = min(i0 + TOK, S) - 1;
         const int nblk = (p0 + ilast) / PF_BK + 1;  // blocks up to the last token's position
@@ -213,39 +235,57 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        load_block(0);
-        store_block(0);
+        load_k(0, smem);
+        load_v(0);
+        store_v(smem + KTILE);
         // Every load issued so far (the query fragments included) has landed,
         // so the waits inside the loop only ever cover the next block's loads.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
-        // One block for this wave: its 32 keys x its 32 rows.
-        auto block = [&](int kb, int buf, bool masked) {
-            const uint16_t* kt = smem + buf * BUF + kq * PF_KW * KPITCH;
-            const uint16_t* vtb = smem + buf * BUF + KTILE;
+        // One block for this wave, its 32 keys x its 32 rows, in two halves:
+        // the front reads every LDS fragment it needs and forms the scores, the
+        // back weighs them and accumulates the outputs.
+        f32x4_t st[2][2];
+        uint4 vf[DT];
+        auto front = [&](const uint16_t* kt, const uint16_t* vtb) {
+            // The block's K fragments first, all at once.
+            uint4 kf[DS][2];
+#pragma unroll
+            for (int s = 0; s < DS; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r = kq * PF_KW + t * 16 + col;
+                    kf[s][t] = *reinterpret_cast<const uint4*>(&kt[r * D + k_chunk<D>(r, s * 4 + kg) * 8]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
 
             // S^T tiles: keys 32 kq + 16 t .. + 15 of the block x this wave's
             // rows; four independent accumulation chains.
-            f32x4_t st[2][2];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) st[t][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < DS; ++s) {
-                uint4 kf[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    kf[t] = *reinterpret_cast<const uint4*>(&kt[(t * 16 + col) * KPITCH + s * 32 + kg * 8]);
+            for (int s = 0; s < DS; ++s)
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) st[t][rt] = mfma16x32(kf[t], qf[rt][s], st[t][rt]);
+                    for (int rt = 0; rt < 2; ++rt) st[t][rt] = mfma16x32(kf[s][t], qf[rt][s], st[t][rt]);
+
+            // V^T fragments (the same 8 keys per lane as the probabilities),
+            // read now so that they land during the softmax.
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = dt * 16 + col;
+                const uint16_t* vrow = &vtb[d * VPITCH + 2 * vt_pair(kp_lane, d)];
+                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+                vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
-
             __builtin_amdgcn_sched_barrier(0);
-
+        };
+        auto back = [&](int kb, bool masked) {
             // Online softmax; the lane holds keys 32 kq + 16 t + 4 kg + j.
             float mx[2];
 #pragma unroll
@@ -299,25 +339,33 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
 
-            // O^T += V^T P^T: V^T rows d, the same 8 keys per lane as the probabilities.
+            // O^T += V^T P^T.
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 16 + col;
-                const uint16_t* vrow = &vtb[d * VPITCH + 2 * vt_pair(kp_lane, d)];
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-                const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = mfma16x32(vf, pk[rt], ot[dt][rt]);
-            }
+                for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = mfma16x32(vf[dt], pk[rt], ot[dt][rt]);
         };
 
+        // One block for the workgroup. The next block's V comes into registers
+        // first; its K goes by DMA into the other stage once this block's LDS
+        // reads are issued (a transfer into LDS ahead of them would make the
+        // compiler wait for it before reading); V is written transposed after
+        // the work.
         auto step = [&](int kb, bool masked) {
             const int buf = kb & 1;
-            if (kb + 1 < nblk) load_block(kb + 1);
+            const bool more = kb + 1 < nblk;
+            uint16_t* cur = smem + buf * BUF;
+            uint16_t* nxt = smem + (buf ^ 1) * BUF;
+            if (more) load_v(kb + 1);
             // a quarter wholly past the last token's position holds no visible key
-            if (!masked || kb * PF_BK + kq * PF_KW <= plast) block(kb, buf, masked);
-            if (kb + 1 < nblk) store_block(buf ^ 1);
+            const bool active = !masked || kb * PF_BK + kq * PF_KW <= plast;
+            if (active) front(cur, cur + KTILE);
+            if (more) load_k(kb + 1, nxt);
+            if (active) back(kb, masked);
+            if (more) {
+                store_v(nxt + KTILE);
+                __builtin_amdgcn_s_waitcnt(0);      // the K transfers have landed in LDS
+            }
             __syncthreads();
         };
         // Blocks every row sees whole, then the diagonal ones, in two loops so
@@ -326,12 +374,10 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
         for (; kb < nfull; ++kb) step(kb, false);
         for (; kb < nblk; ++kb) step(kb, true);
 
-        // Merge the key quarters: waves of quarters 1..3 publish (m, l, O^T),
-        // the quarter-0 wave of each row group combines and writes the output.
-        // Layout [row group][quarter - 1][value][lane]: lane-contiguous.
-        float* mgbase = reinterpret_cast<float*>(smem) + rg * 3 * NV * 64;
-        if (kq != 0) {
-            float* mg = mgbase + (kq - 1) * NV * 64;
+        // Merge the key quarters by their log-sum-exp weights, in two rounds
+        // through the idle tiles: quarters 2, 3 into 0, 1, then 1 into 0.
+        // Layout [value][lane]: lane-contiguous.
+        auto publish = [&](float* mg) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
                 mg[(2 * rt) * 64 + lane] = mrun[rt];
@@ -341,45 +387,44 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) mg[(4 + (dt * 2 + rt) * 4 + j) * 64 + lane] = ot[dt][rt][j];
             }
-        }
-        __syncthreads();
-        if (kq == 0) {
+        };
+        auto combine = [&](const float* mg) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                float mq[3], w[3];
-                float m = mrun[rt];                   // finite: key 0 is in quarter 0
+                const float mb = mg[(2 * rt) * 64 + lane], lb = mg[(2 * rt + 1) * 64 + lane];
+                const float m = fmaxf(mrun[rt], mb);
+                const float mr = m == -INFINITY ? 0.f : m;      // both halves empty: stay empty
+                const float wa = __builtin_amdgcn_exp2f(mrun[rt] - mr), wb = __builtin_amdgcn_exp2f(mb - mr);
+                mrun[rt] = m;
+                lrun[rt] = lrun[rt] * wa + lb * wb;
 #pragma unroll
-                for (int e = 0; e < 3; ++e) {
-                    mq[e] = mgbase[(e * NV + 2 * rt) * 64 + lane];
-                    m = fmaxf(m, mq[e]);
-                }
-                const float w0 = __builtin_amdgcn_exp2f(mrun[rt] - m);
-                float l = lrun[rt] * w0;
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int e = 0; e < 3; ++e) {
-                    w[e] = __builtin_amdgcn_exp2f(mq[e] - m);
-                    l += mgbase[(e * NV + 2 * rt + 1) * 64 + lane] * w[e];
-                }
-                const float inv = 1.0f / l;
-                if (tok[rt] < S) {
-                    const int r = rg * 32 + rt * 16 + col;
-                    const int hq = g * GQ + r % GQ;
-                    uint16_t* orow = obase + (((size_t)b * S + tok[rt]) * a.q_heads + hq) * D;
+                    for (int j = 0; j < 4; ++j)
+                        ot[dt][rt][j] = ot[dt][rt][j] * wa + mg[(4 + (dt * 2 + rt) * 4 + j) * 64 + lane] * wb;
+            }
+        };
+        auto region = [&](int i) -> float* { return reinterpret_cast<float*>(smem) + i * NV * 64; };
+        if (kq >= 2) publish(region(rg * 2 + (kq - 2)));
+        __syncthreads();
+        if (kq < 2) combine(region(rg * 2 + kq));
+        __syncthreads();
+        if (kq == 1) publish(region(rg));
+        __syncthreads();
+        if (kq == 0) {
+            combine(region(rg));
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) {
-                        float o[4];
+            for (int rt = 0; rt < 2; ++rt) {
+                if (tok[rt] >= S) continue;
+                const float inv = 1.0f / lrun[rt];
+                const int r = rg * 32 + rt * 16 + col;
+                const int hq = g * GQ + r % GQ;
+                uint16_t* orow = obase + (((size_t)b * S + tok[rt]) * a.q_heads + hq) * D;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            float acc = ot[dt][rt][j] * w0;
-#pragma unroll
-                            for (int e = 0; e < 3; ++e)
-                                acc += mgbase[(e * NV + 4 + (dt * 2 + rt) * 4 + j) * 64 + lane] * w[e];
-                            o[j] = acc * inv;
-                        }
-                        *reinterpret_cast<uint2*>(orow + dt * 16 + kg * 4) =
-                            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-                    }
-                }
+                for (int dt = 0; dt < DT; ++dt)
+                    *reinterpret_cast<uint2*>(orow + dt * 16 + kg * 4) =
+                        make_uint2(pack_bf16x2(ot[dt][rt][0] * inv, ot[dt][rt][1] * inv),
+                                   pack_bf16x2(ot[dt][rt][2] * inv, ot[dt][rt][3] * inv));
             }
         }
         __syncthreads();                            // the next query block reuses the tiles
