@@ -148,6 +148,50 @@ def attention_block(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len: int, n_q: i
     return {"u": u, "q": q, "k": k, "v": v, "k_cache": kc, "v_cache": vc, "o": o, "y": y}
 
 
+def append_kv_block(k_cache, v_cache, k_new, v_new, kv_len: int, n_kv: int, d: int):
+    """Copies of the caches with a block's k, v [B, S, n_kv * d] at positions kv_len - S .. kv_len - 1."""
+    kc = f64(k_cache).copy()
+    vc = f64(v_cache).copy()
+    B, S = np.shape(k_new)[0], np.shape(k_new)[1]
+    kc[:, :, kv_len - S:kv_len, :] = f64(k_new).reshape(B, S, n_kv, d).transpose(0, 2, 1, 3)
+    vc[:, :, kv_len - S:kv_len, :] = f64(v_new).reshape(B, S, n_kv, d).transpose(0, 2, 1, 3)
+    return kc, vc
+
+
+def attention_block_prefill(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len: int, n_q: int, n_kv: int,
+                            d: int, gamma=None, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """The attention block for a block of S new tokens per sequence, x [B, S, H].
+
+    Optional RMSNorm and the QKV projections of every token, the block's k, v
+    written to cache positions kv_len - S .. kv_len - 1, causal prefill
+    attention, output projection. Returns y [B, S, H] (and the pieces).
+    """
+    x = f64(x)
+    B, S, H = x.shape
+    u = rmsnorm(x.reshape(B * S, H), gamma, eps) if gamma is not None else x.reshape(B * S, H)
+    q = linear(u, w_q).reshape(B, S, -1)
+    k = linear(u, w_k).reshape(B, S, -1)
+    v = linear(u, w_v).reshape(B, S, -1)
+    kc, vc = append_kv_block(k_cache, v_cache, k, v, kv_len, n_kv, d)
+    o = prefill_attention(q, kc, vc, kv_len, n_q, n_kv, d)
+    y = linear(o.reshape(B * S, -1), w_o).reshape(B, S, H)
+    return {"u": u, "q": q, "k": k, "v": v, "k_cache": kc, "v_cache": vc, "o": o, "y": y}
+
+
+def layer_prefill(x, w: Dict[str, np.ndarray], k_cache, v_cache, kv_len: int, n_q: int, n_kv: int, d: int,
+                  eps: float = 1e-5, residual: bool = True) -> Dict[str, np.ndarray]:
+    """The layer over a block of S new tokens per sequence, x [B, S, H]: attention block, then MLP block."""
+    x = f64(x)
+    B, S, H = x.shape
+    attn = attention_block_prefill(x, w["w_q"], w["w_k"], w["w_v"], w["w_o"], k_cache, v_cache, kv_len,
+                                   n_q, n_kv, d, w.get("gamma1"), eps)
+    h = x + attn["y"] if residual else attn["y"]
+    mlp = mlp_block(h.reshape(B * S, H), w["w_gate"], w["w_up"], w["w_down"], w.get("gamma2"), eps)
+    y = mlp["y"].reshape(B, S, H)
+    out = h + y if residual else y
+    return {"attn": attn, "h": h, "mlp": mlp, "out": out}
+
+
 def layer(x, w: Dict[str, np.ndarray], k_cache, v_cache, kv_len: int, n_q: int, n_kv: int, d: int,
           eps: float = 1e-5, residual: bool = True) -> Dict[str, np.ndarray]:
     """Attention block then MLP block.

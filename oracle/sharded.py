@@ -147,6 +147,50 @@ def rank_prefill_attention(q_rank, k_rank, v_rank, kv_len: int, n_q: int, n_kv: 
     return o.reshape(B, S, qn * d)
 
 
+def rank_attention_prefill(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len: int, n_q: int, n_kv: int,
+                           d: int, p: dict, gamma=None, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """One rank's attention stage for a block of S new tokens per sequence, x [B, S, H].
+
+    Owned q and kv heads of every token; the block's k, v go into this rank's
+    kv-head block of the (unsharded [B, n_kv, capacity, d]) caches at positions
+    kv_len - S .. kv_len - 1; causal attention on the owned heads; W_o row
+    partial [B, S, H].
+    """
+    x = _f(x)
+    B, S, H = x.shape
+    qb, qn = p["q_head_begin"], p["q_heads"]
+    kb, kn = p["kv_head_begin"], p["kv_heads"]
+    u = _norm(x.reshape(B * S, H), gamma, eps)
+    q = _mm(u, column_shard(w_q, qb * d, qn * d)).reshape(B, S, qn * d)
+    k = _mm(u, column_shard(w_k, kb * d, kn * d)).reshape(B, S, kn, d)
+    v = _mm(u, column_shard(w_v, kb * d, kn * d)).reshape(B, S, kn, d)
+    kc = _f(k_cache[:, kb:kb + kn]).copy()
+    vc = _f(v_cache[:, kb:kb + kn]).copy()
+    for i in range(S):
+        kc[:, :, kv_len - S + i] = k[:, i]
+        vc[:, :, kv_len - S + i] = v[:, i]
+    o = rank_prefill_attention(q, kc, vc, kv_len, n_q, n_kv, d, p).reshape(B * S, qn * d)
+    partial = _mm(o, row_shard(w_o, qb * d, qn * d)).reshape(B, S, H)
+    return {"q": q, "k_cache": kc, "v_cache": vc, "o": o, "partial": partial}
+
+
+def sharded_layer_prefill(x, w: Dict[str, Optional[np.ndarray]], k_cache, v_cache, kv_len: int, n_q: int,
+                          n_kv: int, d: int, t: int, eps: float = 1e-5, residual: bool = True) -> Dict[str, object]:
+    """All t ranks of the attention stage over a token block x [B, S, H], sum, then the MLP stage, sum."""
+    x = _f(x)
+    B, S, H = x.shape
+    I = np.shape(w["w_gate"])[1]
+    desc = _plan.ModelDesc(hidden=H, intermediate=I, n_q_heads=n_q, n_kv_heads=n_kv, head_dim=d)
+    plans = [_plan.rank_plan(desc, t, r) for r in range(t)]
+    attn = [rank_attention_prefill(x, w["w_q"], w["w_k"], w["w_v"], w["w_o"], k_cache, v_cache, kv_len,
+                                   n_q, n_kv, d, p, w.get("gamma1"), eps) for p in plans]
+    h = sum_partials([a["partial"] for a in attn], x if residual else None)
+    h2 = h.reshape(B * S, H)
+    mlp = [rank_mlp(h2, w["w_gate"], w["w_up"], w["w_down"], p, w.get("gamma2"), eps) for p in plans]
+    out = sum_partials([m["partial"] for m in mlp], h2 if residual else None).reshape(B, S, H)
+    return {"plans": plans, "attn": attn, "h": h, "mlp": mlp, "out": out}
+
+
 def sharded_layer(x, w: Dict[str, Optional[np.ndarray]], k_cache, v_cache, kv_len: int, n_q: int,
                   n_kv: int, d: int, t: int, eps: float = 1e-5, residual: bool = True) -> Dict[str, object]:
     """All t ranks of the attention stage, sum, then all t ranks of the MLP stage, sum."""

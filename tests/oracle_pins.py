@@ -388,3 +388,77 @@ def pin_layer_vs_naive(layer):
     assert np.array_equal(got["attn"]["v_cache"][:, :, keep], Vn[:, :, keep])
     # the input caches are left untouched
     assert np.array_equal(K, K0) and np.array_equal(V, V0)
+
+
+def small_prefill(seed=45, B=2, S=5, H=16, I=24, n_q=4, n_kv=2, d=4, cap=9):
+    """A token block x [B, S, H] and the weights and caches of a small layer."""
+    _, w, K, V = small_layer(seed=seed, B=B, H=H, I=I, n_q=n_q, n_kv=n_kv, d=d, cap=cap)
+    x = W.storage_round(W.normal(seed, W.Q_PREFILL, (B, S, H)), "f32")
+    return x, w, K, V
+
+
+def pin_layer_prefill_one_token(layer_prefill, layer):
+    """A block of one token per sequence is a decode step."""
+    x, w, K, V = small_prefill(S=1)
+    for kv_len in (1, 6, 9):
+        for residual in (True, False):
+            got = layer_prefill(x, w, K, V, kv_len, 4, 2, 4, 1e-5, residual)
+            ref = layer(x[:, 0], w, K, V, kv_len, 4, 2, 4, 1e-5, residual)
+            assert relerr(got["out"][:, 0], ref["out"]) < 1e-13, kv_len
+            assert relerr(got["attn"]["k_cache"], ref["attn"]["k_cache"]) < 1e-13
+            assert relerr(got["attn"]["v_cache"], ref["attn"]["v_cache"]) < 1e-13
+
+
+def pin_layer_prefill_chunks(layer_prefill):
+    """Prefilling a block in two chunks through the cache gives the block's result."""
+    x, w, K, V = small_prefill(S=6)
+    kv_len = 8
+    whole = layer_prefill(x, w, K, V, kv_len, 4, 2, 4, 1e-5, True)
+    for s1 in (1, 2, 5):
+        first = layer_prefill(x[:, :s1], w, K, V, kv_len - 6 + s1, 4, 2, 4, 1e-5, True)
+        second = layer_prefill(x[:, s1:], w, first["attn"]["k_cache"], first["attn"]["v_cache"], kv_len, 4, 2, 4,
+                               1e-5, True)
+        out = np.concatenate([first["out"], second["out"]], axis=1)
+        assert relerr(out, whole["out"]) < 1e-13, s1
+        assert relerr(second["attn"]["k_cache"], whole["attn"]["k_cache"]) < 1e-13
+
+
+def pin_layer_prefill_vs_naive(layer_prefill):
+    """The layer over a token block against brute-force loops, the block's KV append included."""
+    B, S, H, I, n_q, n_kv, d, cap, kv_len = 2, 3, 8, 12, 4, 2, 2, 6, 5
+    x, w, K, V = small_prefill(seed=47, B=B, S=S, H=H, I=I, n_q=n_q, n_kv=n_kv, d=d, cap=cap)
+    K0, V0 = K.copy(), V.copy()
+    got = layer_prefill(x, w, K, V, kv_len, n_q, n_kv, d, 1e-5, True)
+    rows = [x[b, i] for b in range(B) for i in range(S)]            # token rows, sequence-major
+    u = naive.rmsnorm(rows, w["gamma1"], 1e-5)
+    q = naive.matmul(u, w["w_q"]); k = naive.matmul(u, w["w_k"]); v = naive.matmul(u, w["w_v"])
+    Kn = K.astype(np.float64).copy(); Vn = V.astype(np.float64).copy()
+    for b in range(B):
+        for i in range(S):
+            for g in range(n_kv):
+                Kn[b, g, kv_len - S + i] = k[b * S + i][g * d:(g + 1) * d]
+                Vn[b, g, kv_len - S + i] = v[b * S + i][g * d:(g + 1) * d]
+    qb = [[q[b * S + i] for i in range(S)] for b in range(B)]
+    o = naive.prefill_attention(qb, Kn, Vn, kv_len, n_q, n_kv, d)
+    y = naive.matmul([o[b][i] for b in range(B) for i in range(S)], w["w_o"])
+    h = [[float(rows[r][j]) + y[r][j] for j in range(H)] for r in range(B * S)]
+    m = naive.mlp(h, w["w_gate"], w["w_up"], w["w_down"], w["gamma2"], 1e-5)
+    out = [[h[r][j] + m[r][j] for j in range(H)] for r in range(B * S)]
+    assert relerr(got["out"].reshape(B * S, H), out) < 1e-13
+    assert relerr(got["attn"]["k_cache"], Kn) < 1e-13
+    assert relerr(got["attn"]["v_cache"], Vn) < 1e-13
+    assert np.array_equal(K, K0) and np.array_equal(V, V0)
+
+
+def pin_sharded_layer_prefill(sharded_layer_prefill, layer_prefill):
+    for n_q, n_kv in [(8, 8), (16, 8)]:
+        x, w, K, V = small_prefill(seed=49, B=2, S=4, H=32, I=64, n_q=n_q, n_kv=n_kv, d=4, cap=10)
+        for residual in (True, False):
+            ref = layer_prefill(x, w, K, V, 7, n_q, n_kv, 4, 1e-5, residual)
+            for t in (1, 2, 4, 8):
+                s = sharded_layer_prefill(x, w, K, V, 7, n_q, n_kv, 4, t, 1e-5, residual)
+                assert relerr(s["out"], ref["out"]) < 1e-12, (n_q, t, residual)
+                assert relerr(s["h"], ref["h"]) < 1e-12
+                for a, p in zip(s["attn"], s["plans"]):
+                    kb, kn = p["kv_head_begin"], p["kv_heads"]
+                    assert relerr(a["k_cache"], ref["attn"]["k_cache"][:, kb:kb + kn]) < 1e-13

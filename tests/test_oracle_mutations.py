@@ -28,6 +28,13 @@ def _all_prefill_pins():
     P.pin_rank_prefill(S.rank_prefill_attention, L.prefill_attention, plan.rank_plan, plan.ModelDesc)
 
 
+def _all_layer_prefill_pins():
+    P.pin_layer_prefill_one_token(L.layer_prefill, L.layer)
+    P.pin_layer_prefill_chunks(L.layer_prefill)
+    P.pin_layer_prefill_vs_naive(L.layer_prefill)
+    P.pin_sharded_layer_prefill(S.sharded_layer_prefill, L.layer_prefill)
+
+
 def _all_sharded_pins():
     P.pin_silu(S._silu)
     P.pin_rmsnorm(lambda x, g, eps: S._norm(x, g, eps))
@@ -80,6 +87,37 @@ def _rank_prefill_global_kv(q, k, v, kv_len, n_q, n_kv, d, p):
     p2["kv_head_begin"] = 0
     return _orig_rank_prefill(q, k, v, kv_len, n_q, n_kv, d, p2) if p["kv_head_begin"] == 0 else \
         _orig_rank_prefill(q, np.roll(k, 1, axis=1), np.roll(v, 1, axis=1), kv_len, n_q, n_kv, d, p)
+
+
+_orig_append_block = L.append_kv_block
+_orig_rank_attention_prefill = S.rank_attention_prefill
+
+
+def _append_block_shifted(kc, vc, kn, vn, kv_len, n_kv, d):
+    # writes the block one position early (starting at kv_len - S - 1)
+    S_ = np.shape(kn)[1]
+    if kv_len - S_ - 1 < 0:
+        return _orig_append_block(kc, vc, kn, vn, kv_len, n_kv, d)
+    return _orig_append_block(kc, vc, kn, vn, kv_len - 1, n_kv, d)
+
+
+def _append_block_skipped(kc, vc, kn, vn, kv_len, n_kv, d):
+    # attends over the cache as it was, without the block's own keys and values
+    return np.asarray(kc, np.float64).copy(), np.asarray(vc, np.float64).copy()
+
+
+def _append_block_token_major(kc, vc, kn, vn, kv_len, n_kv, d):
+    # reads the block's k as [n_kv, S] instead of [S, n_kv] per sequence
+    B, S_ = np.shape(kn)[0], np.shape(kn)[1]
+    kc2 = np.asarray(kc, np.float64).copy()
+    vc2 = np.asarray(vc, np.float64).copy()
+    kc2[:, :, kv_len - S_:kv_len, :] = np.asarray(kn, np.float64).reshape(B, n_kv, S_, d)
+    vc2[:, :, kv_len - S_:kv_len, :] = np.asarray(vn, np.float64).reshape(B, n_kv, S_, d)
+    return kc2, vc2
+
+
+def _rank_attention_prefill_no_norm(x, w_q, w_k, w_v, w_o, kc, vc, kv_len, n_q, n_kv, d, p, gamma=None, eps=1e-5):
+    return _orig_rank_attention_prefill(x, w_q, w_k, w_v, w_o, kc, vc, kv_len, n_q, n_kv, d, p, None, eps)
 
 
 def _plan_shift_heads(desc, t, rank):
@@ -154,6 +192,11 @@ MUTATIONS = {
     "prefill_no_mask": (L, "prefill_attention", _prefill_no_mask, _all_prefill_pins),
     "prefill_positions_from_zero": (L, "prefill_attention", _prefill_positions_from_zero, _all_prefill_pins),
     "rank_prefill_wrong_kv_head": (S, "rank_prefill_attention", _rank_prefill_global_kv, _all_prefill_pins),
+    "prefill_block_append_shifted": (L, "append_kv_block", _append_block_shifted, _all_layer_prefill_pins),
+    "prefill_block_append_skipped": (L, "append_kv_block", _append_block_skipped, _all_layer_prefill_pins),
+    "prefill_block_append_transposed": (L, "append_kv_block", _append_block_token_major, _all_layer_prefill_pins),
+    "rank_attention_prefill_no_norm": (S, "rank_attention_prefill", _rank_attention_prefill_no_norm,
+                                       _all_layer_prefill_pins),
     # decomposition
     "sum_drops_last_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
         [np.asarray(p, float) for p in parts[:-1]] or [np.zeros_like(parts[0])], axis=0)

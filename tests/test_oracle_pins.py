@@ -83,3 +83,19 @@ def test_prefill_attention():
 
 def test_rank_prefill_attention():
     P.pin_rank_prefill(S.rank_prefill_attention, L.prefill_attention, plan.rank_plan, plan.ModelDesc)
+
+
+def test_layer_prefill_one_token():
+    P.pin_layer_prefill_one_token(L.layer_prefill, L.layer)
+
+
+def test_layer_prefill_chunks():
+    P.pin_layer_prefill_chunks(L.layer_prefill)
+
+
+def test_layer_prefill_vs_naive():
+    P.pin_layer_prefill_vs_naive(L.layer_prefill)
+
+
+def test_sharded_layer_prefill():
+    P.pin_sharded_layer_prefill(S.sharded_layer_prefill, L.layer_prefill)
