@@ -247,7 +247,9 @@ typedef struct tp_kv_view {
     void* k;
     void* v;
     int64_t capacity;
-    int64_t kv_len;          /* keys attended over, the new token included */
+    int64_t kv_len;          /* keys attended over, the new tokens included */
+    int64_t new_tokens;      /* new tokens per sequence: 0 or 1 for a decode step, S > 1 for a
+                                block of S tokens at positions kv_len - S .. kv_len - 1 */
 } tp_kv_view;
 
 /* Workspace bytes of tp_layer_shard_forward for this stage and m. */
@@ -260,10 +262,15 @@ size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* p
  * parallel scaling curves", section "What tensor parallelism actually
  * splits", pseudocode for the attention block and the two all-reduces per
  * layer).
- * TP_STAGE_ATTN (decode, bf16): u = RMSNorm(in; attn_norm); [q|k|v] =
- *   u @ W_qkv^T; the new k, v are written to the cache at position
- *   kv_len - 1; o = decode attention over the owned heads;
- *   partial = o @ W_o^T. m is the batch (one new token per sequence).
+ * TP_STAGE_ATTN (bf16): u = RMSNorm(in; attn_norm); [q|k|v] = u @ W_qkv^T.
+ *   Decode (kv->new_tokens 0 or 1; m is the batch, one new token per
+ *   sequence): the new k, v are written to the cache at position kv_len - 1
+ *   and o = decode attention over the owned heads. Prefill (new_tokens =
+ *   S > 1; m = batch * S rows, sequence-major): the block's k, v are written
+ *   to positions kv_len - S .. kv_len - 1 and o = causal prefill attention
+ *   over the owned heads (as tp_prefill_attention), with S <= kv_len and at
+ *   most 65535 sequences (TP_ERR_KV / TP_ERR_SHAPE). Then
+ *   partial = o @ W_o^T. A prefill block of one token is a decode step.
  * TP_STAGE_MLP (bf16 or float32, any m): u = RMSNorm(in; mlp_norm);
  *   a = silu(u @ W_gate^T) * (u @ W_up^T); partial = a @ W_down^T.
  * in       device [m, H] (dtype): x for ATTN; h = x + sum of attention

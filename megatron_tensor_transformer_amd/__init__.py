@@ -62,7 +62,7 @@ class tp_rank_weights(ctypes.Structure):
 
 class tp_kv_view(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int64),
-                ("kv_len", ctypes.c_int64)]
+                ("kv_len", ctypes.c_int64), ("new_tokens", ctypes.c_int64)]
 
 
 _P, _I64, _I32, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -243,14 +243,17 @@ def tp_layer_workspace_bytes(desc: tp_model_desc, plan: tp_rank_plan, stage: int
 def tp_layer_shard_forward(desc: tp_model_desc, plan: tp_rank_plan, stage: int, weights: Dict[str, torch.Tensor],
                            inp: torch.Tensor, partial: torch.Tensor, kv: Optional[Dict] = None,
                            ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One rank's ATTN or MLP block; ``kv`` = {"k", "v", "kv_len"} for ATTN."""
+    """One rank's ATTN or MLP block; ``kv`` = {"k", "v", "kv_len"[, "new_tokens"]} for ATTN.
+
+    inp [m, H]: m sequences of one new token, or with ``new_tokens`` = S > 1,
+    m / S sequences of S new tokens each, rows sequence-major."""
     m = inp.shape[0]
     dt = _dtype_code(inp)
     w = tp_rank_weights(*[_ptr(weights.get(n)) for n in
                           ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down")])
     kvv = None
     if kv is not None:
-        kvv = tp_kv_view(_ptr(kv["k"]), _ptr(kv["v"]), kv["k"].shape[2], kv["kv_len"])
+        kvv = tp_kv_view(_ptr(kv["k"]), _ptr(kv["v"]), kv["k"].shape[2], kv["kv_len"], kv.get("new_tokens", 1))
     if ws is None:
         ws = workspace(tp_layer_workspace_bytes(desc, plan, stage, m, dt), inp.device)
     wp, wn = _ws(ws)

@@ -210,10 +210,17 @@ struct LayerWs {
     size_t act1, act2, lin, attn, total;
 };
 
-LayerWs layer_ws(const tp_model_desc* d, const tp_rank_plan* p, tp_stage stage, int64_t m, tp_dtype dt) {
+LayerWs layer_ws(const tp_model_desc* d, const tp_rank_plan* p, tp_stage stage, int64_t m, tp_dtype dt,
+                 bool prefill) {
     LayerWs w{};
     const int64_t H = d->hidden;
-    if (stage == TP_STAGE_ATTN) {
+    if (stage == TP_STAGE_ATTN && prefill) {
+        w.act1 = round256((size_t)m * p->qkv_cols * 2);  // [q | k | v] of every token
+        w.act2 = round256((size_t)m * p->o_rows * 2);    // attention output
+        const size_t l1 = linear_scratch(m, H, p->qkv_cols, dt, tpk::EPI_STORE, true);
+        const size_t l2 = linear_scratch(m, p->o_rows, H, dt, tpk::EPI_PARTIAL, false);
+        w.lin = l1 > l2 ? l1 : l2;
+    } else if (stage == TP_STAGE_ATTN) {
         w.act1 = round256((size_t)m * p->o_rows * 2);   // q
         w.act2 = round256((size_t)m * p->o_rows * 2);   // attention output
         const size_t l1 = linear_scratch(m, H, p->qkv_cols, dt, tpk::EPI_QKV, true);
@@ -425,7 +432,7 @@ tp_status tp_prefill_attention(const void* q, const void* k, const void* v, void
         return fail(TP_ERR_ALIAS, "out overlaps q or the caches");
     tpk::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.out = out;
-    a.capacity = capacity; a.kv_len = (int)kv_len;
+    a.capacity = capacity; a.q_stride = (int64_t)q_heads * head_dim; a.kv_len = (int)kv_len;
     a.batch = (int)batch; a.seq = (int)seq; a.q_heads = q_heads; a.kv_heads = kv_heads; a.head_dim = head_dim;
     hipError_t e = tpk::prefill_attn_launch(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
@@ -438,7 +445,12 @@ size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* p
     if (dtype != TP_F32 && dtype != TP_BF16) return 0;
     if (stage == TP_STAGE_ATTN && (plan->q_heads < 1 || desc->seq_len < 1)) return 0;
     if (stage == TP_STAGE_MLP && plan->inter_cols < 1) return 0;
-    return layer_ws(desc, plan, stage, m, dtype).total;
+    // m rows serve either m sequences of one new token or a block of tokens;
+    // the larger of the two layouts covers both.
+    const size_t dec = layer_ws(desc, plan, stage, m, dtype, false).total;
+    if (stage != TP_STAGE_ATTN) return dec;
+    const size_t pre = layer_ws(desc, plan, stage, m, dtype, true).total;
+    return dec > pre ? dec : pre;
 }
 
 tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
@@ -473,14 +485,23 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
             return fail(TP_ERR_SHAPE, "q heads per kv head = %d must be 1, 2, 4, 8 or 16", gq);
         if (desc->head_dim != 64 && desc->head_dim != 128)
             return fail(TP_ERR_SHAPE, "head_dim=%d must be 64 or 128", desc->head_dim);
-        if (m > (1 << 20)) return fail(TP_ERR_SHAPE, "batch m=%lld too large", (long long)m);
+        if (m > (1 << 20)) return fail(TP_ERR_SHAPE, "m=%lld too large", (long long)m);
         if (kv->capacity < 1 || kv->capacity > (int64_t(1) << 24))
             return fail(TP_ERR_SHAPE, "kv capacity outside 1..2^24");
         if (kv->kv_len < 1 || kv->kv_len > kv->capacity)
             return fail(TP_ERR_KV, "kv_len=%lld outside 1..capacity=%lld", (long long)kv->kv_len,
                         (long long)kv->capacity);
+        if (kv->new_tokens < 0) return fail(TP_ERR_SHAPE, "kv->new_tokens=%lld is negative", (long long)kv->new_tokens);
+        const int64_t S = kv->new_tokens > 1 ? kv->new_tokens : 1;   // new tokens per sequence
+        if (m % S)
+            return fail(TP_ERR_SHAPE, "m=%lld rows are not a whole number of %lld-token blocks", (long long)m,
+                        (long long)S);
+        if (S > kv->kv_len)
+            return fail(TP_ERR_KV, "new_tokens=%lld exceeds kv_len=%lld", (long long)S, (long long)kv->kv_len);
+        const int64_t B = m / S;                                     // sequences
+        if (S > 1 && B > 65535) return fail(TP_ERR_SHAPE, "%lld sequences exceed 65535", (long long)B);
         {
-            const size_t nc = (size_t)m * plan->kv_heads * kv->capacity * desc->head_dim * 2;
+            const size_t nc = (size_t)B * plan->kv_heads * kv->capacity * desc->head_dim * 2;
             if (overlaps(kv->k, nc, kv->v, nc)) return fail(TP_ERR_ALIAS, "kv->k overlaps kv->v");
             if (overlaps(kv->k, nc, in, (size_t)m * H * 2) || overlaps(kv->v, nc, in, (size_t)m * H * 2) ||
                 overlaps(kv->k, nc, partial, (size_t)m * H * 4) || overlaps(kv->v, nc, partial, (size_t)m * H * 4))
@@ -489,14 +510,37 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         if (kv->capacity != desc->seq_len)
             return fail(TP_ERR_KV, "kv capacity %lld differs from desc seq_len %lld", (long long)kv->capacity,
                         (long long)desc->seq_len);
-        const LayerWs L = layer_ws(desc, plan, stage, m, dtype);
+        const LayerWs L = layer_ws(desc, plan, stage, m, dtype, S > 1);
         TRY(check_ws(ws, ws_bytes, L.total));
         char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
         unsigned* cnt = ws_counters(ws);
-        void* qbuf = b;
+        void* act1 = b;
         void* obuf = b + L.act1;
         void* lin = b + L.act1 + L.act2;
         void* aws = b + L.act1 + L.act2 + L.lin;
+        if (S > 1) {
+            // A block of S tokens per sequence: [q | k | v] of every token, the
+            // block's k, v into the cache, causal attention reading q from the
+            // projected rows, W_o partial.
+            TRY(run_linear(in, wts->w_qkv, nullptr, wts->attn_norm, desc->eps, act1, m, H, plan->qkv_cols, dtype,
+                           tpk::EPI_STORE, cnt, lin, s));
+            tpk::KvAppendArgs ka{};
+            ka.qkv = act1; ka.k_cache = kv->k; ka.v_cache = kv->v; ka.capacity = kv->capacity;
+            ka.row_stride = plan->qkv_cols; ka.rows = (int)m; ka.seq = (int)S; ka.kv_heads = plan->kv_heads;
+            ka.head_dim = desc->head_dim; ka.pos0 = (int)(kv->kv_len - S);
+            ka.k_col0 = (int)plan->o_rows; ka.v_col0 = (int)(plan->o_rows + plan->kv_heads * desc->head_dim);
+            hipError_t e = tpk::kv_append_launch(ka, s);
+            if (e != hipSuccess) return hip_fail(e, "KV append launch");
+            tpk::PrefillArgs pa{};
+            pa.q = act1; pa.k = kv->k; pa.v = kv->v; pa.out = obuf;
+            pa.capacity = kv->capacity; pa.q_stride = plan->qkv_cols; pa.kv_len = (int)kv->kv_len;
+            pa.batch = (int)B; pa.seq = (int)S; pa.q_heads = plan->q_heads; pa.kv_heads = plan->kv_heads;
+            pa.head_dim = desc->head_dim;
+            e = tpk::prefill_attn_launch(pa, s);
+            if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+            return run_linear(obuf, wts->w_o, nullptr, nullptr, 0.f, partial, m, plan->o_rows, H, dtype,
+                              tpk::EPI_PARTIAL, cnt, lin, s);
+        }
         tpk::GemvArgs extra{};
         extra.k_cache = kv->k;
         extra.v_cache = kv->v;
@@ -506,10 +550,10 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         extra.kv_cols = plan->kv_heads * desc->head_dim;
         extra.head_dim = desc->head_dim;
         extra.kv_heads = plan->kv_heads;
-        TRY(run_linear(in, wts->w_qkv, nullptr, wts->attn_norm, desc->eps, qbuf, m, H, plan->qkv_cols, dtype,
+        TRY(run_linear(in, wts->w_qkv, nullptr, wts->attn_norm, desc->eps, act1, m, H, plan->qkv_cols, dtype,
                        tpk::EPI_QKV, cnt, lin, s, &extra));
         tpk::AttnArgs a{};
-        a.q = qbuf; a.k = kv->k; a.v = kv->v; a.out = obuf;
+        a.q = act1; a.k = kv->k; a.v = kv->v; a.out = obuf;
         a.capacity = kv->capacity; a.kv_len = (int)kv->kv_len;
         a.batch = (int)m; a.q_heads = plan->q_heads; a.kv_heads = plan->kv_heads; a.head_dim = desc->head_dim;
         const tpk::AttnPlan ap_len = tpk::attn_plan(a.batch, a.q_heads, a.kv_heads, a.head_dim, a.kv_len);
@@ -527,7 +571,7 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
     if (wts->mlp_norm) TRY(check_ptr(wts->mlp_norm, "weights->mlp_norm"));
     if (plan->inter_cols % (int64_t)vec_elems(dtype))
         return fail(TP_ERR_ALIGN, "inter_cols=%lld not a multiple of %zu", (long long)plan->inter_cols, vec_elems(dtype));
-    const LayerWs L = layer_ws(desc, plan, stage, m, dtype);
+    const LayerWs L = layer_ws(desc, plan, stage, m, dtype, false);
     TRY(check_ws(ws, ws_bytes, L.total));
     char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
     unsigned* cnt = ws_counters(ws);

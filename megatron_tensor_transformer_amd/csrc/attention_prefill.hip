@@ -223,7 +223,7 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
             tok[rt] = i0 + r / GQ;
             pos[rt] = p0 + tok[rt];
             const int hq = g * GQ + r % GQ;
-            const uint16_t* qrow = qbase + (((size_t)b * S + min(tok[rt], S - 1)) * a.q_heads + hq) * D;
+            const uint16_t* qrow = qbase + ((size_t)b * S + min(tok[rt], S - 1)) * a.q_stride + (size_t)hq * D;
 #pragma unroll
             for (int s = 0; s < DS; ++s) qf[rt][s] = load_u4(qrow + s * 32 + kg * 8);
         }

@@ -1,6 +1,7 @@
 // Bandwidth-bound elementwise kernels: the on-device sum of the t row-parallel
-// partials (the value the all-reduce returns), standalone SwiGLU, and the
-// row-wise RMSNorm used in front of the prefill GEMM. All use 128-bit loads
+// partials (the value the all-reduce returns), standalone SwiGLU, the
+// row-wise RMSNorm used in front of the prefill GEMM, and the append of a
+// block of tokens' k, v to the cache. All use 128-bit loads
 // and grid-stride loops sized to a few workgroups per compute unit.
 #include "device_common.h"
 #include "kernels.h"
@@ -178,6 +179,37 @@ hipError_t rmsnorm_launch(const void* x, const void* gamma, void* u, int m, int 
         hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3(m), dim3(EW_THREADS), 0, s, x, gamma, u, K, eps);
     else
         hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3(m), dim3(EW_THREADS), 0, s, x, gamma, u, K, eps);
+    return hipGetLastError();
+}
+
+// Block KV append: the k and v columns of each token row of the projected
+// [q | k | v] buffer go to cache positions pos0 .. pos0 + S - 1. A thread moves
+// one 16-byte chunk of k and the matching chunk of v; consecutive threads
+// take consecutive chunks of one row, so reads and writes are contiguous runs
+// of a head's d elements.
+__global__ __launch_bounds__(EW_THREADS) void kv_append_kernel(KvAppendArgs a) {
+    const int dc = a.head_dim / 8;                 // chunks per head
+    const int per_row = a.kv_heads * dc;
+    const int64_t total = (int64_t)a.rows * per_row;
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.qkv);
+    for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < total; i += stride) {
+        const int64_t r = i / per_row;             // token row, sequence-major
+        const int c = (int)(i - r * per_row);
+        const int g = c / dc, off = (c - g * dc) * 8;
+        const int64_t b = r / a.seq, t = r - b * a.seq;
+        const uint16_t* row = src + r * a.row_stride + g * a.head_dim + off;
+        const size_t dst = (((size_t)b * a.kv_heads + g) * a.capacity + a.pos0 + t) * a.head_dim + off;
+        const uint4 k = load_u4(row + a.k_col0);
+        const uint4 v = load_u4(row + a.v_col0);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.k_cache) + dst) = k;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.v_cache) + dst) = v;
+    }
+}
+
+hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t s) {
+    const int blocks = ew_blocks((int64_t)a.rows * a.kv_heads * (a.head_dim / 8));
+    hipLaunchKernelGGL(kv_append_kernel, dim3(blocks), dim3(EW_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -107,13 +107,27 @@ struct GemmArgs {
 bool gemm_supported(int M, int N, int K, int epi);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
 
+// Block KV append: k, v columns of rows [batch * seq] of a [q | k | v] buffer
+// (row_stride elements per row) to cache positions pos0 .. pos0 + seq - 1 (bf16).
+struct KvAppendArgs {
+    const void* qkv;
+    void* k_cache;      // [batch, kv_heads, capacity, d]
+    void* v_cache;
+    int64_t capacity;
+    int64_t row_stride;
+    int rows, seq, kv_heads, head_dim;
+    int pos0, k_col0, v_col0;
+};
+hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t stream);
+
 // Causal grouped-query attention over a block of seq new tokens (bf16).
 struct PrefillArgs {
-    const void* q;      // [batch, seq, q_heads * d]
+    const void* q;      // [batch, seq] rows of q_stride elements; a row holds q_heads * d
     const void* k;      // [batch, kv_heads, capacity, d]
     const void* v;
     void* out;          // [batch, seq, q_heads * d]
     int64_t capacity;
+    int64_t q_stride;   // elements between consecutive tokens' q rows
     int kv_len;         // token i of the block sits at position kv_len - seq + i
     int batch, seq, q_heads, kv_heads, head_dim;
 };

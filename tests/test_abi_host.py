@@ -219,7 +219,7 @@ def test_layer_validation():
     d = tp.make_desc(8192, 28672, 64, 8, 128, seq_len=8192, batch=16)
     p = tp.tp_shard_plan(d, 8, 3)
     w = tp.tp_rank_weights(*[A + i * 256 * MB for i in range(7)])
-    kv = tp.tp_kv_view(A + 4096 * MB, A + 5120 * MB, 8192, 8192)
+    kv = tp.tp_kv_view(A + 4096 * MB, A + 5120 * MB, 8192, 8192, 1)
 
     def f(stage=tp.TP_STAGE_MLP, plan=p, weights=w, inp=A + 3000 * MB, kvv=kv, part=A + 3100 * MB, m=16,
           dt=tp.TP_BF16, ws=None, wsn=0):
@@ -233,7 +233,11 @@ def test_layer_validation():
     assert f(weights=None) == "TP_ERR_NULL"
     assert f(stage=tp.TP_STAGE_ATTN, kvv=None) == "TP_ERR_NULL"
     assert f(stage=tp.TP_STAGE_ATTN, dt=tp.TP_F32) == "TP_ERR_DTYPE"
-    assert f(stage=tp.TP_STAGE_ATTN, kvv=tp.tp_kv_view(A + 4096 * MB, A + 5120 * MB, 8192, 0)) == "TP_ERR_KV"
+    assert f(stage=tp.TP_STAGE_ATTN, kvv=tp.tp_kv_view(A + 4096 * MB, A + 5120 * MB, 8192, 0, 1)) == "TP_ERR_KV"
+    kvp = lambda kv_len, new: tp.tp_kv_view(A + 4096 * MB, A + 5120 * MB, 8192, kv_len, new)
+    assert f(stage=tp.TP_STAGE_ATTN, kvv=kvp(8192, -1)) == "TP_ERR_SHAPE"     # negative block
+    assert f(stage=tp.TP_STAGE_ATTN, kvv=kvp(8192, 3)) == "TP_ERR_SHAPE"      # 16 rows are not 3-token blocks
+    assert f(stage=tp.TP_STAGE_ATTN, kvv=kvp(7, 8)) == "TP_ERR_KV"            # block longer than kv_len
     assert f(inp=None) == "TP_ERR_NULL"
     assert f(part=A + 3000 * MB + 64) == "TP_ERR_ALIAS"
     assert f(ws=None) in ("TP_ERR_WORKSPACE",)
@@ -242,6 +246,11 @@ def test_layer_validation():
     need_mlp = tp.tp_layer_workspace_bytes(d, p, tp.TP_STAGE_MLP, 16, tp.TP_BF16)
     assert need_attn > 16 * 1024 * 2 * 2 and need_mlp > 16 * 3584 * 2
     assert f(ws=A + 6000 * MB, wsn=need_mlp - 1) == "TP_ERR_WORKSPACE"
+    # m rows of a 2048-token block: the [q | k | v] rows and the attention output fit the workspace
+    need_pre = tp.tp_layer_workspace_bytes(d, p, tp.TP_STAGE_ATTN, 4096, tp.TP_BF16)
+    assert need_pre >= 4096 * (p.qkv_cols + p.o_rows) * 2
+    assert f(stage=tp.TP_STAGE_ATTN, kvv=kvp(8192, 2048), m=4096, ws=A + 6000 * MB,
+             wsn=4096 * p.qkv_cols * 2) == "TP_ERR_WORKSPACE"
 
 
 def test_workspace_sizes_are_zero_for_bad_args():

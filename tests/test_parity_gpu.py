@@ -248,6 +248,76 @@ def test_full_layer_decode_bf16():
     check("layer output", host(out), ref["out"], TOL["bf16"])
 
 
+PREFILL_LAYER_CASES = [
+    # hidden, intermediate, q heads, kv heads, head_dim, t, sequences, new tokens, kv_len, capacity
+    (512, 1024, 8, 2, 64, 2, 2, 4, 9, 16),           # 8 rows: the projections take the GEMV path
+    (1024, 2816, 16, 4, 64, 4, 2, 96, 130, 160),     # MFMA GEMMs, a chunk after a cached prefix
+    (1024, 2048, 64, 8, 128, 8, 2, 200, 200, 256),   # 70B heads at t=8 (8 q heads on 1 kv head), a prompt
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", PREFILL_LAYER_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_full_layer_prefill_bf16(case):
+    """All t rank shards of both stages over a block of new tokens, summed on device, against the oracle."""
+    H, I, nq, nkv, d, t, B, S_, kv_len, cap = case
+    seed = 60 + t
+    a = W.attention_inputs(seed, H, nq, nkv, d, B, cap, "bf16", "random")
+    mi = W.mlp_inputs(seed, H, I, 1, "bf16", "random")
+    x = W.to_bf16(W.normal(seed, W.Q_PREFILL, (B, S_, H)))
+    w = {"gamma1": a["gamma"], "w_q": a["w_q"], "w_k": a["w_k"], "w_v": a["w_v"], "w_o": a["w_o"],
+         "gamma2": mi["gamma"], "w_gate": mi["w_gate"], "w_up": mi["w_up"], "w_down": mi["w_down"]}
+    desc = tp.make_desc(H, I, nq, nkv, d, n_layers=1, seq_len=cap, batch=B)
+    M = B * S_
+    xd = dev(x.reshape(M, H), "bf16")
+    g1, g2 = dev(a["gamma"], "bf16"), dev(mi["gamma"], "bf16")
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    rank_w, caches, attn_parts = [], [], []
+    for p in plans:
+        kb, kn = p.kv_head_begin, p.kv_heads
+        rw = {"attn_norm": g1, "w_qkv": dev(qkv_rank_phys(a, p, d), "bf16"),
+              "w_o": dev(phys(a["w_o"][p.q_head_begin * d:(p.q_head_begin + p.q_heads) * d, :]), "bf16"),
+              "mlp_norm": g2}
+        rw["w_gate"], rw["w_up"], rw["w_down"] = [dev(q, "bf16") for q in mlp_rank_phys(mi, p)]
+        kc = dev(a["k_cache"][:, kb:kb + kn], "bf16")
+        vc = dev(a["v_cache"][:, kb:kb + kn], "bf16")
+        part = empty((M, H), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_ATTN, rw, xd, part,
+                                  kv={"k": kc, "v": vc, "kv_len": kv_len, "new_tokens": S_})
+        rank_w.append(rw)
+        caches.append((kc, vc))
+        attn_parts.append(part)
+    h = empty((M, H), torch.bfloat16)
+    tp.tp_partial_sum(attn_parts, h, residual=xd)
+    mlp_parts = []
+    for p, rw in zip(plans, rank_w):
+        part = empty((M, H), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, rw, h, part)
+        mlp_parts.append(part)
+    out = empty((M, H), torch.bfloat16)
+    tp.tp_partial_sum(mlp_parts, out, residual=h)
+    torch.cuda.synchronize()
+
+    ref = L.layer_prefill(x, w, a["k_cache"], a["v_cache"], kv_len, nq, nkv, d)
+    blk = slice(kv_len - S_, kv_len)
+    for r, p in enumerate(plans):
+        kb, kn = p.kv_head_begin, p.kv_heads
+        kc, vc = caches[r]
+        check(f"rank{r} appended k block", host(kc)[:, :, blk], ref["attn"]["k_cache"][:, kb:kb + kn, blk],
+              TOL["bf16"])
+        check(f"rank{r} appended v block", host(vc)[:, :, blk], ref["attn"]["v_cache"][:, kb:kb + kn, blk],
+              TOL["bf16"])
+        keep = [j for j in range(cap) if not kv_len - S_ <= j < kv_len]
+        assert np.array_equal(host(kc)[:, :, keep], W.to_bf16(a["k_cache"][:, kb:kb + kn][:, :, keep]))
+    sr = S.rank_attention_prefill(x, a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], kv_len,
+                                  nq, nkv, d, tp.plan_dict(plans[-1]), a["gamma"])
+    check("last rank attention partial", host(attn_parts[-1]), sr["partial"].reshape(M, H), TOL["bf16"])
+    check(f"h = x + sum of {t} attention partials", host(h), ref["h"].reshape(M, H), TOL["bf16"])
+    mref = L.mlp_block(host(h), w["w_gate"], w["w_up"], w["w_down"], w["gamma2"])
+    check(f"sum of {t} MLP partials at the GPU's h", sum(host(q) for q in mlp_parts), mref["y"], TOL["bf16"])
+    check("layer output", host(out), ref["out"].reshape(M, H), TOL["bf16"])
+
+
 # ---------------------------------------------------------------- ragged and edge shapes
 
 LINEAR_CASES = [
