@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mlp_decode",
-                    choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill"])
+                    choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill",
+                             "layer_prefill"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of the timed step (default: the workload's)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true")
@@ -101,7 +102,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
     bench = {"mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
-             "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill}[args.workload]
+             "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill,
+             "layer_prefill": bench_layer_prefill}[args.workload]
     if args.calibrate_copy:
         calibrate_copy(torch)
     res = bench(ctx)
@@ -714,6 +716,105 @@ def bench_attn_prefill(ctx):
                                "kind": "oracle",
                                "sample": f"{n} float64 passes of rank 0's shard over the last {n_tail} tokens of "
                                          f"sequence 0 (each sees about {kv_len} keys), {el:.1f} s"}
+    return res
+
+
+
+def bench_layer_prefill(ctx):
+    torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
+    wl = W.WORKLOADS[7]
+    H, I, nq, nkv, d, t, kv_len = wl.hidden, wl.intermediate, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t, \
+        wl.kv_len
+    M = args.tokens or wl.tokens[0]
+    B = 2
+    S_ = M // B
+    log(f"[bench] drawing {wl.name}")
+    a = W.attention_inputs(7, H, nq, nkv, d, B, kv_len, "bf16", "random", with_cache=True)
+    mi = W.mlp_inputs(7, H, I, 1, "bf16", "random")
+    x_host = W.to_bf16(W.normal(7, W.Q_PREFILL, (B, S_, H)))
+    desc = tp.make_desc(H, I, nq, nkv, d, n_layers=1, seq_len=kv_len, batch=B, eps=wl.eps)
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    g1, g2 = ctx.dev(a["gamma"]), ctx.dev(mi["gamma"])
+    ranks = []
+    for p in plans:
+        qs = slice(p.q_head_begin * d, (p.q_head_begin + p.q_heads) * d)
+        b0, n = p.inter_begin, p.inter_cols
+        kb, kn = p.kv_head_begin, p.kv_heads
+        ranks.append({"attn_norm": g1, "w_qkv": ctx.dev(qkv_rank_phys(a, p, d)),
+                      "w_o": ctx.dev(ctx.phys(a["w_o"][qs, :])), "mlp_norm": g2,
+                      "w_gate": ctx.dev(ctx.phys(mi["w_gate"][:, b0:b0 + n])),
+                      "w_up": ctx.dev(ctx.phys(mi["w_up"][:, b0:b0 + n])),
+                      "w_down": ctx.dev(ctx.phys(mi["w_down"][b0:b0 + n])),
+                      "k": ctx.dev(a["k_cache"][:, kb:kb + kn]), "v": ctx.dev(a["v_cache"][:, kb:kb + kn])})
+    x = ctx.dev(x_host.reshape(M, H))
+    ws = tp.workspace(max(max(tp.tp_layer_workspace_bytes(desc, p, tp.TP_STAGE_ATTN, M, tp.TP_BF16),
+                              tp.tp_layer_workspace_bytes(desc, p, tp.TP_STAGE_MLP, M, tp.TP_BF16)) for p in plans))
+    parts = [torch.empty(M, H, device="cuda") for _ in range(t)]
+    h = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    p0 = plans[0]
+    a_out = torch.empty(M, p0.inter_cols, dtype=torch.bfloat16, device="cuda")
+    hn = torch.empty(M, H, dtype=torch.bfloat16, device="cuda").normal_()
+
+    def step(i):
+        for r, p in enumerate(plans):
+            rw = ranks[r]
+            tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_ATTN, rw, x, parts[r],
+                                      kv={"k": rw["k"], "v": rw["v"], "kv_len": kv_len, "new_tokens": S_}, ws=ws)
+        tp.tp_partial_sum(parts, h, residual=x)
+        for r, p in enumerate(plans):
+            tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], h, parts[r], ws=ws)
+        tp.tp_partial_sum(parts, out, residual=h)
+
+    def gateup(i):
+        rw = ranks[i % t]
+        tp.tp_column_linear(hn, rw["w_gate"], a_out, w_up=rw["w_up"], ws=ws)
+
+    for i in range(2 * t):
+        gateup(i)
+    g_t = event_time_ms(torch, gateup, 2 * t, reps=3)
+    g_fl = 2.0 * M * H * 2 * p0.inter_cols
+    g_tf = g_fl / (g_t[0] * 1e-3) / 1e12
+    log(f"[bench] gate/up GEMM {g_t[0] * 1e3:.1f} us ({g_tf:.0f} TFLOP/s)")
+    total_ms = time_steps(ctx, step, 1)
+    ms_step = total_ms / args.steps
+    rank_fl = (2.0 * M * H * p0.qkv_cols + causal_flops(B, S_, kv_len, p0.q_heads, d) + 2.0 * M * p0.o_rows * H
+               + 2.0 * M * H * 3 * p0.inter_cols)
+    tflops = t * rank_fl * args.steps / (total_ms * 1e-3) / 1e12
+    extra = {
+        "tokens_per_s": M * args.steps / (total_ms * 1e-3),
+        "pct_mfma_peak": 100 * tflops / BF16_PEAK_TFLOPS,
+        "per_rank": {"flops": rank_fl, "step_us_per_rank": ms_step * 1e3 / t, "gateup_us": g_t[0] * 1e3},
+        "roofline": {"kernel": projection_kernel(M) + ": MLP gate/up + SwiGLU, one rank shard", "bound": "mfma",
+                     "achieved": g_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": g_tf / BF16_PEAK_TFLOPS,
+                     "traffic": counted_traffic(f"gateup_layer_prefill_m{M}"), "flops_per_launch": g_fl,
+                     "us_mean": g_t[0] * 1e3, "us_median": g_t[1] * 1e3, "us_min": g_t[2] * 1e3},
+    }
+    config = {"workload": f"70B-shaped full layer prefill, all t={t} rank shards (attention and MLP stages) + "
+                          f"on-device sums with residual", "hidden": H, "intermediate": I, "q_heads": nq,
+              "kv_heads": nkv, "head_dim": d, "t": t, "batch": B, "new_tokens": S_, "kv_len": kv_len}
+    res = result(ctx, tflops, "TFLOP/s", ms_step, config, extra)
+    if not args.no_cpu:
+        from oracle import sharded as S
+        pd = tp.plan_dict(p0)
+        n_tail = 16
+        xs = x_host[:1, S_ - n_tail:]
+        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
+
+        def one_rank():
+            at = S.rank_attention_prefill(xs, a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"][:1],
+                                          a["v_cache"][:1], kv_len, nq, nkv, d, pd, a["gamma"], wl.eps)
+            S.rank_mlp(xs.reshape(n_tail, H) + at["partial"].reshape(n_tail, H), mi["w_gate"], mi["w_up"],
+                       mi["w_down"], pd, mi["gamma"], wl.eps)
+
+        n, el = repeat_for(args.cpu_seconds, one_rank)
+        sfl = (2.0 * n_tail * H * p0.qkv_cols + causal_flops(1, n_tail, kv_len, p0.q_heads, d)
+               + 2.0 * n_tail * p0.o_rows * H + 2.0 * n_tail * H * 3 * p0.inter_cols)
+        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} float64 passes of rank 0's shard (attention and MLP stages) over "
+                                         f"the last {n_tail} tokens of sequence 0 (each sees about {kv_len} keys), "
+                                         f"{el:.1f} s"}
     return res
 
 

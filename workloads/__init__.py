@@ -110,6 +110,9 @@ WORKLOADS: Dict[int, Workload] = {
     6: Workload(6, "70B-shaped causal prefill attention shard, bf16, t=8, batch 2 x 2048 tokens",
                 "bf16", hidden=8192, intermediate=0, t=8, tokens=(4096,), n_q_heads=64, n_kv_heads=8,
                 head_dim=128, kv_len=2048),
+    7: Workload(7, "70B-shaped full layer prefill shard, bf16, t=8, batch 2 x 2048 tokens",
+                "bf16", hidden=8192, intermediate=28672, t=8, tokens=(4096,), n_q_heads=64, n_kv_heads=8,
+                head_dim=128, kv_len=2048, norm=True),
 }
 
 
