@@ -365,6 +365,21 @@ def bench_mlp_decode(ctx):
 
     total_ms = time_steps(ctx, step, copies_n)
     ms_step = total_ms / args.steps
+
+    # The same step with bf16 row partials and their float32 sum (half the
+    # bytes an all-reduce would move); the headline stays on float32 partials.
+    a_bufs = [torch.empty(M, I_r, dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+    parts_b = [torch.empty(M, H, dtype=torch.bfloat16, device="cuda") for _ in range(t)]
+
+    def step_bf16(i):
+        ranks = copies[i % copies_n]
+        for r in range(t):
+            rw = ranks[r]
+            tp.tp_column_linear(x, rw["w_gate"], a_bufs[r], w_up=rw["w_up"], gamma=gam, eps=wl.eps, ws=ws)
+            tp.tp_row_linear_partial_bf16(a_bufs[r], rw["w_down"], parts_b[r], ws=ws)
+        tp.tp_partial_sum_bf16(parts_b, out)
+
+    total_b = time_steps(ctx, step_bf16, copies_n)
     hb = per_batch[M]
     k_mean, k_med, k_min = hb.pop("_times")
     for v in per_batch.values():
@@ -372,6 +387,8 @@ def bench_mlp_decode(ctx):
     extra = {
         "step_GBps": t * hb["shard_bytes"] / (ms_step * 1e-3) / 1e9,
         "per_rank_shard": {str(m): v for m, v in per_batch.items()},
+        "bf16_partials": {"ms_per_step": total_b / args.steps, "tokens_per_s": M * args.steps / (total_b * 1e-3),
+                          "partial_bytes_per_rank": M * H * 2},
         "roofline": roofline_hbm(projection_kernel(M) + ": fused RMSNorm + gate/up + SwiGLU, one rank shard",
                                  f"gateup_mlp_decode_m{M}", hb["gateup_bytes"], k_mean, k_med, k_min),
     }

@@ -186,6 +186,24 @@ tp_status tp_row_linear_partial(const void* a, const void* w, float* partial, in
 tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* residual, void* out,
                          int64_t m, int64_t n, tp_dtype out_dtype, void* stream);
 
+/*
+ * bf16 partials. The partial sums a row-parallel projection emits are what
+ * the all-reduce moves ("Tensor parallel scaling curves", section "What
+ * tensor parallelism actually splits"; the bandwidth term of "The scaling
+ * math" is proportional to the message bytes). Emitting them in bf16 halves
+ * that message; the sum still adds in float32.
+ *
+ * tp_row_linear_partial_bf16 - as tp_row_linear_partial with bf16 a, w and
+ *   partial: partial = bf16(a @ w^T). ws: tp_linear_workspace_bytes(m, k, n,
+ *   TP_BF16, 0). k must be a multiple of 8 (TP_ERR_ALIGN).
+ * tp_partial_sum_bf16 - as tp_partial_sum over t bf16 partials:
+ *   out = sum_r float32(partials[r]) (+ residual), in rank order.
+ */
+tp_status tp_row_linear_partial_bf16(const void* a, const void* w, void* partial, int64_t m, int64_t k,
+                                     int64_t n, void* ws, size_t ws_bytes, void* stream);
+tp_status tp_partial_sum_bf16(const void* const* partials, int32_t t, const void* residual, void* out,
+                              int64_t m, int64_t n, tp_dtype out_dtype, void* stream);
+
 /* Workspace bytes of tp_decode_attention. */
 size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                     int64_t kv_len);

@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtpshard.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m megatron_tensor_transformer_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python megatron_tensor_transformer_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -35,7 +35,8 @@ STATUS = ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_
           "TP_ERR_ALIGN", "TP_ERR_WORKSPACE", "TP_ERR_KV", "TP_ERR_ALIAS", "TP_ERR_HIP"]
 
 EXPORTS = ["tp_shard_plan", "tp_linear_workspace_bytes", "tp_column_linear", "tp_swiglu",
-           "tp_row_linear_partial", "tp_partial_sum", "tp_attention_workspace_bytes", "tp_decode_attention",
+           "tp_row_linear_partial", "tp_partial_sum", "tp_row_linear_partial_bf16", "tp_partial_sum_bf16",
+           "tp_attention_workspace_bytes", "tp_decode_attention",
            "tp_prefill_attention", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_status_name", "tp_last_error"]
 
 
@@ -73,6 +74,8 @@ _SIGS = {
     "tp_swiglu": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P]),
     "tp_row_linear_partial": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I32, _P, _SZ, _P]),
     "tp_partial_sum": (_I32, [ctypes.POINTER(_P), _I32, _P, _P, _I64, _I64, _I32, _P]),
+    "tp_row_linear_partial_bf16": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "tp_partial_sum_bf16": (_I32, [ctypes.POINTER(_P), _I32, _P, _P, _I64, _I64, _I32, _P]),
     "tp_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I64]),
     "tp_decode_attention": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P, _SZ, _P]),
     "tp_prefill_attention": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P]),
@@ -205,6 +208,28 @@ def tp_partial_sum(partials: Sequence[torch.Tensor], out: torch.Tensor, residual
     m, n = out.shape
     arr = (ctypes.c_void_p * max(t, 1))(*[_ptr(p) for p in partials])
     _check(lib.tp_partial_sum(arr, t, _ptr(residual), _ptr(out), m, n, _dtype_code(out), _stream(stream)))
+    return out
+
+
+def tp_row_linear_partial_bf16(a: torch.Tensor, w: torch.Tensor, partial: torch.Tensor,
+                               ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """partial[m, n] = bf16(a @ w^T); a, w, partial bf16."""
+    m, k = a.shape
+    n = w.shape[0]
+    if ws is None:
+        ws = workspace(tp_linear_workspace_bytes(m, k, n, TP_BF16), a.device)
+    wp, wn = _ws(ws)
+    _check(lib.tp_row_linear_partial_bf16(_ptr(a), _ptr(w), _ptr(partial), m, k, n, wp, wn, _stream(stream)))
+    return partial
+
+
+def tp_partial_sum_bf16(partials: Sequence[torch.Tensor], out: torch.Tensor, residual: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """out = sum of t bf16 partials (float32 arithmetic, rank order) (+ residual)."""
+    t = len(partials)
+    m, n = out.shape
+    arr = (ctypes.c_void_p * max(t, 1))(*[_ptr(p) for p in partials])
+    _check(lib.tp_partial_sum_bf16(arr, t, _ptr(residual), _ptr(out), m, n, _dtype_code(out), _stream(stream)))
     return out
 
 

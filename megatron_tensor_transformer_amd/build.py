@@ -1,6 +1,8 @@
 """Build libtpshard.so in-tree with hipcc for gfx950.
 
-    python -m megatron_tensor_transformer_amd.build
+    python megatron_tensor_transformer_amd/build.py
+
+(run as a script: importing the package first would load a stale library)
 
 Each source under csrc/ is compiled to an object in _build/ (in parallel),
 then linked into megatron_tensor_transformer_amd/libtpshard.so. Packed-FP32

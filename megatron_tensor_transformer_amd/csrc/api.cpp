@@ -333,8 +333,12 @@ tp_status tp_swiglu(const void* gate, const void* up, void* out, int64_t m, int6
     return ok();
 }
 
-tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* residual, void* out, int64_t m,
-                         int64_t n, tp_dtype out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+tp_status partial_sum_impl(const void* const* partials, int in_bf16, int32_t t, const void* residual, void* out,
+                           int64_t m, int64_t n, tp_dtype out_dtype, void* stream) {
     TRY(check_dtype(out_dtype));
     if (!partials) return fail(TP_ERR_NULL, "partials is NULL");
     if (t < 1 || t > 8) return fail(TP_ERR_RANK, "t=%d outside 1..8", t);
@@ -342,7 +346,7 @@ tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* re
     if (residual) TRY(check_ptr(residual, "residual"));
     TRY(check_dims(m, 1, n));
     tpk::PartialPtrs ps{};
-    const size_t np = (size_t)m * n * 4;
+    const size_t np = (size_t)m * n * (in_bf16 ? 2 : 4);
     const size_t no = (size_t)m * n * esize(out_dtype);
     for (int r = 0; r < t; ++r) {
         char name[32];
@@ -353,9 +357,43 @@ tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* re
     }
     if (residual && residual != out && overlaps(out, no, residual, no))
         return fail(TP_ERR_ALIAS, "out partially overlaps residual (only exact in-place is allowed)");
-    hipError_t e = tpk::partial_sum_launch(ps, t, residual, out, m * n, out_dtype == TP_BF16, (hipStream_t)stream);
+    hipError_t e = tpk::partial_sum_launch(ps, t, residual, out, m * n, in_bf16, out_dtype == TP_BF16,
+                                           (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "partial-sum launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_partial_sum(const float* const* partials, int32_t t, const void* residual, void* out, int64_t m,
+                         int64_t n, tp_dtype out_dtype, void* stream) {
+    return partial_sum_impl(reinterpret_cast<const void* const*>(partials), 0, t, residual, out, m, n, out_dtype,
+                            stream);
+}
+
+tp_status tp_partial_sum_bf16(const void* const* partials, int32_t t, const void* residual, void* out, int64_t m,
+                              int64_t n, tp_dtype out_dtype, void* stream) {
+    return partial_sum_impl(partials, 1, t, residual, out, m, n, out_dtype, stream);
+}
+
+tp_status tp_row_linear_partial_bf16(const void* a, const void* w, void* partial, int64_t m, int64_t k, int64_t n,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    TRY(check_ptr(a, "a"));
+    TRY(check_ptr(w, "w"));
+    TRY(check_ptr(partial, "partial"));
+    TRY(check_dims(m, k, n));
+    if (k % 8) return fail(TP_ERR_ALIGN, "k=%lld is not a multiple of 8 (rows are read in 128-bit vectors)",
+                           (long long)k);
+    const size_t np = (size_t)m * n * 2;
+    if (overlaps(partial, np, a, (size_t)m * k * 2) || overlaps(partial, np, w, (size_t)n * k * 2))
+        return fail(TP_ERR_ALIAS, "partial overlaps an input");
+    if (ws && overlaps(ws, ws_bytes, partial, np)) return fail(TP_ERR_ALIAS, "workspace overlaps partial");
+    TRY(check_ws(ws, ws_bytes, linear_ws(m, k, n, TP_BF16, tpk::EPI_STORE, false)));
+    // A bf16 partial is the plain projection rounded to bf16: the store epilogue.
+    return run_linear(a, w, nullptr, nullptr, 0.f, partial, m, k, n, TP_BF16, tpk::EPI_STORE, ws_counters(ws),
+                      ws_scratch(ws), (hipStream_t)stream);
 }
 
 size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,

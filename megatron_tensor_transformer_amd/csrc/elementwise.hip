@@ -17,17 +17,32 @@ static int ew_blocks(int64_t items) {
     return (int)b;
 }
 
-// Sum of partials: each thread handles 4 float32 per partial (one 128-bit load
-// from each), added in rank order, then the residual.
-template <bool OUT_BF16>
+// Sum of partials: each thread handles 4 elements of every partial (one
+// 128-bit float32 or 64-bit bf16 load from each), added in float32 in rank
+// order, then the residual.
+template <bool IN_BF16>
+__device__ __forceinline__ float4 load4(const void* p, int64_t i) {
+    if (IN_BF16) {
+        const uint2 v = reinterpret_cast<const uint2*>(p)[i];
+        return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+    }
+    return reinterpret_cast<const float4*>(p)[i];
+}
+template <bool IN_BF16>
+__device__ __forceinline__ float load1(const void* p, int64_t i) {
+    if (IN_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+    return reinterpret_cast<const float*>(p)[i];
+}
+
+template <bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(EW_THREADS) void partial_sum_kernel(PartialPtrs ps, int t, const void* residual,
                                                                  void* out, int64_t count) {
     const int64_t n4 = count / 4;
     const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
     for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n4; i += stride) {
-        float4 acc = reinterpret_cast<const float4*>(ps.p[0])[i];
+        float4 acc = load4<IN_BF16>(ps.p[0], i);
         for (int r = 1; r < t; ++r) {
-            const float4 v = reinterpret_cast<const float4*>(ps.p[r])[i];
+            const float4 v = load4<IN_BF16>(ps.p[r], i);
             acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
         }
         if (OUT_BF16) {
@@ -50,8 +65,8 @@ __global__ __launch_bounds__(EW_THREADS) void partial_sum_kernel(PartialPtrs ps,
     // tail (count not a multiple of 4)
     const int64_t tail0 = n4 * 4;
     for (int64_t i = tail0 + (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < count; i += stride) {
-        float acc = ps.p[0][i];
-        for (int r = 1; r < t; ++r) acc += ps.p[r][i];
+        float acc = load1<IN_BF16>(ps.p[0], i);
+        for (int r = 1; r < t; ++r) acc += load1<IN_BF16>(ps.p[r], i);
         if (OUT_BF16) {
             if (residual) acc += bf16_to_f32(reinterpret_cast<const uint16_t*>(residual)[i]);
             reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(acc);
@@ -63,12 +78,16 @@ __global__ __launch_bounds__(EW_THREADS) void partial_sum_kernel(PartialPtrs ps,
 }
 
 hipError_t partial_sum_launch(const PartialPtrs& ps, int t, const void* residual, void* out, int64_t count,
-                              int out_bf16, hipStream_t s) {
+                              int in_bf16, int out_bf16, hipStream_t s) {
     const int blocks = ew_blocks((count + 3) / 4);
-    if (out_bf16)
-        hipLaunchKernelGGL(partial_sum_kernel<true>, dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
+    if (in_bf16 && out_bf16)
+        hipLaunchKernelGGL((partial_sum_kernel<true, true>), dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
+    else if (in_bf16)
+        hipLaunchKernelGGL((partial_sum_kernel<true, false>), dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
+    else if (out_bf16)
+        hipLaunchKernelGGL((partial_sum_kernel<false, true>), dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
     else
-        hipLaunchKernelGGL(partial_sum_kernel<false>, dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
+        hipLaunchKernelGGL((partial_sum_kernel<false, false>), dim3(blocks), dim3(EW_THREADS), 0, s, ps, t, residual, out, count);
     return hipGetLastError();
 }
 

@@ -72,10 +72,11 @@ hipError_t rmsnorm_launch(const void* x, const void* gamma, void* u, int m, int 
 hipError_t swiglu_launch(const void* gate, const void* up, void* out, int64_t count, int is_bf16,
                          hipStream_t stream);
 
-// out = sum_r partials[r] (+ residual), rank order.
-struct PartialPtrs { const float* p[8]; };
+// out = sum_r partials[r] (+ residual), rank order, float32 arithmetic;
+// partials float32 or bf16.
+struct PartialPtrs { const void* p[8]; };
 hipError_t partial_sum_launch(const PartialPtrs& ptrs, int t, const void* residual, void* out, int64_t count,
-                              int out_bf16, hipStream_t stream);
+                              int in_bf16, int out_bf16, hipStream_t stream);
 
 // Split-KV grouped-query decode attention.
 struct AttnArgs {

@@ -177,6 +177,24 @@ def test_partial_sum_validation():
     assert rejected(tp.lib.tp_partial_sum(None, 2, None, A, 4, 4, 0, None)) == "TP_ERR_NULL"
 
 
+def test_bf16_partial_validation():
+    def row(a=A, w=A + 64 * MB, part=A + 128 * MB, m=4, k=256, n=512, ws=None, wsn=0):
+        return rejected(tp.lib.tp_row_linear_partial_bf16(a, w, part, m, k, n, ws, wsn, None))
+    assert row(a=None) == "TP_ERR_NULL"
+    assert row(k=260) == "TP_ERR_ALIGN"
+    assert row(part=A + 16) == "TP_ERR_ALIAS"
+    assert row(m=0) == "TP_ERR_SHAPE"
+
+    def f(ptrs, t, res=None, out=A + 100 * MB, m=4, n=64, dt=tp.TP_BF16):
+        arr = (ctypes.c_void_p * max(len(ptrs), 1))(*ptrs)
+        return rejected(tp.lib.tp_partial_sum_bf16(arr, t, res, out, m, n, dt, None))
+    ptrs = [A + i * MB for i in range(8)]
+    assert f(ptrs, 0) == "TP_ERR_RANK"
+    assert f([A, None], 2) == "TP_ERR_NULL"
+    assert f(ptrs, 4, out=A + 2 * MB + 256) == "TP_ERR_ALIAS"
+    assert f(ptrs, 4, dt=7) == "TP_ERR_DTYPE"
+
+
 def attn(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=16, qh=8, kvh=1, d=128, cap=8192, L=8192,
          dt=tp.TP_BF16, ws=None, wsn=0):
     return rejected(tp.lib.tp_decode_attention(q, k, v, out, B, qh, kvh, d, cap, L, dt, ws, wsn, None))

@@ -115,6 +115,30 @@ def test_mlp_decode_bf16(mlp8b, m, gamma_mode):
     check("sum of 4 partials", host(out), ref["y"], TOL["bf16"])
 
 
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_mlp_decode_bf16_partials(mlp8b, m):
+    """The MLP decode step with bf16 row partials and their float32 sum."""
+    wl, inp, desc, ranks = mlp8b
+    xs = inp["x"][:m]
+    ref = L.mlp_block(xs, inp["w_gate"], inp["w_up"], inp["w_down"], inp["gamma"], wl.eps)
+    sref = S.sharded_mlp(xs, inp["w_gate"], inp["w_up"], inp["w_down"], wl.t, inp["gamma"], wl.eps)
+    x = dev(xs, "bf16")
+    gam = dev(inp["gamma"], "bf16")
+    parts = []
+    for r, (p, (wg, wu, wd)) in enumerate(ranks):
+        a = empty((m, p.inter_cols), torch.bfloat16)
+        tp.tp_column_linear(x, wg, a, w_up=wu, gamma=gam, eps=wl.eps)
+        part = empty((m, wl.hidden), torch.bfloat16)
+        tp.tp_row_linear_partial_bf16(a, wd, part)
+        parts.append(part)
+    out = empty((m, wl.hidden), torch.bfloat16)
+    tp.tp_partial_sum_bf16(parts, out)
+    torch.cuda.synchronize()
+    for r in range(wl.t):
+        check(f"rank{r} bf16 partial", host(parts[r]), sref["ranks"][r]["partial"], TOL["bf16"])
+    check("sum of 4 bf16 partials", host(out), ref["y"], TOL["bf16"])
+
+
 # ---------------------------------------------------------------- 70B-shaped attention projections, t=4
 
 def qkv_rank_phys(a, p, d):
@@ -433,6 +457,33 @@ def test_partial_sum_shapes(t, shape, out_dt, residual):
     tp.tp_partial_sum([dev(p, "f32") for p in parts], out, residual=dev(res, out_dt) if residual else None)
     torch.cuda.synchronize()
     check(f"partial sum t={t} {shape} {out_dt}", host(out), ref, 1e-6 if out_dt == "f32" else 2 ** -8)
+
+
+@pytest.mark.parametrize("t", [1, 3, 8])
+@pytest.mark.parametrize("shape", [(5, 7), (16, 8192), (3, 1)])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+@pytest.mark.parametrize("residual", [False, True])
+def test_partial_sum_bf16_shapes(t, shape, out_dt, residual):
+    parts = [W.to_bf16(W.normal(300 + r, 0, shape)) for r in range(t)]
+    res = W.storage_round(W.normal(399, 0, shape), out_dt) if residual else None
+    ref = sum(p.astype(np.float64) for p in parts) + (res if residual else 0.0)
+    out = empty(shape, torch.bfloat16 if out_dt == "bf16" else torch.float32)
+    tp.tp_partial_sum_bf16([dev(p, "bf16") for p in parts], out, residual=dev(res, out_dt) if residual else None)
+    torch.cuda.synchronize()
+    check(f"bf16 partial sum t={t} {shape} {out_dt}", host(out), ref, 1e-6 if out_dt == "f32" else 2 ** -8)
+
+
+@pytest.mark.parametrize("case", [c for c in LINEAR_CASES if c[3] == "bf16"], ids=lambda c: "x".join(map(str, c)))
+def test_row_partial_bf16_shapes(case):
+    m, k, n, _ = case
+    seed = 500 + m + k
+    x = W.to_bf16(W.normal(seed, 0, (m, k)))
+    wl_ = W.to_bf16(W.normal(seed, 1, (k, n), 0.02))
+    ref = L.linear(x, wl_)
+    part = empty((m, n), torch.bfloat16)
+    tp.tp_row_linear_partial_bf16(dev(x, "bf16"), dev(phys(wl_), "bf16"), part)
+    torch.cuda.synchronize()
+    check(f"bf16 row partial m={m} k={k} n={n}", host(part), ref, TOL["bf16"])
 
 
 @pytest.mark.parametrize("count", [(1, 1), (3, 333), (16, 3584)])
