@@ -215,3 +215,38 @@ def attn_proj_block(x, attn_in, w_q, w_k, w_v, w_o) -> Dict[str, np.ndarray]:
 
 def maybe(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
     return None if a is None else f64(a)
+
+
+def moe_route(logits, k: int) -> np.ndarray:
+    """Router gates [m, E] from logits [m, E]: the k largest logits of a token
+    (ties to the lower expert index) get softmax weights over those k alone,
+    the other experts 0. (Mixtral-style top-k routing; the softmax over the
+    selected logits equals a softmax over all experts renormalised on the top k.)
+    """
+    logits = f64(logits)
+    m, E = logits.shape
+    gates = np.zeros((m, E))
+    for t in range(m):
+        order = sorted(range(E), key=lambda e: (-logits[t, e], e))[:k]
+        sel = logits[t, order]
+        p = np.exp(sel - sel.max())
+        gates[t, order] = p / p.sum()
+    return gates
+
+
+def moe_block(x, gamma, w_router, experts, k: int, eps: float = 1e-5, gates=None) -> Dict[str, np.ndarray]:
+    """Mixture-of-experts FFN: u = RMSNorm(x); gates from u @ W_router [H, E];
+    y = sum_e gate[:, e] * (swiglu(u @ W_gate_e, u @ W_up_e) @ W_down_e).
+
+    ``experts`` is a list of (w_gate [H, I], w_up [H, I], w_down [I, H]).
+    ``gates`` may be given to take the routing decision elsewhere (for
+    instance on logits computed in another precision).
+    """
+    u = rmsnorm(x, gamma, eps) if gamma is not None else f64(x)
+    logits = linear(u, w_router)
+    if gates is None:
+        gates = moe_route(logits, k)
+    y = np.zeros((u.shape[0], np.shape(experts[0][2])[1]))
+    for e, (wg, wu, wd) in enumerate(experts):
+        y += gates[:, e:e + 1] * linear(swiglu(linear(u, wg), linear(u, wu)), wd)
+    return {"u": u, "logits": logits, "gates": gates, "y": y}

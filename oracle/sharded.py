@@ -204,3 +204,22 @@ def sharded_layer(x, w: Dict[str, Optional[np.ndarray]], k_cache, v_cache, kv_le
     mlp = [rank_mlp(h, w["w_gate"], w["w_up"], w["w_down"], p, w.get("gamma2"), eps) for p in plans]
     out = sum_partials([m["partial"] for m in mlp], h if residual else None)
     return {"plans": plans, "attn": attn, "h": h, "mlp": mlp, "out": out}
+
+
+def rank_moe(x, gamma, w_router, experts, gates, p: dict, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """One rank's share of a mixture-of-experts FFN: every expert's gate/up
+    column block and down row block (the expert FFNs are sharded like the
+    dense MLP), weighted by the routing gates [m, E] the router (replicated
+    on every rank) produced, summed over the experts into one row partial."""
+    b, c = p["inter_begin"], p["inter_cols"]
+    u = _norm(x, gamma, eps)
+    gates = _f(gates)
+    partial = np.zeros((u.shape[0], np.shape(experts[0][2])[1]))
+    acts = []
+    for e, (wg, wu, wd) in enumerate(experts):
+        g = _mm(u, column_shard(wg, b, c))
+        v = _mm(u, column_shard(wu, b, c))
+        a = _silu(g) * v * gates[:, e][:, None]
+        acts.append(a)
+        partial = partial + _mm(a, row_shard(wd, b, c))
+    return {"a": np.concatenate(acts, axis=1), "partial": partial}

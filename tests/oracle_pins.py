@@ -462,3 +462,74 @@ def pin_sharded_layer_prefill(sharded_layer_prefill, layer_prefill):
                 for a, p in zip(s["attn"], s["plans"]):
                     kb, kn = p["kv_head_begin"], p["kv_heads"]
                     assert relerr(a["k_cache"], ref["attn"]["k_cache"][:, kb:kb + kn]) < 1e-13
+
+
+def pin_moe_route(moe_route):
+    """Top-k routing on hand-computed cases."""
+    g = moe_route(np.array([[1.0, 3.0, 2.0, 0.0]]), 2)
+    w1 = 1.0 / (1.0 + math.exp(-1.0))                # e^3 / (e^3 + e^2)
+    assert np.allclose(g, [[0.0, w1, 1.0 - w1, 0.0]], rtol=0, atol=1e-15)
+    g = moe_route(np.array([[5.0, 5.0, 5.0, 1.0]]), 2)  # ties go to the lower index
+    assert np.allclose(g, [[0.5, 0.5, 0.0, 0.0]], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((6, 8))
+    one = moe_route(logits, 1)
+    assert np.array_equal(one, np.eye(8)[np.argmax(logits, axis=1)])
+    from scipy.special import softmax as sp_softmax
+    assert np.allclose(moe_route(logits, 8), sp_softmax(logits, axis=1), rtol=0, atol=1e-14)
+    g2 = moe_route(logits, 2)
+    assert np.allclose(g2.sum(axis=1), 1.0, atol=1e-15) and np.all((g2 > 0).sum(axis=1) == 2)
+    top2 = np.argsort(-logits, axis=1, kind="stable")[:, :2]
+    assert all(set(np.nonzero(g2[t])[0]) == set(top2[t]) for t in range(6))
+
+
+def small_moe(seed=61, m=5, H=16, I=12, E=4):
+    x = W.storage_round(W.normal(seed, W.X, (m, H)), "f32")
+    gamma = W.gamma(seed, W.GAMMA2, H, "random", "f32")
+    w_router = W.storage_round(W.normal(seed, W.ATTN_IN, (H, E)), "f32")
+    experts = []
+    for e in range(E):
+        mi = W.mlp_inputs(seed * 100 + e, H, I, 1, "f32")
+        experts.append((mi["w_gate"], mi["w_up"], mi["w_down"]))
+    return x, gamma, w_router, experts
+
+
+def pin_moe_identical_and_single(moe_block, mlp_block):
+    """Identical experts give the dense MLP (gates sum to one); so does one expert with k=1."""
+    x, gamma, w_router, experts = small_moe()
+    same = [experts[0]] * 4
+    ref = mlp_block(x, *experts[0], gamma, 1e-5)["y"]
+    for k in (1, 2, 4):
+        assert relerr(moe_block(x, gamma, w_router, same, k, 1e-5)["y"], ref) < 1e-13, k
+    assert relerr(moe_block(x, gamma, w_router[:, :1], experts[:1], 1, 1e-5)["y"], ref) < 1e-13
+
+
+def pin_moe_vs_naive(moe_block):
+    """The MoE FFN against brute-force loops: routing by hand, then each chosen expert."""
+    x, gamma, w_router, experts = small_moe(seed=63, m=3, H=6, I=5, E=4)
+    k = 2
+    got = moe_block(x, gamma, w_router, experts, k, 1e-5)
+    u = naive.rmsnorm(x, gamma, 1e-5)
+    logits = naive.matmul(u, w_router)
+    out = [[0.0] * 6 for _ in range(3)]
+    for t in range(3):
+        order = sorted(range(4), key=lambda e: (-logits[t][e], e))[:k]
+        mx = max(logits[t][e] for e in order)
+        den = sum(math.exp(logits[t][e] - mx) for e in order)
+        for e in order:
+            w = math.exp(logits[t][e] - mx) / den
+            y = naive.mlp([u[t]], *experts[e])[0]
+            for j in range(6):
+                out[t][j] += w * y[j]
+    assert relerr(got["y"], out) < 1e-13
+
+
+def pin_rank_moe(rank_moe, moe_block, rank_plan, ModelDesc):
+    """Every expert sharded like the dense MLP: the rank partials sum to the unsharded MoE FFN."""
+    x, gamma, w_router, experts = small_moe(seed=65, m=4, H=16, I=16, E=4)
+    ref = moe_block(x, gamma, w_router, experts, 2, 1e-5)
+    for t in (1, 2, 4):
+        desc = ModelDesc(hidden=16, intermediate=16)
+        parts = [rank_moe(x, gamma, w_router, experts, ref["gates"], rank_plan(desc, t, r), 1e-5)["partial"]
+                 for r in range(t)]
+        assert relerr(sum(parts), ref["y"]) < 1e-12, t

@@ -35,6 +35,13 @@ def _all_layer_prefill_pins():
     P.pin_sharded_layer_prefill(S.sharded_layer_prefill, L.layer_prefill)
 
 
+def _all_moe_pins():
+    P.pin_moe_route(L.moe_route)
+    P.pin_moe_identical_and_single(L.moe_block, L.mlp_block)
+    P.pin_moe_vs_naive(L.moe_block)
+    P.pin_rank_moe(S.rank_moe, L.moe_block, plan.rank_plan, plan.ModelDesc)
+
+
 def _all_sharded_pins():
     P.pin_silu(S._silu)
     P.pin_rmsnorm(lambda x, g, eps: S._norm(x, g, eps))
@@ -120,6 +127,30 @@ def _rank_attention_prefill_no_norm(x, w_q, w_k, w_v, w_o, kc, vc, kv_len, n_q, 
     return _orig_rank_attention_prefill(x, w_q, w_k, w_v, w_o, kc, vc, kv_len, n_q, n_kv, d, p, None, eps)
 
 
+_orig_moe_route = L.moe_route
+_orig_rank_moe = S.rank_moe
+
+
+def _moe_route_no_renorm(logits, k):
+    # keeps the full-softmax probabilities of the top k instead of renormalising them
+    g = _orig_moe_route(logits, k)
+    full = L.softmax(np.asarray(logits, np.float64))
+    return np.where(g > 0, full, 0.0)
+
+
+def _moe_route_smallest(logits, k):
+    return _orig_moe_route(-np.asarray(logits, np.float64), k)
+
+
+def _moe_route_ties_high(logits, k):
+    lg = np.asarray(logits, np.float64)
+    return _orig_moe_route(lg[:, ::-1], k)[:, ::-1]
+
+
+def _rank_moe_no_gates(x, gamma, w_router, experts, gates, p, eps=1e-5):
+    return _orig_rank_moe(x, gamma, w_router, experts, (np.asarray(gates) > 0).astype(float), p, eps)
+
+
 def _plan_shift_heads(desc, t, rank):
     p = dict(_orig_rank_plan(desc, t, rank))
     p["q_head_begin"] = rank * p["q_heads"] + (1 if rank and p["q_heads"] > 1 else 0)
@@ -197,6 +228,10 @@ MUTATIONS = {
     "prefill_block_append_transposed": (L, "append_kv_block", _append_block_token_major, _all_layer_prefill_pins),
     "rank_attention_prefill_no_norm": (S, "rank_attention_prefill", _rank_attention_prefill_no_norm,
                                        _all_layer_prefill_pins),
+    "moe_route_not_renormalised": (L, "moe_route", _moe_route_no_renorm, _all_moe_pins),
+    "moe_route_picks_smallest": (L, "moe_route", _moe_route_smallest, _all_moe_pins),
+    "moe_route_ties_to_higher_index": (L, "moe_route", _moe_route_ties_high, _all_moe_pins),
+    "rank_moe_ignores_gate_weights": (S, "rank_moe", _rank_moe_no_gates, _all_moe_pins),
     # decomposition
     "sum_drops_last_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
         [np.asarray(p, float) for p in parts[:-1]] or [np.zeros_like(parts[0])], axis=0)

@@ -99,3 +99,19 @@ def test_layer_prefill_vs_naive():
 
 def test_sharded_layer_prefill():
     P.pin_sharded_layer_prefill(S.sharded_layer_prefill, L.layer_prefill)
+
+
+def test_moe_route():
+    P.pin_moe_route(L.moe_route)
+
+
+def test_moe_identical_and_single():
+    P.pin_moe_identical_and_single(L.moe_block, L.mlp_block)
+
+
+def test_moe_vs_naive():
+    P.pin_moe_vs_naive(L.moe_block)
+
+
+def test_rank_moe():
+    P.pin_rank_moe(S.rank_moe, L.moe_block, plan.rank_plan, plan.ModelDesc)
