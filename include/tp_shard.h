@@ -302,6 +302,51 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
                                  float* partial, int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/*
+ * Mixture of experts. "Tensor Parallelism Fundamentals", section "Sizing
+ * Heuristics and Limits": for a mixture-of-experts model tensor parallelism
+ * shards the expert feed-forward layers as well as attention. Each expert's
+ * FFN is split like the dense MLP: this rank holds the same column block of
+ * every expert's gate and up projections and the matching row block of its
+ * down projection. The router is replicated on every rank.
+ *
+ * One rank's MoE FFN (bf16, float32 accumulation):
+ *   u = RMSNorm(x; norm) (or x when norm is NULL)
+ *   logits = u @ W_router^T                       [m, E] float32
+ *   gates  = top_k of each row of logits (ties to the lower expert), softmax
+ *            over the selected logits, 0 for the other experts
+ *   a_e = gates[:, e] * silu(u @ W_gate_e^T) * (u @ W_up_e^T)
+ *   partial = sum_e a_e @ W_down_e^T              [m, H] float32
+ * The caller sums the t ranks' partials with tp_partial_sum; all ranks must
+ * see the same gates (the router weights are identical on every rank).
+ * Experts a token is not routed to carry gate 0, so the result is the sum
+ * over its top_k experts; every expert's weights are read each call.
+ */
+typedef struct tp_moe_weights {
+    const void* norm;      /* [H] gamma in front of the router and experts, or NULL */
+    const void* w_router;  /* [E, H] */
+    const void* w_gate;    /* [E * inter_cols, H]: expert e's rows e*inter_cols .. (e+1)*inter_cols - 1 */
+    const void* w_up;      /* [E * inter_cols, H], stacked the same way */
+    const void* w_down;    /* [H, E * inter_cols]: expert e's columns e*inter_cols .. (e+1)*inter_cols - 1 */
+} tp_moe_weights;
+
+/* Workspace bytes of tp_moe_shard_forward (has_norm: weights->norm != NULL). */
+size_t tp_moe_workspace_bytes(int64_t m, int64_t hidden, int32_t n_experts, int64_t inter_cols,
+                              int32_t has_norm);
+
+/*
+ * tp_moe_shard_forward - the MoE FFN above for m tokens x [m, hidden] (bf16).
+ * partial     device [m, hidden] float32
+ * gates_out   device [m, n_experts] float32, or NULL
+ * logits_out  device [m, n_experts] float32, or NULL
+ * 1 <= n_experts <= 64, 1 <= top_k <= n_experts (TP_ERR_SHAPE); hidden and
+ * inter_cols (this rank's columns of one expert, intermediate / t) multiples
+ * of 8 (TP_ERR_ALIGN).
+ */
+tp_status tp_moe_shard_forward(const tp_moe_weights* weights, const void* x, float* partial, float* gates_out,
+                               float* logits_out, int64_t m, int64_t hidden, int32_t n_experts, int32_t top_k,
+                               int64_t inter_cols, float eps, void* ws, size_t ws_bytes, void* stream);
+
 /* Name of a status code, e.g. "TP_ERR_SHAPE". */
 const char* tp_status_name(tp_status status);
 

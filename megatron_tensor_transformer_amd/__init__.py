@@ -37,7 +37,7 @@ STATUS = ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_
 EXPORTS = ["tp_shard_plan", "tp_linear_workspace_bytes", "tp_column_linear", "tp_swiglu",
            "tp_row_linear_partial", "tp_partial_sum", "tp_row_linear_partial_bf16", "tp_partial_sum_bf16",
            "tp_attention_workspace_bytes", "tp_decode_attention",
-           "tp_prefill_attention", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_status_name", "tp_last_error"]
+           "tp_prefill_attention", "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_status_name", "tp_last_error"]
 
 
 class tp_model_desc(ctypes.Structure):
@@ -66,6 +66,10 @@ class tp_kv_view(ctypes.Structure):
                 ("kv_len", ctypes.c_int64), ("new_tokens", ctypes.c_int64)]
 
 
+class tp_moe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("norm", "w_router", "w_gate", "w_up", "w_down")]
+
+
 _P, _I64, _I32, _F, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "tp_shard_plan": (_I32, [ctypes.POINTER(tp_model_desc), _I32, _I32, ctypes.POINTER(tp_rank_plan)]),
@@ -79,6 +83,9 @@ _SIGS = {
     "tp_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I64]),
     "tp_decode_attention": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P, _SZ, _P]),
     "tp_prefill_attention": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P]),
+    "tp_moe_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I64, _I32]),
+    "tp_moe_shard_forward": (_I32, [ctypes.POINTER(tp_moe_weights), _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I64,
+                                    _F, _P, _SZ, _P]),
     "tp_layer_workspace_bytes": (_SZ, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
                                        _I64, _I32]),
     "tp_layer_shard_forward": (_I32, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
@@ -259,6 +266,26 @@ def tp_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     _check(lib.tp_prefill_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, q_heads, kv_heads, d, cap, kv_len,
                                     _dtype_code(q), _stream(stream)))
     return out
+
+
+def tp_moe_workspace_bytes(m: int, hidden: int, n_experts: int, inter_cols: int, has_norm: bool = True) -> int:
+    return lib.tp_moe_workspace_bytes(m, hidden, n_experts, inter_cols, int(bool(has_norm)))
+
+
+def tp_moe_shard_forward(weights: Dict[str, torch.Tensor], x: torch.Tensor, partial: torch.Tensor, n_experts: int,
+                         top_k: int, inter_cols: int, eps: float = 1e-5, gates: Optional[torch.Tensor] = None,
+                         logits: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """One rank's MoE FFN: weights {"norm", "w_router", "w_gate", "w_up", "w_down"} (experts stacked)."""
+    m, H = x.shape
+    w = tp_moe_weights(*[_ptr(weights.get(n)) for n in ("norm", "w_router", "w_gate", "w_up", "w_down")])
+    if ws is None:
+        ws = workspace(tp_moe_workspace_bytes(m, H, n_experts, inter_cols, weights.get("norm") is not None),
+                       x.device)
+    wp, wn = _ws(ws)
+    _check(lib.tp_moe_shard_forward(ctypes.byref(w), _ptr(x), _ptr(partial), _ptr(gates), _ptr(logits), m, H,
+                                    n_experts, top_k, inter_cols, eps, wp, wn, _stream(stream)))
+    return partial
 
 
 def tp_layer_workspace_bytes(desc: tp_model_desc, plan: tp_rank_plan, stage: int, m: int, dtype: int) -> int:

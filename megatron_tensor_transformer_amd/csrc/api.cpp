@@ -396,6 +396,97 @@ tp_status tp_row_linear_partial_bf16(const void* a, const void* w, void* partial
                       ws_scratch(ws), (hipStream_t)stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// MoE workspace: [header][u (normalised x)][logits][gates][expert activations][projection scratch].
+struct MoeWs {
+    size_t u, logits, gates, act, lin, total;
+};
+
+MoeWs moe_ws(int64_t m, int64_t H, int32_t E, int64_t cols, bool norm) {
+    MoeWs w{};
+    const int64_t ecols = (int64_t)E * cols;
+    w.u = norm ? round256((size_t)m * H * 2) : 0;
+    w.logits = round256((size_t)m * E * 4);
+    w.gates = round256((size_t)m * E * 4);
+    w.act = round256((size_t)m * ecols * 2);
+    size_t l = linear_scratch(m, H, E, TP_BF16, tpk::EPI_PARTIAL, false);
+    const size_t l2 = linear_scratch(m, H, ecols, TP_BF16, tpk::EPI_SWIGLU, false);
+    const size_t l3 = linear_scratch(m, ecols, H, TP_BF16, tpk::EPI_PARTIAL, false);
+    if (l2 > l) l = l2;
+    if (l3 > l) l = l3;
+    w.lin = l;
+    w.total = tpk::WS_HEADER + w.u + w.logits + w.gates + w.act + w.lin;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tp_moe_workspace_bytes(int64_t m, int64_t hidden, int32_t n_experts, int64_t inter_cols, int32_t has_norm) {
+    if (m < 1 || hidden < 1 || n_experts < 1 || n_experts > 64 || inter_cols < 1) return 0;
+    return moe_ws(m, hidden, n_experts, inter_cols, has_norm != 0).total;
+}
+
+tp_status tp_moe_shard_forward(const tp_moe_weights* w, const void* x, float* partial, float* gates_out,
+                               float* logits_out, int64_t m, int64_t hidden, int32_t n_experts, int32_t top_k,
+                               int64_t inter_cols, float eps, void* ws, size_t ws_bytes, void* stream) {
+    if (!w) return fail(TP_ERR_NULL, "weights is NULL");
+    TRY(check_ptr(x, "x"));
+    TRY(check_ptr(partial, "partial"));
+    TRY(check_ptr(w->w_router, "weights->w_router"));
+    TRY(check_ptr(w->w_gate, "weights->w_gate"));
+    TRY(check_ptr(w->w_up, "weights->w_up"));
+    TRY(check_ptr(w->w_down, "weights->w_down"));
+    if (w->norm) TRY(check_ptr(w->norm, "weights->norm"));
+    if (gates_out) TRY(check_ptr(gates_out, "gates_out"));
+    if (logits_out) TRY(check_ptr(logits_out, "logits_out"));
+    if (n_experts < 1 || n_experts > 64) return fail(TP_ERR_SHAPE, "n_experts=%d outside 1..64", n_experts);
+    if (top_k < 1 || top_k > n_experts) return fail(TP_ERR_SHAPE, "top_k=%d outside 1..n_experts", top_k);
+    if (!(eps >= 0.0f)) return fail(TP_ERR_SHAPE, "eps must be >= 0");
+    TRY(check_dims(m, hidden, (int64_t)n_experts * inter_cols));
+    if (hidden % 8 || inter_cols % 8)
+        return fail(TP_ERR_ALIGN, "hidden=%lld and inter_cols=%lld must be multiples of 8", (long long)hidden,
+                    (long long)inter_cols);
+    const int64_t ecols = (int64_t)n_experts * inter_cols;
+    const size_t np = (size_t)m * hidden * 4;
+    if (overlaps(partial, np, x, (size_t)m * hidden * 2)) return fail(TP_ERR_ALIAS, "partial overlaps x");
+    const MoeWs L = moe_ws(m, hidden, n_experts, inter_cols, w->norm != nullptr);
+    TRY(check_ws(ws, ws_bytes, L.total));
+    if (overlaps(ws, ws_bytes, partial, np)) return fail(TP_ERR_ALIAS, "workspace overlaps partial");
+    char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
+    unsigned* cnt = ws_counters(ws);
+    void* u = b;
+    float* logits = logits_out ? logits_out : reinterpret_cast<float*>(b + L.u);
+    float* gates = gates_out ? gates_out : reinterpret_cast<float*>(b + L.u + L.logits);
+    void* act = b + L.u + L.logits + L.gates;
+    void* lin = b + L.u + L.logits + L.gates + L.act;
+    hipStream_t s = (hipStream_t)stream;
+    const void* xin = x;
+    if (w->norm) {
+        hipError_t e = tpk::rmsnorm_launch(x, w->norm, u, (int)m, (int)hidden, eps, 1, s);
+        if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+        xin = u;
+    }
+    // The router is replicated on every rank: logits = u @ W_router^T, float32.
+    TRY(run_linear(xin, w->w_router, nullptr, nullptr, 0.f, logits, m, hidden, n_experts, TP_BF16,
+                   tpk::EPI_PARTIAL, cnt, lin, s));
+    hipError_t e = tpk::moe_gates_launch(logits, gates, (int)m, n_experts, top_k, s);
+    if (e != hipSuccess) return hip_fail(e, "router gates launch");
+    // Every expert's gate/up column block at once (rows stacked expert by expert).
+    TRY(run_linear(xin, w->w_gate, w->w_up, nullptr, 0.f, act, m, hidden, ecols, TP_BF16, tpk::EPI_SWIGLU, cnt,
+                   lin, s));
+    e = tpk::moe_scale_launch(act, gates, (int)m, n_experts, inter_cols, s);
+    if (e != hipSuccess) return hip_fail(e, "expert gate scaling launch");
+    // Every expert's down row block at once: the gate-weighted sum over experts is the contraction over the
+    // stacked intermediate columns.
+    return run_linear(act, w->w_down, nullptr, nullptr, 0.f, partial, m, ecols, hidden, TP_BF16, tpk::EPI_PARTIAL,
+                      cnt, lin, s);
+}
+
 size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
                                     int64_t kv_len) {
     if (batch < 1 || q_heads < 1 || kv_heads < 1 || q_heads % kv_heads || kv_len < 1) return 0;

@@ -232,4 +232,59 @@ hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Router gates: per token, the top_k largest of its E logits (ties to the
+// lower expert index) get softmax weights over those k alone, the rest 0.
+// One thread per token; E is small.
+__global__ __launch_bounds__(EW_THREADS) void moe_gates_kernel(const float* logits, float* gates, int m, int E,
+                                                               int top_k) {
+    const int t = blockIdx.x * EW_THREADS + threadIdx.x;
+    if (t >= m) return;
+    const float* lg = logits + (size_t)t * E;
+    float* g = gates + (size_t)t * E;
+    uint64_t chosen = 0;                            // bit e: expert e selected (E <= 64)
+    float mx = 0.f;
+    for (int j = 0; j < top_k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (!((chosen >> e) & 1) && (best < 0 || lg[e] > lg[best])) best = e;
+        chosen |= uint64_t(1) << best;
+        if (j == 0) mx = lg[best];
+    }
+    float den = 0.f;
+    for (int e = 0; e < E; ++e)
+        if ((chosen >> e) & 1) den += expf(lg[e] - mx);
+    for (int e = 0; e < E; ++e) g[e] = ((chosen >> e) & 1) ? expf(lg[e] - mx) / den : 0.f;
+}
+
+hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t s) {
+    hipLaunchKernelGGL(moe_gates_kernel, dim3((m + EW_THREADS - 1) / EW_THREADS), dim3(EW_THREADS), 0, s, logits,
+                       gates, m, E, top_k);
+    return hipGetLastError();
+}
+
+// a[t, e * cols + i] *= gates[t, e] in place (bf16), 8 elements per thread.
+__global__ __launch_bounds__(EW_THREADS) void moe_scale_kernel(uint16_t* a, const float* gates, int m, int E,
+                                                               int64_t cols) {
+    const int64_t row8 = (int64_t)E * cols / 8;
+    const int64_t total = (int64_t)m * row8;
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < total; i += stride) {
+        const int64_t t = i / row8;
+        const int e = (int)((i - t * row8) * 8 / cols);
+        const float w = gates[t * E + e];
+        uint4 v = reinterpret_cast<const uint4*>(a)[i];
+        uint32_t* p = &v.x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[j] = pack_bf16x2(bf16lo(p[j]) * w, bf16hi(p[j]) * w);
+        reinterpret_cast<uint4*>(a)[i] = v;
+    }
+}
+
+hipError_t moe_scale_launch(void* a, const float* gates, int m, int E, int64_t cols, hipStream_t s) {
+    const int blocks = ew_blocks((int64_t)m * E * cols / 8);
+    hipLaunchKernelGGL(moe_scale_kernel, dim3(blocks), dim3(EW_THREADS), 0, s, reinterpret_cast<uint16_t*>(a), gates,
+                       m, E, cols);
+    return hipGetLastError();
+}
+
 }  // namespace tpk

@@ -108,6 +108,12 @@ struct GemmArgs {
 bool gemm_supported(int M, int N, int K, int epi);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
 
+// Mixture of experts: top-k router gates from float32 logits [m, E] (E <= 64),
+// and a[t, e * cols + i] *= gates[t, e] on bf16 expert activations
+// (cols a multiple of 8).
+hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t stream);
+hipError_t moe_scale_launch(void* a, const float* gates, int m, int E, int64_t cols, hipStream_t stream);
+
 // Block KV append: k, v columns of rows [batch * seq] of a [q | k | v] buffer
 // (row_stride elements per row) to cache positions pos0 .. pos0 + seq - 1 (bf16).
 struct KvAppendArgs {

@@ -195,6 +195,28 @@ def test_bf16_partial_validation():
     assert f(ptrs, 4, dt=7) == "TP_ERR_DTYPE"
 
 
+def test_moe_validation():
+    w = tp.tp_moe_weights(A, A + 64 * MB, A + 128 * MB, A + 1024 * MB, A + 2048 * MB)
+    need = tp.tp_moe_workspace_bytes(16, 4096, 8, 7168, True)
+    assert need > 16 * 8 * 7168 * 2
+
+    def f(weights=w, x=A + 3000 * MB, part=A + 3100 * MB, g=None, lg=None, m=16, H=4096, E=8, k=2, cols=7168,
+          eps=1e-5, ws=A + 3200 * MB, wsn=None):
+        return rejected(tp.lib.tp_moe_shard_forward(ctypes.byref(weights) if weights is not None else None, x, part,
+                                                    g, lg, m, H, E, k, cols, eps, ws, need if wsn is None else wsn,
+                                                    None))
+    assert f(weights=None) == "TP_ERR_NULL"
+    assert f(x=None) == "TP_ERR_NULL"
+    assert f(E=65) == "TP_ERR_SHAPE"
+    assert f(k=9) == "TP_ERR_SHAPE"
+    assert f(k=0) == "TP_ERR_SHAPE"
+    assert f(cols=7170) == "TP_ERR_ALIGN"
+    assert f(part=A + 3000 * MB + 256) == "TP_ERR_ALIAS"
+    assert f(wsn=need - 256) == "TP_ERR_WORKSPACE"
+    assert f(g=A + 5) == "TP_ERR_ALIGN"
+    assert tp.tp_moe_workspace_bytes(16, 4096, 0, 7168, True) == 0
+
+
 def attn(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=16, qh=8, kvh=1, d=128, cap=8192, L=8192,
          dt=tp.TP_BF16, ws=None, wsn=0):
     return rejected(tp.lib.tp_decode_attention(q, k, v, out, B, qh, kvh, d, cap, L, dt, ws, wsn, None))

@@ -342,6 +342,71 @@ def test_full_layer_prefill_bf16(case):
     check("layer output", host(out), ref["out"].reshape(M, H), TOL["bf16"])
 
 
+MOE_CASES = [
+    # hidden, intermediate (per expert), experts, top_k, t, tokens
+    (512, 1024, 4, 2, 2, 5),
+    (1024, 2816, 8, 2, 2, 16),
+    (1024, 2048, 8, 1, 4, 3),
+]
+
+
+def moe_inputs(seed, H, I, E, m):
+    x = W.to_bf16(W.normal(seed, W.X, (m, H)))
+    gamma = W.gamma(seed, W.GAMMA2, H, "random", "bf16")
+    w_router = W.to_bf16(W.normal(seed, W.ATTN_IN, (H, E), 0.02))
+    experts = []
+    for e in range(E):
+        mi = W.mlp_inputs(seed * 100 + e, H, I, 1, "bf16")
+        experts.append((mi["w_gate"], mi["w_up"], mi["w_down"]))
+    return x, gamma, w_router, experts
+
+
+def moe_rank_phys(experts, p):
+    """A rank's stacked expert weights: gate/up [E * cols, H], down [H, E * cols]."""
+    b, c = p.inter_begin, p.inter_cols
+    wg = np.concatenate([phys(g[:, b:b + c]) for g, _, _ in experts], axis=0)
+    wu = np.concatenate([phys(u[:, b:b + c]) for _, u, _ in experts], axis=0)
+    wd = np.concatenate([phys(d[b:b + c, :]) for _, _, d in experts], axis=1)
+    return wg, wu, wd
+
+
+@pytest.mark.parametrize("case", MOE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_moe_shard_bf16(case):
+    H, I, E, k, t, m = case
+    x, gamma, w_router, experts = moe_inputs(70 + E + k, H, I, E, m)
+    desc = tp.make_desc(H, I)
+    xd, gd, rd = dev(x, "bf16"), dev(gamma, "bf16"), dev(phys(w_router), "bf16")
+    parts, gates, logits, plans = [], [], [], []
+    for r in range(t):
+        p = tp.tp_shard_plan(desc, t, r)
+        wg, wu, wd = moe_rank_phys(experts, p)
+        w = {"norm": gd, "w_router": rd, "w_gate": dev(wg, "bf16"), "w_up": dev(wu, "bf16"),
+             "w_down": dev(wd, "bf16")}
+        part = empty((m, H), torch.float32)
+        g = empty((m, E), torch.float32)
+        lg = empty((m, E), torch.float32)
+        tp.tp_moe_shard_forward(w, xd, part, E, k, p.inter_cols, gates=g, logits=lg)
+        parts.append(part); gates.append(g); logits.append(lg); plans.append(p)
+    out = empty((m, H), torch.float32)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    ref = L.moe_block(x, gamma, w_router, experts, k)
+    lg0 = host(logits[0])
+    check("router logits", lg0, ref["logits"], TOL["bf16"])
+    for r in range(1, t):
+        assert np.array_equal(host(gates[r]), host(gates[0])), "ranks disagree on the routing"
+    # the routing decision taken in the kernel's precision: top-k of the GPU's logits
+    g_ref = L.moe_route(lg0, k)
+    g0 = host(gates[0])
+    assert np.array_equal(g0 > 0, g_ref > 0), "top-k selection differs"
+    assert np.max(np.abs(g0 - g_ref)) < 1e-5
+    for r, p in enumerate(plans):
+        sr = S.rank_moe(x, gamma, w_router, experts, g0, tp.plan_dict(p))
+        check(f"rank{r} MoE partial", host(parts[r]), sr["partial"], TOL["bf16"])
+    yref = L.moe_block(x, gamma, w_router, experts, k, gates=g0)["y"]
+    check(f"sum of {t} MoE partials", host(out), yref, TOL["bf16"])
+
+
 # ---------------------------------------------------------------- ragged and edge shapes
 
 LINEAR_CASES = [
