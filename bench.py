@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mlp_decode",
                     choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill",
-                             "layer_prefill"])
+                             "layer_prefill", "moe_decode"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of the timed step (default: the workload's)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true")
@@ -103,7 +103,7 @@ def main():
     torch.cuda.set_device(0)
     bench = {"mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
              "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill,
-             "layer_prefill": bench_layer_prefill}[args.workload]
+             "layer_prefill": bench_layer_prefill, "moe_decode": bench_moe_decode}[args.workload]
     if args.calibrate_copy:
         calibrate_copy(torch)
     res = bench(ctx)
@@ -832,6 +832,79 @@ def bench_layer_prefill(ctx):
                                "sample": f"{n} float64 passes of rank 0's shard (attention and MLP stages) over "
                                          f"the last {n_tail} tokens of sequence 0 (each sees about {kv_len} keys), "
                                          f"{el:.1f} s"}
+    return res
+
+
+
+def bench_moe_decode(ctx):
+    torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
+    wl = W.WORKLOADS[8]
+    H, I, t, E, k = wl.hidden, wl.intermediate, wl.t, W.MOE_EXPERTS, W.MOE_TOP_K
+    M = args.tokens or wl.tokens[0]
+    log(f"[bench] drawing {wl.name}")
+    inp = W.moe_inputs(8, H, I, E, M, "bf16", progress=lambda e: log(f"[bench]   expert {e} drawn"))
+    desc = tp.make_desc(H, I)
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    cols = plans[0].inter_cols
+    gam, rtr = ctx.dev(inp["gamma"]), ctx.dev(ctx.phys(inp["w_router"]))
+    ranks = []
+    for p in plans:
+        b, c = p.inter_begin, p.inter_cols
+        log(f"[bench] staging rank {p.rank}'s stacked experts")
+        ranks.append({"norm": gam, "w_router": rtr,
+                      "w_gate": ctx.dev(np.concatenate([ctx.phys(g[:, b:b + c]) for g, _, _ in inp["experts"]])),
+                      "w_up": ctx.dev(np.concatenate([ctx.phys(u[:, b:b + c]) for _, u, _ in inp["experts"]])),
+                      "w_down": ctx.dev(np.concatenate([ctx.phys(d[b:b + c]) for _, _, d in inp["experts"]],
+                                                       axis=1))})
+    x = ctx.dev(inp["x"])
+    ws = tp.workspace(max(tp.tp_moe_workspace_bytes(M, H, E, cols, True),
+                          tp.tp_linear_workspace_bytes(M, H, E * cols, tp.TP_BF16, tp.TP_LINEAR_SWIGLU)))
+    parts = [torch.empty(M, H, device="cuda") for _ in range(t)]
+    out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    a_out = torch.empty(M, E * cols, dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        for r in range(t):
+            tp.tp_moe_shard_forward(ranks[r], x, parts[r], E, k, cols, eps=wl.eps, ws=ws)
+        tp.tp_partial_sum(parts, out)
+
+    def gateup(i):
+        rw = ranks[i % t]
+        tp.tp_column_linear(x, rw["w_gate"], a_out, w_up=rw["w_up"], ws=ws)
+
+    for i in range(4 * t):
+        gateup(i)
+    g_t = event_time_ms(torch, gateup, 8 * t)
+    g_bytes = 2 * E * cols * H * 2 + M * H * 2 + M * E * cols * 2
+    log(f"[bench] stacked expert gate/up {g_t[0] * 1e3:.1f} us ({g_bytes / (g_t[0] * 1e-3) / 1e9:.0f} GB/s)")
+    total_ms = time_steps(ctx, step, 1)
+    ms_step = total_ms / args.steps
+    rank_bytes = 3 * E * cols * H * 2 + E * H * 2
+    extra = {
+        "step_GBps": t * rank_bytes / (ms_step * 1e-3) / 1e9,
+        "per_rank": {"weight_bytes": rank_bytes, "gateup_us": g_t[0] * 1e3, "experts": E, "top_k": k},
+        "roofline": roofline_hbm(projection_kernel(M) + ": every expert's gate/up + SwiGLU (stacked), one rank shard",
+                                 f"gateup_moe_decode_m{M}", g_bytes, *g_t),
+    }
+    config = {"workload": f"Mixtral-8x7B-shaped MoE FFN decode block, all t={t} rank shards + on-device sum",
+              "hidden": H, "intermediate": I, "experts": E, "top_k": k, "t": t, "tokens": M}
+    res = result(ctx, M * args.steps / (total_ms * 1e-3), "tokens/s", ms_step, config, extra)
+    if not args.no_cpu:
+        from oracle import layer as L
+        from oracle import sharded as S
+        n_tok = 4
+        xs = inp["x"][:n_tok]
+        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
+
+        def one_rank():
+            gates = L.moe_route(L.linear(L.rmsnorm(xs, inp["gamma"], wl.eps), inp["w_router"]), k)
+            S.rank_moe(xs, inp["gamma"], inp["w_router"], inp["experts"], gates, tp.plan_dict(plans[0]), wl.eps)
+
+        n, el = repeat_for(args.cpu_seconds, one_rank)
+        res["cpu_baseline"] = {"value": n_tok * n / (el * t), "unit": "tokens/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} float64 passes of rank 0's MoE shard (router + all {E} experts) over "
+                                         f"{n_tok} of the {M} tokens, {el:.1f} s; scaled by 1/{t} for the {t} ranks"}
     return res
 
 

@@ -110,6 +110,9 @@ WORKLOADS: Dict[int, Workload] = {
     6: Workload(6, "70B-shaped causal prefill attention shard, bf16, t=8, batch 2 x 2048 tokens",
                 "bf16", hidden=8192, intermediate=0, t=8, tokens=(4096,), n_q_heads=64, n_kv_heads=8,
                 head_dim=128, kv_len=2048),
+    8: Workload(8, "Mixtral-8x7B-shaped MoE FFN decode shard, bf16, hidden 4096, 8 experts x intermediate "
+                   "14336, top-2, t=2, 16 tokens", "bf16", hidden=4096, intermediate=14336, t=2, tokens=(16,),
+                norm=True),
     7: Workload(7, "70B-shaped full layer prefill shard, bf16, t=8, batch 2 x 2048 tokens",
                 "bf16", hidden=8192, intermediate=28672, t=8, tokens=(4096,), n_q_heads=64, n_kv_heads=8,
                 head_dim=128, kv_len=2048, norm=True),
@@ -171,3 +174,26 @@ def prefill_attention_inputs(workload_id: int, batch: int, seq: int, n_q: int, n
         "k_cache": storage_round(normal(workload_id, K_CACHE, (batch, n_kv, capacity, d)), dtype),
         "v_cache": storage_round(normal(workload_id, V_CACHE, (batch, n_kv, capacity, d)), dtype),
     }
+
+
+MOE_EXPERTS, MOE_TOP_K = 8, 2       # the Mixtral-8x7B routing of workload 8
+
+
+def moe_inputs(workload_id: int, hidden: int, intermediate: int, n_experts: int, m: int,
+               dtype: str, progress=None) -> Dict[str, object]:
+    """x [m, H], gamma [H] (1 + 0.1 N(0,1)), router [H, E] N(0, 0.02), and per expert the logical
+    (w_gate [H, I], w_up [H, I], w_down [I, H]) drawn as an MLP of its own seed. ``progress(e)`` is
+    called after each expert is drawn."""
+    experts = []
+    for e in range(n_experts):
+        mi = mlp_inputs(workload_id * 100 + e, hidden, intermediate, 1, dtype)
+        experts.append((mi["w_gate"], mi["w_up"], mi["w_down"]))
+        if progress is not None:
+            progress(e)
+    return {
+        "x": storage_round(normal(workload_id, X, (m, hidden)), dtype),
+        "gamma": gamma(workload_id, GAMMA2, hidden, "random", dtype),
+        "w_router": storage_round(normal(workload_id, ATTN_IN, (hidden, n_experts), WEIGHT_STD), dtype),
+        "experts": experts,
+    }
+
