@@ -105,7 +105,7 @@ typedef struct tp_rank_plan {
     int64_t o_rows;                   /* q_heads * d: the K of this rank's W_o */
     int64_t weight_elems;             /* this rank's projection weights, one layer (norms excluded) */
     int64_t kv_elems_per_seq_all_layers; /* 2 L n_kv d S: one sequence, all layers, unsharded */
-    int64_t kv_bytes_rank;            /* 2 L n_kv d S bytes_per_elem B / t */
+    int64_t kv_bytes_rank;            /* 2 L n_kv d S bytes_per_elem B / t (/ n_kv when replicated) */
 } tp_rank_plan;
 
 /*
@@ -115,8 +115,11 @@ typedef struct tp_rank_plan {
  * Fundamentals", section "Memory Overhead and Communication Bottlenecks":
  * weights and KV cache per GPU are the totals divided by t).
  * Host only; touches no device. Intermediate columns follow the same
- * contiguous rank order as heads; t must divide n_q, n_kv and I
- * (TP_ERR_INDIVISIBLE), 1 <= t <= 8 and 0 <= rank < t (TP_ERR_RANK).
+ * contiguous rank order as heads; t must divide n_q and I, and either divide
+ * n_kv or be a multiple of it (TP_ERR_INDIVISIBLE); 1 <= t <= 8 and
+ * 0 <= rank < t (TP_ERR_RANK). When t > n_kv every rank keeps a copy of the
+ * one kv head its q heads read (kv_heads = 1, head rank / (t / n_kv)), and
+ * its KV cache is that head's: the total divided by n_kv, not by t.
  */
 tp_status tp_shard_plan(const tp_model_desc* desc, int32_t t, int32_t rank, tp_rank_plan* out);
 

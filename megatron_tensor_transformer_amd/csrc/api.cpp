@@ -158,15 +158,19 @@ tp_status plan_impl(const tp_model_desc* d, int32_t t, int32_t rank, tp_rank_pla
         if (d->n_q_heads % d->n_kv_heads)
             return fail(TP_ERR_INDIVISIBLE, "n_q_heads=%d is not a multiple of n_kv_heads=%d", d->n_q_heads,
                         d->n_kv_heads);
-        if (d->n_q_heads % t || d->n_kv_heads % t)
-            return fail(TP_ERR_INDIVISIBLE, "t=%d must divide n_q_heads=%d and n_kv_heads=%d; pick t from the "
-                        "common divisors", t, d->n_q_heads, d->n_kv_heads);
+        if (d->n_q_heads % t)
+            return fail(TP_ERR_INDIVISIBLE, "t=%d must divide n_q_heads=%d", t, d->n_q_heads);
+        if (d->n_kv_heads % t && t % d->n_kv_heads)
+            return fail(TP_ERR_INDIVISIBLE, "t=%d must divide n_kv_heads=%d or be a multiple of it (then each "
+                        "rank keeps a copy of the kv head its q heads read)", t, d->n_kv_heads);
     }
     if (d->intermediate % t)
         return fail(TP_ERR_INDIVISIBLE, "t=%d must divide intermediate=%lld", t, (long long)d->intermediate);
     const int64_t H = d->hidden;
     const int32_t q_r = attn ? d->n_q_heads / t : 0;
-    const int32_t kv_r = attn ? d->n_kv_heads / t : 0;
+    // t > n_kv: every rank keeps the one kv head its q heads read (t / n_kv copies of each).
+    const bool replicate = attn && (d->n_kv_heads % t) != 0;
+    const int32_t kv_r = attn ? (replicate ? 1 : d->n_kv_heads / t) : 0;
     const int64_t hd = attn ? d->head_dim : 0;
     const int64_t i_r = d->intermediate / t;
     tp_rank_plan p{};
@@ -174,7 +178,7 @@ tp_status plan_impl(const tp_model_desc* d, int32_t t, int32_t rank, tp_rank_pla
     p.rank = rank;
     p.q_head_begin = rank * q_r;
     p.q_heads = q_r;
-    p.kv_head_begin = rank * kv_r;
+    p.kv_head_begin = replicate ? rank / (t / d->n_kv_heads) : rank * kv_r;
     p.kv_heads = kv_r;
     p.inter_begin = rank * i_r;
     p.inter_cols = i_r;
@@ -185,7 +189,7 @@ tp_status plan_impl(const tp_model_desc* d, int32_t t, int32_t rank, tp_rank_pla
         const int64_t per_seq = 2 * (int64_t)d->n_layers * d->n_kv_heads * hd * d->seq_len;
         const int64_t total = per_seq * d->bytes_per_elem * d->batch;
         p.kv_elems_per_seq_all_layers = per_seq;
-        p.kv_bytes_rank = total / t;
+        p.kv_bytes_rank = replicate ? total / d->n_kv_heads : total / t;   // replicated: one head's cache
     }
     *out = p;
     return ok();

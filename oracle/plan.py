@@ -87,27 +87,37 @@ def rank_plan(desc: ModelDesc, t: int, rank: int) -> dict:
             raise PlanError("SHAPE", "attention needs n_kv_heads > 0 and head_dim > 0")
         if desc.n_q_heads % desc.n_kv_heads:
             raise PlanError("INDIVISIBLE", "n_q_heads must be a multiple of n_kv_heads")
-        if desc.n_q_heads % t or desc.n_kv_heads % t:
-            raise PlanError("INDIVISIBLE", f"t={t} must divide q heads {desc.n_q_heads} "
-                                           f"and kv heads {desc.n_kv_heads}")
+        if desc.n_q_heads % t:
+            raise PlanError("INDIVISIBLE", f"t={t} must divide q heads {desc.n_q_heads}")
+        if desc.n_kv_heads % t and t % desc.n_kv_heads:
+            raise PlanError("INDIVISIBLE", f"t={t} must divide, or be a multiple of, kv heads {desc.n_kv_heads}")
     if desc.intermediate % t:
         raise PlanError("INDIVISIBLE", f"t={t} must divide intermediate {desc.intermediate}")
 
     q_r = desc.n_q_heads // t if has_attn else 0
-    kv_r = desc.n_kv_heads // t if has_attn else 0
+    # t > n_kv: every rank keeps the one kv head its q heads read (t / n_kv copies of each).
+    replicate = has_attn and desc.n_kv_heads % t != 0
+    kv_r = (1 if replicate else desc.n_kv_heads // t) if has_attn else 0
+    kv_begin = (rank // (t // desc.n_kv_heads) if replicate else rank * kv_r) if has_attn else 0
     i_r = desc.intermediate // t
     d = desc.head_dim if has_attn else 0
     H = desc.hidden
     weight_elems = H * (q_r + 2 * kv_r) * d + q_r * d * H + 3 * H * i_r
     kv_seq = kv_elements_per_sequence(desc.n_layers, desc.n_kv_heads, d, desc.seq_len) if has_attn else 0
-    kv_rank = (kv_bytes_per_gpu(desc.n_layers, desc.n_kv_heads, d, desc.seq_len,
-                                desc.bytes_per_elem, desc.batch, t) if has_attn else 0)
+    if not has_attn:
+        kv_rank = 0
+    elif replicate:
+        # one kv head's cache: the total divided by n_kv, not by t
+        kv_rank = kv_elements_per_sequence(desc.n_layers, 1, d, desc.seq_len) * desc.bytes_per_elem * desc.batch
+    else:
+        kv_rank = kv_bytes_per_gpu(desc.n_layers, desc.n_kv_heads, d, desc.seq_len, desc.bytes_per_elem,
+                                   desc.batch, t)
     return {
         "t": t,
         "rank": rank,
         "q_head_begin": rank * q_r,
         "q_heads": q_r,
-        "kv_head_begin": rank * kv_r,
+        "kv_head_begin": kv_begin,
         "kv_heads": kv_r,
         "inter_begin": rank * i_r,
         "inter_cols": i_r,

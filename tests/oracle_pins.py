@@ -112,7 +112,8 @@ def pin_plan_errors(rank_plan, ModelDesc, PlanError):
         (ModelDesc(hidden=8, intermediate=9), 2, 0, "INDIVISIBLE"),
         (ModelDesc(hidden=8, n_q_heads=64, n_kv_heads=8, head_dim=4), 3, 0, "INDIVISIBLE"),
         (ModelDesc(hidden=8, n_q_heads=6, n_kv_heads=4, head_dim=4), 2, 0, "INDIVISIBLE"),
-        (ModelDesc(hidden=8, n_q_heads=8, n_kv_heads=2, head_dim=4), 4, 0, "INDIVISIBLE"),
+        (ModelDesc(hidden=8, n_q_heads=12, n_kv_heads=4, head_dim=4), 6, 0, "INDIVISIBLE"),
+        (ModelDesc(hidden=8, n_q_heads=8, n_kv_heads=2, head_dim=4), 3, 0, "INDIVISIBLE"),
         (ModelDesc(hidden=0, intermediate=8), 1, 0, "SHAPE"),
         (ModelDesc(hidden=8, n_q_heads=8, n_kv_heads=0, head_dim=4), 1, 0, "SHAPE"),
     ]
@@ -340,7 +341,7 @@ def small_layer(seed=41, B=3, H=32, I=64, n_q=8, n_kv=8, d=4, cap=10):
 
 
 def pin_sharded_layer(sharded_layer, layer):
-    for n_q, n_kv in [(8, 8), (16, 8)]:
+    for n_q, n_kv in [(8, 8), (16, 8), (8, 2)]:          # (8, 2) at t = 4, 8: kv heads replicated
         x, w, K, V = small_layer(n_q=n_q, n_kv=n_kv)
         for residual in (True, False):
             ref = layer(x, w, K, V, 7, n_q, n_kv, 4, 1e-5, residual)
@@ -533,3 +534,19 @@ def pin_rank_moe(rank_moe, moe_block, rank_plan, ModelDesc):
         parts = [rank_moe(x, gamma, w_router, experts, ref["gates"], rank_plan(desc, t, r), 1e-5)["partial"]
                  for r in range(t)]
         assert relerr(sum(parts), ref["y"]) < 1e-12, t
+
+
+def pin_kv_replication(rank_plan, ModelDesc):
+    """t > n_kv: each rank holds the one kv head its q heads read; its KV cache is one head's."""
+    d = ModelDesc(hidden=32, intermediate=64, n_q_heads=8, n_kv_heads=2, head_dim=4, n_layers=2, seq_len=10,
+                  batch=3, bytes_per_elem=2)
+    for t, heads in [(4, [0, 0, 1, 1]), (8, [0, 0, 0, 0, 1, 1, 1, 1])]:
+        for r in range(t):
+            p = rank_plan(d, t, r)
+            assert p["kv_heads"] == 1 and p["kv_head_begin"] == heads[r], (t, r)
+            group = 8 // 2
+            assert all(h // group == p["kv_head_begin"]
+                       for h in range(p["q_head_begin"], p["q_head_begin"] + p["q_heads"]))
+            assert p["qkv_cols"] == (8 // t + 2) * 4
+            assert p["kv_bytes_rank"] == 2 * 2 * 1 * 4 * 10 * 2 * 3       # 2 (k, v) x layers x 1 head x d x seq x bytes x batch
+

@@ -63,6 +63,9 @@ def test_plan_matches_oracle():
                         seq_len=4096, batch=4),
         oplan.ModelDesc(hidden=256, intermediate=1024),
         oplan.ModelDesc(hidden=96, intermediate=48, n_q_heads=12, n_kv_heads=6, head_dim=8, seq_len=7, batch=3),
+        oplan.ModelDesc(hidden=4096, intermediate=14336, n_q_heads=32, n_kv_heads=2, head_dim=128, n_layers=4,
+                        seq_len=64, batch=2, bytes_per_elem=2),             # t = 4, 8: kv heads replicated
+        oplan.ModelDesc(hidden=64, intermediate=64, n_q_heads=8, n_kv_heads=1, head_dim=8, seq_len=5, batch=1),
     ]
     for d, t in itertools.product(shapes, range(1, 9)):
         for r in range(t):

@@ -151,6 +151,14 @@ def _rank_moe_no_gates(x, gamma, w_router, experts, gates, p, eps=1e-5):
     return _orig_rank_moe(x, gamma, w_router, experts, (np.asarray(gates) > 0).astype(float), p, eps)
 
 
+def _plan_replicate_round_robin(desc, t, rank):
+    # t > n_kv: assigns kv heads to ranks round robin instead of by q-head group
+    p = dict(_orig_rank_plan(desc, t, rank))
+    if desc.n_q_heads and desc.n_kv_heads % t:
+        p["kv_head_begin"] = rank % desc.n_kv_heads
+    return p
+
+
 def _plan_shift_heads(desc, t, rank):
     p = dict(_orig_rank_plan(desc, t, rank))
     p["q_head_begin"] = rank * p["q_heads"] + (1 if rank and p["q_heads"] > 1 else 0)
@@ -249,6 +257,7 @@ MUTATIONS = {
     "weights_not_divided": (plan, "weight_bytes_per_gpu", lambda total, t: total, _all_plan_pins),
     "heads_shifted": (plan, "rank_plan", _plan_shift_heads, _all_plan_pins),
     "inter_block_swapped": (plan, "rank_plan", _plan_wrong_inter, _all_sharded_pins),
+    "kv_replicated_round_robin": (plan, "rank_plan", _plan_replicate_round_robin, _all_sharded_pins),
 }
 
 

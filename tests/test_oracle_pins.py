@@ -115,3 +115,8 @@ def test_moe_vs_naive():
 
 def test_rank_moe():
     P.pin_rank_moe(S.rank_moe, L.moe_block, plan.rank_plan, plan.ModelDesc)
+
+
+def test_kv_replication():
+    P.pin_kv_replication(plan.rank_plan, plan.ModelDesc)
+

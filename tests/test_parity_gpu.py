@@ -277,6 +277,8 @@ PREFILL_LAYER_CASES = [
     (512, 1024, 8, 2, 64, 2, 2, 4, 9, 16),           # 8 rows: the projections take the GEMV path
     (1024, 2816, 16, 4, 64, 4, 2, 96, 130, 160),     # MFMA GEMMs, a chunk after a cached prefix
     (1024, 2048, 64, 8, 128, 8, 2, 200, 200, 256),   # 70B heads at t=8 (8 q heads on 1 kv head), a prompt
+    (512, 1024, 8, 2, 64, 4, 3, 1, 20, 32),          # t > n_kv: kv heads replicated; a decode step
+    (512, 1024, 8, 1, 64, 8, 2, 33, 33, 40),         # t = 8 on one kv head (8 copies), a prompt
 ]
 
 
