@@ -191,7 +191,10 @@ __global__ __launch_bounds__(SK_NW * 64) void gemv_mfma_kernel(GemvDev d) {
 // the epilogue.
 template <int EPI, bool NORM>
 __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
-    constexpr int NT = 256, PER = SK_MT * SK_RPT / NT, UNR = 8;
+    // The plan splits K about four ways, so one batch of loads usually
+    // covers every slice; the squared-sum slices of a fused RMSNorm travel in
+    // the same batch.
+    constexpr int NT = 256, PER = SK_MT * SK_RPT / NT, UNR = 4;
     __shared__ float res[SK_MT * SK_RPT];
     __shared__ float ssl[SK_MT];
     const int tid = threadIdx.x, tile = blockIdx.x, mb = d.mb0 + blockIdx.z;
@@ -200,30 +203,32 @@ __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
     const int S = d.splits;
     const int tile_id = blockIdx.z * d.n_tiles + tile;
     const float* base = d.part + (size_t)tile_id * S * (SK_MT * SK_RPT);
+    const float* sqb = NORM ? d.ssq + (size_t)tile_id * S * SK_MT + min(tid, mvalid - 1) : nullptr;
     const int live = mvalid * SK_RPT;
-    float acc[PER];
+    float acc[PER], sq = 0.f;
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] = 0.f;
     for (int sp0 = 0; sp0 < S; sp0 += UNR) {
-        float v[PER][UNR];
+        float v[PER][UNR], q[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+            if (NORM) q[u] = sqb[(size_t)min(sp0 + u, S - 1) * SK_MT];
 #pragma unroll
         for (int p = 0; p < PER; ++p)
 #pragma unroll
             for (int u = 0; u < UNR; ++u)
                 v[p][u] = base[(size_t)min(sp0 + u, S - 1) * (SK_MT * SK_RPT) + min(tid + p * NT, live - 1)];
 #pragma unroll
-        for (int p = 0; p < PER; ++p)
+        for (int u = 0; u < UNR; ++u)
+            if (sp0 + u < S) {
+                if (NORM) sq += q[u];
 #pragma unroll
-            for (int u = 0; u < UNR; ++u)
-                if (sp0 + u < S) acc[p] += v[p][u];
+                for (int p = 0; p < PER; ++p) acc[p] += v[p][u];
+            }
     }
 #pragma unroll
     for (int p = 0; p < PER; ++p) res[tid + p * NT] = acc[p];
-    if (NORM && tid < mvalid) {
-        float t = 0.f;
-        for (int sp = 0; sp < S; ++sp) t += d.ssq[((size_t)tile_id * S + sp) * SK_MT + tid];
-        ssl[tid] = t;
-    }
+    if (NORM && tid < mvalid) ssl[tid] = sq;
     __syncthreads();
     gemv_epilogue<uint16_t, SK_MT, SK_RPT, EPI, NORM, NT>(d.a, res, ssl, tile, m0, mvalid);
 }
