@@ -44,7 +44,8 @@ struct GemvArgs {
 struct GemvPlan {
     int mfma;      // 1: matrix-core kernel (bf16, 16-token blocks), 0: v_dot2 / fma kernel
     int mt;        // tokens per block (1, 2, 4, 8, 16)
-    int nw;        // waves per workgroup (1 or 4)
+    int nw;        // waves per workgroup
+    int rg, ks;    // matrix-core kernel: waves per K range (16 rows each), K ranges per workgroup
     int mblocks;   // ceil(m / mt)
     int mb_per_launch;  // m-blocks per launch, so a launch's tiles fit the counter header
     int rows_per_tile;  // weight rows a workgroup covers
