@@ -113,6 +113,23 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_base) {
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Buffer view of one key block of a head's K or V rows: the block's first
+// row as base and its rows below kv_len as the range. Reads past the range
+// return zeros, so keys past kv_len need no clamping (their scores are
+// masked), and the per-lane offsets stay the same from block to block.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t key_block(const uint16_t* rows, int key0, int nvalid, int d) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rows + (size_t)key0 * d), (short)0,
+                                             min(nvalid, PF_BK) * d * 2, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned off, uint16_t* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ uint4 load_u4_buf(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    typedef unsigned u4v __attribute__((ext_vector_type(4)));
+    const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int D, int GQ>
 __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     constexpr int DC = D / 8;                      // 16-byte chunks per row
@@ -153,32 +170,36 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     // K block: wave transfer i covers tile bytes [(i * 8 + wave) KB, + 1 KB),
     // lane L the 16 bytes at L * 16 in it: row e / D, physical chunk
     // (e % D) / 8, which holds logical chunk k_chunk(row, physical).
-    int klast = kv_len - 1;                         // last valid key; loads clamp to it
-    int krow[KDMA], kcol[KDMA];
+    unsigned koff[KDMA];                            // byte offsets within a key block
 #pragma unroll
     for (int i = 0; i < KDMA; ++i) {
         const int e = (i * 8 + wave) * 512 + lane * 8;
-        krow[i] = e / D;
-        kcol[i] = k_chunk<D>(krow[i], (e % D) / 8) * 8;
+        const int r = e / D;
+        koff[i] = (unsigned)(r * D + k_chunk<D>(r, (e % D) / 8) * 8) * 2u;
     }
     auto load_k = [&](int kb, uint16_t* kdst) {
         const int key0 = kb * PF_BK;
+        const __amdgpu_buffer_rsrc_t r = key_block(kbase, key0, kv_len - key0, D);
 #pragma unroll
-        for (int i = 0; i < KDMA; ++i)
-            dma16(kbase + (size_t)min(key0 + krow[i], klast) * D + kcol[i], kdst + (i * 8 + wave) * 512);
+        for (int i = 0; i < KDMA; ++i) dma16_buf(r, koff[i], kdst + (i * 8 + wave) * 512);
     };
     // V unit u -> keys 2 (u / DC) and 2 (u / DC) + 1, chunk u % DC, through
-    // registers (the tile is stored transposed). Keys past kv_len are
-    // clamped; their scores are masked.
+    // registers (the tile is stored transposed). Keys past kv_len read as
+    // zeros; their scores are masked.
     uint4 va[VU], vb[VU];
+    unsigned voff[VU];
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+        const int u = j * PF_NT + tid;
+        voff[j] = (unsigned)(2 * (u / DC) * D + (u % DC) * 8) * 2u;
+    }
     auto load_v = [&](int kb) {
         const int key0 = kb * PF_BK;
+        const __amdgpu_buffer_rsrc_t r = key_block(vbase, key0, kv_len - key0, D);
 #pragma unroll
         for (int j = 0; j < VU; ++j) {
-            const int u = j * PF_NT + tid;
-            const int key = key0 + 2 * (u / DC);
-            va[j] = load_u4(vbase + (size_t)min(key, klast) * D + (u % DC) * 8);
-            vb[j] = load_u4(vbase + (size_t)min(key + 1, klast) * D + (u % DC) * 8);
+            va[j] = load_u4_buf(r, voff[j]);
+            vb[j] = load_u4_buf(r, voff[j] + D * 2);
         }
     };
     auto store_v = [&](uint16_t* vt) {
@@ -205,9 +226,6 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     for (int ph = 0; ph < 2; ++ph) {
         const int qblk = ph == 0 ? pair : nqb - 1 - pair;
         if (ph == 1 && qblk == pair) break;
-        // Opaque per query block: keeps the compiler from hoisting the first
-        // block's load addresses out of this loop and holding them throughout.
-        asm volatile("" : "+s"(klast));
         const int i0 = qblk * TOK;                  // first token of the query block
         const int ilast = min(i0 + TOK, S) - 1;
         const int nblk = (p0 + ilast) / PF_BK + 1;  // blocks up to the last token's position
