@@ -150,7 +150,8 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     constexpr int BUF = KTILE + VTILE;
     __shared__ __align__(16) uint16_t smem[2 * BUF];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
     const int rg = wave & 1, kq = wave >> 1;      // row group, key quarter
     const int col = lane & 15, kg = lane >> 4;
     const int heads = a.kv_heads * a.batch;
