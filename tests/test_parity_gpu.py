@@ -452,6 +452,47 @@ def test_linear_shapes(case, mode):
     check(f"{mode} m={m} k={k} n={n} {dt}", host(y), ref, TOL[dt])
 
 
+def _random_linear_cases(n_cases=24, seed=2024):
+    """Seeded shapes across both decode projection kernels and the GEMM: m 1-40, k a multiple of 8 up
+    to 9000, n up to 9000 (work kept small enough for the float64 reference)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n_cases:
+        m = int(rng.choice([1, 3, 5, 8, 12, 16, 16, 16, 20, 40]))
+        k = 8 * int(rng.integers(1, 1126))
+        n = int(rng.integers(1, 9001))
+        if m * k * n > 1.5e8:
+            continue
+        mode = ["col", "col_norm", "swiglu", "swiglu_norm", "row"][len(cases) % 5]
+        cases.append((m, k, n, mode))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_linear_cases(), ids=lambda c: "x".join(map(str, c)))
+def test_linear_random_shapes(case):
+    m, k, n, mode = case
+    seed = 700 + (13 * m + 5 * k + n) % 1000
+    x = W.to_bf16(W.normal(seed, 0, (m, k)))
+    wp = W.to_bf16(W.normal(seed, 1, (n, k), 0.05))
+    wu = W.to_bf16(W.normal(seed, 2, (n, k), 0.05))
+    gam = W.to_bf16(W.normal(seed, 3, (k,), 0.1, 1.0))
+    norm = mode.endswith("norm")
+    u = L.rmsnorm(x, gam, 1e-5) if norm else x.astype(np.float64)
+    if mode.startswith("swiglu"):
+        ref = L.swiglu(L.linear(u, wp.T), L.linear(u, wu.T))
+    else:
+        ref = L.linear(u, wp.T)
+    tx, tw, twu, tg = dev(x, "bf16"), dev(wp, "bf16"), dev(wu, "bf16"), dev(gam, "bf16")
+    if mode == "row":
+        y = empty((m, n), torch.float32)
+        tp.tp_row_linear_partial(tx, tw, y)
+    else:
+        y = empty((m, n), torch.bfloat16)
+        tp.tp_column_linear(tx, tw, y, w_up=twu if mode.startswith("swiglu") else None, gamma=tg if norm else None)
+    torch.cuda.synchronize()
+    check(f"{mode} m={m} k={k} n={n}", host(y), ref, TOL["bf16"])
+
+
 ATTN_CASES = [
     # batch, q_heads, kv_heads, head_dim, capacity, kv_len
     (1, 1, 1, 64, 1, 1), (2, 4, 2, 128, 300, 257), (3, 16, 1, 128, 1000, 1000), (4, 8, 8, 64, 5000, 4097),
@@ -484,6 +525,7 @@ PREFILL_CASES = [
     (2, 8, 1, 128, 3000, 200, 2900),   # 70B t=8 head shard, chunked prefill
     (1, 4, 4, 128, 64, 64, 64),        # GQ 1 with several kv heads, one key block
     (2, 8, 1, 128, 2048, 2048, 2048),  # 70B t=8 head shard at batch 2 x 2048 tokens
+    (1, 8, 1, 128, 1000, 128, 640),    # whole key blocks only, cache longer than kv_len
 ]
 
 
@@ -499,6 +541,24 @@ def test_prefill_attention_shapes(case):
     tp.tp_prefill_attention(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, kv_len, qh)
     torch.cuda.synchronize()
     check(f"prefill attention {case}", host(out), ref, TOL["bf16"])
+
+
+def test_prefill_ignores_cache_past_kv_len():
+    """Cache rows at kv_len and beyond hold NaN: no key or value past kv_len may reach the output."""
+    B, qh, kvh, d, cap, S, kv_len = 2, 8, 2, 128, 700, 150, 555
+    q = W.to_bf16(W.normal(43, 0, (B, S, qh * d)))
+    k = W.to_bf16(W.normal(43, 1, (B, kvh, cap, d)))
+    v = W.to_bf16(W.normal(43, 2, (B, kvh, cap, d)))
+    ref = L.prefill_attention(q, k, v, kv_len, qh, kvh, d)
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, kv_len:] = np.nan
+    vp[:, :, kv_len:] = np.nan
+    out = empty((B, S, qh * d), torch.bfloat16)
+    tp.tp_prefill_attention(dev(q, "bf16"), dev(kp, "bf16"), dev(vp, "bf16"), out, kv_len, qh)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isfinite(got).all(), "a row past kv_len reached the output"
+    check("prefill attention with NaN past kv_len", got, ref, TOL["bf16"])
 
 
 def test_prefill_last_token_matches_decode():
