@@ -514,6 +514,23 @@ def test_decode_attention_shapes(case):
     check(f"attention {case}", host(out), ref, TOL["bf16"])
 
 
+def test_decode_ignores_cache_past_kv_len():
+    """Cache rows at kv_len and beyond hold NaN: no key or value past kv_len may reach the output."""
+    B, qh, kvh, d, cap, kv_len = 3, 8, 2, 128, 5000, 4097
+    q = W.to_bf16(W.normal(44, 0, (B, qh * d)))
+    k = W.to_bf16(W.normal(44, 1, (B, kvh, cap, d)))
+    v = W.to_bf16(W.normal(44, 2, (B, kvh, cap, d)))
+    ref = L.decode_attention(q, k, v, kv_len, qh, kvh, d)
+    k[:, :, kv_len:] = np.nan
+    v[:, :, kv_len:] = np.nan
+    out = empty((B, qh * d), torch.bfloat16)
+    tp.tp_decode_attention(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, kv_len, qh)
+    torch.cuda.synchronize()
+    got = host(out)
+    assert np.isfinite(got).all(), "a row past kv_len reached the output"
+    check("decode attention with NaN past kv_len", got, ref, TOL["bf16"])
+
+
 PREFILL_CASES = [
     # batch, q_heads, kv_heads, head_dim, capacity, seq, kv_len
     (1, 1, 1, 64, 1, 1, 1),            # one token, one key
