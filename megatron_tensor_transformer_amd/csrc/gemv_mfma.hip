@@ -25,8 +25,9 @@
 //    rows hit distinct banks.
 //  - Wide projections: 8 waves per workgroup, 2 per K range (32 rows: for
 //    SwiGLU the gate and up rows of 16 outputs) and 4 K ranges, whose sums
-//    are added in LDS before the epilogue. One kernel, nothing in memory
-//    between the slices.
+//    are added in LDS before the epilogue (SwiGLU over 512 tiles or more: 2
+//    K ranges, 4 waves, three workgroups per compute unit). One kernel,
+//    nothing in memory between the slices.
 //  - Narrow projections (too few 32-row tiles to fill the chip): 4 waves
 //    share one K range of a 64-row tile and K is split over workgroups. Each
 //    writes its float32 slice with plain stores and a small merge kernel (one
@@ -285,18 +286,21 @@ GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
     p.lds_bytes = 0;                            // static LDS only
     const bool swi = epi == EPI_SWIGLU;
     const int64_t mb = p.mblocks;
-    // Wide projections: one workgroup of 8 waves per tile of 16 outputs
-    // (SwiGLU: 16 gate and 16 up rows; otherwise 32 rows), its K range split
-    // over 4 wave groups whose sums meet in LDS: no second kernel and no
-    // float32 slices in memory. Taken when that gives at least 128 (SwiGLU)
-    // or 192 workgroups; measured on replayed 8B MLP and 70B attention
-    // projection steps, narrower projections stream better as 64-row tiles
-    // split over workgroups.
+    // Wide projections: one workgroup per tile of 16 outputs (SwiGLU: 16
+    // gate and 16 up rows; otherwise 32 rows), its K range split over 4 wave
+    // groups of 2 waves (2 groups for SwiGLU over 512 tiles or more) whose
+    // sums meet in LDS: no second kernel and no float32 slices in memory.
+    // Taken when that gives at least 128 (SwiGLU) or 192 workgroups;
+    // measured on replayed 8B MLP and 70B attention projection steps,
+    // narrower projections stream better as 64-row tiles split over
+    // workgroups.
     const int64_t t2 = swi ? (N + 15) / 16 : (N + 31) / 32;
     int rg = SK_NW, ks = 1;
     if (t2 * mb >= (swi ? 128 : 192) && K <= 4 * SK_MAX_STAGES * SK_SUB) {
         rg = 2;
-        ks = 4;
+        // SwiGLU over many tiles (the stacked experts): two K ranges, so three
+        // 4-wave workgroups share a compute unit.
+        ks = (swi && t2 * mb >= 512 && K <= 2 * SK_MAX_STAGES * SK_SUB) ? 2 : 4;
     }
     p.rg = rg;
     p.ks = ks;
@@ -372,6 +376,9 @@ template <int EPI, bool NORM>
 static hipError_t mfma_launch_shape(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
     if (p.rg == SK_NW && p.ks == 1) return mfma_launch_kc<EPI, NORM, SK_NW, 1>(d, p, s);
     if (p.rg == 2 && p.ks == 4) return mfma_launch_kc<EPI, NORM, 2, 4>(d, p, s);
+    if constexpr (EPI == EPI_SWIGLU) {
+        if (p.rg == 2 && p.ks == 2) return mfma_launch_kc<EPI, NORM, 2, 2>(d, p, s);
+    }
     return hipErrorInvalidValue;
 }
 
