@@ -419,7 +419,7 @@ LINEAR_CASES = [
     # wide outputs: K split over the wave groups of one workgroup, ragged n and K, K shorter than one
     # stage, the longest K ranges (8192), and the fallbacks to 64-row tiles split over workgroups
     (16, 4096, 2040, "bf16"), (5, 2056, 6200, "bf16"), (12, 200, 4100, "bf16"), (16, 8200, 6150, "bf16"),
-    (16, 8192, 6152, "bf16"), (7, 16384, 2100, "bf16"), (9, 1032, 8200, "bf16"),
+    (16, 8192, 6152, "bf16"), (7, 16384, 2100, "bf16"), (9, 1032, 8200, "bf16"), (5, 17000, 1030, "bf16"),
     # prefill GEMM with one to three K tiles (the pipeline's prologue alone), ragged and not
     (17, 8, 3, "bf16"), (20, 24, 50, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"), (300, 104, 520, "bf16"),
 ]
