@@ -23,16 +23,17 @@
 //    (a lane's 8 k-values are keys 4kg..4kg+3 of the wave's two key tiles;
 //    the V^T operand reads the same 8 keys).
 //  - K and V go through LDS in blocks of 128 keys, double buffered, one
-//    barrier per block: while a block is multiplied, the next block's V comes
-//    into registers, to be written to the other stage transposed
-//    (V^T[d][key]) after the work, and its K goes straight from global
-//    memory into the other stage (global_load_lds, chunks XOR-swizzled by
-//    row) once this block's LDS reads are issued.
-//    The transpose pairs two keys of one column with one v_perm per dword,
-//    and key pairs are XOR-swizzled by d / 8 so that both the transposing
-//    stores and the operand reads spread over the LDS banks. Each wave reads
-//    its K fragments of a block at once, ahead of the score products, and
-//    its V fragments behind them, ahead of the softmax.
+//    barrier per block: once a block's LDS reads are issued, the next
+//    block's K and V go straight from global memory into the other stage
+//    (buffer loads to LDS), both as rows of D elements with their 16-byte
+//    chunks XOR-swizzled by key. V^T operands come out of the V rows with
+//    LDS transpose reads (ds_read_b64_tr_b16): in each group of 16 lanes,
+//    lane i receives element i % 4 of the 8 bytes that lanes 4j + i / 4
+//    point at, j = 0..3, so lanes pointing at 4 keys x 4 consecutive d
+//    quarters deliver V[key j][d] for lane d: the 4 keys of a lane's
+//    probabilities in one 16-key tile. Each wave reads its K fragments of a
+//    block at once, ahead of the score products, and its V fragments behind
+//    them, ahead of the softmax.
 //  - The online softmax (running max and sum per row, in the base-2 domain
 //    with the 1/sqrt(D) scale folded into one multiply-add) runs in
 //    registers. The reference maximum is raised only when a score exceeds it
@@ -91,13 +92,12 @@ __device__ __forceinline__ float pf_sum4(float v) {
     return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
-// Key-pair column of V^T row d in LDS: pairs are XOR-swizzled by bits of
-// d / 8 moved to pair-index bits 1, 2 and 4. Bits 0 and 3 stay put, so a
-// lane's two 4-key runs (pairs kp, kp + 1 and kp + 8, kp + 9) stay
-// contiguous and 8 pairs apart.
-__device__ __forceinline__ int vt_pair(int kp, int d) {
-    const int g = (d >> 3) & 7;
-    return kp ^ (((g & 3) << 1) | ((g & 4) << 2));
+// Position of V chunk lc (16 bytes) of key row r in the V tile: XOR with an
+// even value from the key, so that the 8 keys x 2 chunks the 32 lanes of one
+// transpose read touch fall into 16 distinct bank groups.
+template <int D>
+__device__ __forceinline__ int v_chunk(int r, int lc) {
+    return lc ^ (D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1));
 }
 
 // Position of K chunk lc (16 bytes) of key row r in the unpadded K tile: the
@@ -124,6 +124,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t key_block(const uint16_t* rows
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned off, uint16_t* lds_base) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
 }
+typedef short pf_s4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    const pf_s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) pf_s4*)p);
+    return __builtin_bit_cast(uint2, v);
+}
 __device__ __forceinline__ uint4 load_u4_buf(__amdgpu_buffer_rsrc_t r, unsigned off) {
     typedef unsigned u4v __attribute__((ext_vector_type(4)));
     const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -132,21 +137,17 @@ __device__ __forceinline__ uint4 load_u4_buf(__amdgpu_buffer_rsrc_t r, unsigned 
 
 template <int D, int GQ>
 __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
-    constexpr int DC = D / 8;                      // 16-byte chunks per row
-    constexpr int VPITCH = PF_BK + 8;              // V^T tile row pitch (elements)
-    constexpr int KDMA = PF_BK * D * 2 / 1024 / 8; // 1 KB transfers per wave per K block
-    constexpr int VUNITS = (PF_BK / 2) * DC;       // V (key pair, chunk) units per block
-    constexpr int VU = VUNITS / PF_NT;
+    constexpr int KDMA = PF_BK * D * 2 / 1024 / 8; // 1 KB transfers per wave per K (or V) block
     constexpr int DS = D / 32;                     // MFMA steps over d for the scores
     constexpr int DT = D / 16;                     // 16-wide d tiles of the output
     constexpr int TOK = PF_ROWS / GQ;              // tokens per query block
     constexpr int KTILE = PF_BK * D;               // elements
-    constexpr int VTILE = D * VPITCH;
+    constexpr int VTILE = PF_BK * D;
     constexpr int NV = DT * 8 + 4;                 // floats a lane publishes in the merge
-    static_assert(VUNITS % PF_NT == 0 && KDMA >= 1, "blocks must split evenly over the threads");
+    static_assert(KDMA >= 1, "blocks must split evenly over the threads");
     static_assert(4 * NV * 64 * 4 <= 2 * (KTILE + VTILE) * 2, "merge area exceeds the tiles");
 
-    // Two stages, each a K tile then a V^T tile.
+    // Two stages, each a K tile then a V tile.
     constexpr int BUF = KTILE + VTILE;
     __shared__ __align__(16) uint16_t smem[2 * BUF];
 
@@ -184,45 +185,26 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < KDMA; ++i) dma16_buf(r, koff[i], kdst + (i * 8 + wave) * 512);
     };
-    // V unit u -> keys 2 (u / DC) and 2 (u / DC) + 1, chunk u % DC, through
-    // registers (the tile is stored transposed). Keys past kv_len read as
-    // zeros; their scores are masked.
-    uint4 va[VU], vb[VU];
-    unsigned voff[VU];
+    // V block: as K, row e / D of the tile from transfer i, chunk swizzled by
+    // v_chunk.
+    unsigned voff[KDMA];
 #pragma unroll
-    for (int j = 0; j < VU; ++j) {
-        const int u = j * PF_NT + tid;
-        voff[j] = (unsigned)(2 * (u / DC) * D + (u % DC) * 8) * 2u;
+    for (int i = 0; i < KDMA; ++i) {
+        const int e = (i * 8 + wave) * 512 + lane * 8;
+        const int r = e / D;
+        voff[i] = (unsigned)(r * D + v_chunk<D>(r, (e % D) / 8) * 8) * 2u;
     }
-    auto load_v = [&](int kb) {
+    auto load_v = [&](int kb, uint16_t* vdst) {
         const int key0 = kb * PF_BK;
         const __amdgpu_buffer_rsrc_t r = key_block(vbase, key0, kv_len - key0, D);
 #pragma unroll
-        for (int j = 0; j < VU; ++j) {
-            va[j] = load_u4_buf(r, voff[j]);
-            vb[j] = load_u4_buf(r, voff[j] + D * 2);
-        }
+        for (int i = 0; i < KDMA; ++i) dma16_buf(r, voff[i], vdst + (i * 8 + wave) * 512);
     };
-    auto store_v = [&](uint16_t* vt) {
-#pragma unroll
-        for (int j = 0; j < VU; ++j) {
-            const int u = j * PF_NT + tid;
-            const int kp = u / DC, d0 = (u % DC) * 8;
-            const int kps = vt_pair(kp, d0);        // d0 .. d0 + 7 share d / 8
-            const uint32_t* A = &va[j].x;
-            const uint32_t* B = &vb[j].x;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                // (V[2kp][d], V[2kp+1][d]) for d = d0 + 2t and d0 + 2t + 1
-                *reinterpret_cast<uint32_t*>(&vt[(d0 + 2 * t) * VPITCH + 2 * kps]) =
-                    __builtin_amdgcn_perm(B[t], A[t], 0x05040100u);
-                *reinterpret_cast<uint32_t*>(&vt[(d0 + 2 * t + 1) * VPITCH + 2 * kps]) =
-                    __builtin_amdgcn_perm(B[t], A[t], 0x07060302u);
-            }
-        }
-    };
-
-    const int kp_lane = kq * 16 + kg * 2;           // first key pair of the lane's run
+    // Transpose reads of a lane (group kg = lane / 16, r = lane % 16): key
+    // 32 kq + 4 kg + r / 4 (+ 16 for the second), d quarter 4 (r % 4) of
+    // each 16-wide d tile.
+    const int tr_key = kq * PF_KW + kg * 4 + ((lane & 15) >> 2);
+    const int tr_q = lane & 3;
     // Query blocks pair and nqb - 1 - pair (once when they coincide).
     for (int ph = 0; ph < 2; ++ph) {
         const int qblk = ph == 0 ? pair : nqb - 1 - pair;
@@ -255,8 +237,7 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
             for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         load_k(0, smem);
-        load_v(0);
-        store_v(smem + KTILE);
+        load_v(0, smem + KTILE);
         // Every load issued so far (the query fragments included) has landed,
         // so the waits inside the loop only ever cover the next block's loads.
         __builtin_amdgcn_s_waitcnt(0);
@@ -296,10 +277,9 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
             // read now so that they land during the softmax.
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int d = dt * 16 + col;
-                const uint16_t* vrow = &vtb[d * VPITCH + 2 * vt_pair(kp_lane, d)];
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+                const int c = dt * 2 + (tr_q >> 1), h = (tr_q & 1) * 4;
+                const uint2 lo = lds_read_tr16(&vtb[tr_key * D + v_chunk<D>(tr_key, c) * 8 + h]);
+                const uint2 hi = lds_read_tr16(&vtb[(tr_key + 16) * D + v_chunk<D>(tr_key + 16, c) * 8 + h]);
                 vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -365,26 +345,24 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
                 for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = mfma16x32(vf[dt], pk[rt], ot[dt][rt]);
         };
 
-        // One block for the workgroup. The next block's V comes into registers
-        // first; its K goes by DMA into the other stage once this block's LDS
-        // reads are issued (a transfer into LDS ahead of them would make the
-        // compiler wait for it before reading); V is written transposed after
-        // the work.
+        // One block for the workgroup. The next block's K and V go by DMA into
+        // the other stage once this block's LDS reads are issued (a transfer
+        // into LDS ahead of them would make the compiler wait for it before
+        // reading).
         auto step = [&](int kb, bool masked) {
             const int buf = kb & 1;
             const bool more = kb + 1 < nblk;
             uint16_t* cur = smem + buf * BUF;
             uint16_t* nxt = smem + (buf ^ 1) * BUF;
-            if (more) load_v(kb + 1);
             // a quarter wholly past the last token's position holds no visible key
             const bool active = !masked || kb * PF_BK + kq * PF_KW <= plast;
             if (active) front(cur, cur + KTILE);
-            if (more) load_k(kb + 1, nxt);
-            if (active) back(kb, masked);
             if (more) {
-                store_v(nxt + KTILE);
-                __builtin_amdgcn_s_waitcnt(0);      // the K transfers have landed in LDS
+                load_k(kb + 1, nxt);
+                load_v(kb + 1, nxt + KTILE);
             }
+            if (active) back(kb, masked);
+            if (more) __builtin_amdgcn_s_waitcnt(0);  // the K and V transfers have landed in LDS
             __syncthreads();
         };
         // Blocks every row sees whole, then the diagonal ones, in two loops so
