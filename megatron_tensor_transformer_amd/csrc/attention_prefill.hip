@@ -108,11 +108,6 @@ __device__ __forceinline__ int k_chunk(int r, int lc) {
     return lc ^ (D == 128 ? (r & 15) : ((r >> 1) & 7));
 }
 
-__device__ __forceinline__ void dma16(const uint16_t* src, uint16_t* lds_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-
 // Buffer view of one key block of a head's K or V rows: the block's first
 // row as base and its rows below kv_len as the range. Reads past the range
 // return zeros, so keys past kv_len need no clamping (their scores are
@@ -128,11 +123,6 @@ typedef short pf_s4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
     const pf_s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) pf_s4*)p);
     return __builtin_bit_cast(uint2, v);
-}
-__device__ __forceinline__ uint4 load_u4_buf(__amdgpu_buffer_rsrc_t r, unsigned off) {
-    typedef unsigned u4v __attribute__((ext_vector_type(4)));
-    const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <int D, int GQ>
