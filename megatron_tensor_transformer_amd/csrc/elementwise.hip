@@ -40,11 +40,15 @@ __global__ __launch_bounds__(EW_THREADS) void partial_sum_kernel(PartialPtrs ps,
     const int64_t n4 = count / 4;
     const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
     for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n4; i += stride) {
-        float4 acc = load4<IN_BF16>(ps.p[0], i);
-        for (int r = 1; r < t; ++r) {
-            const float4 v = load4<IN_BF16>(ps.p[r], i);
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-        }
+        // every partial requested before the first add; added in rank order
+        float4 v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            if (r < t) v[r] = load4<IN_BF16>(ps.p[r], i);
+        float4 acc = v[0];
+#pragma unroll
+        for (int r = 1; r < 8; ++r)
+            if (r < t) { acc.x += v[r].x; acc.y += v[r].y; acc.z += v[r].z; acc.w += v[r].w; }
         if (OUT_BF16) {
             if (residual) {
                 const uint2 rv = reinterpret_cast<const uint2*>(residual)[i];

@@ -310,6 +310,7 @@ hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters,
     d.kc = p.kc;
     d.splits = p.splits;
     d.n_tiles = p.n_tiles;
+    d.opt = p.out_per_tile;
     if (p.splits > 1) {
         const size_t tiles = (size_t)p.n_tiles * p.mb_per_launch;
         char* b = reinterpret_cast<char*>(scratch);

@@ -10,32 +10,30 @@
 //
 // Loading B straight from HBM in that layout reads 16 rows x 64 bytes per
 // wave instruction, which streams at well under the HBM rate; runs of 256
-// bytes or more per row stream at full rate. So weights are read as 2 rows x
-// 512 bytes per instruction and pass through a small wave-private LDS tile
-// on their way to the operand registers.
-//  - A wave owns 16 weight rows and a K range, walked in stages of 256
-//    elements with two stages of loads in flight: the loads of stage i + 1
-//    are requested before stage i is used. Loads return in order, so each
-//    stage's activations and weights are requested together, in the order
-//    they are consumed.
-//  - The waves that share a K range share its activations: per stage they
-//    are staged once (16 tokens x 256, padded with zeros, times gamma when
-//    RMSNorm is fused, their squares summed); each wave stages its own 16
-//    weight rows. Rows are padded by 16 bytes so the operand reads of 16
-//    rows hit distinct banks.
-//  - Wide projections: 8 waves per workgroup, 2 per K range (32 rows: for
-//    SwiGLU the gate and up rows of 16 outputs) and 4 K ranges, whose sums
-//    are added in LDS before the epilogue (SwiGLU over 512 tiles or more: 2
-//    K ranges, 4 waves, three workgroups per compute unit). One kernel,
-//    nothing in memory between the slices.
-//  - Narrow projections (too few 32-row tiles to fill the chip): 4 waves
-//    share one K range of a 64-row tile and K is split over workgroups. Each
-//    writes its float32 slice with plain stores and a small merge kernel (one
-//    workgroup per tile) adds the slices in split order and runs the
-//    epilogue: no counter vote, whose memory round trips would sit at the
-//    end of the projection kernel.
-//  - Unsplit, the results (lane: one weight row, four tokens) go through an
-//    LDS tile to the epilogue shared with the v_dot2 kernel.
+// bytes or more per row stream at full rate. So weights pass through LDS on
+// their way to the operand registers. Two kernels:
+//  - Wide projections (gemv_mfma_wide_kernel): a workgroup of 8 waves takes
+//    32 or 16 weight rows over all of K, one K range per wave. Weights go by
+//    DMA into the wave's own LDS tiles (4 rows x 256 bytes per transfer),
+//    activation operands are read straight from memory, and the waves meet
+//    only when their sums are added at the end: no workgroup barrier while
+//    streaming, no second kernel, no float32 slices in memory.
+//  - Narrow projections and the stacked experts (gemv_mfma_kernel): waves
+//    own 16 rows each and share a K range, walked in stages of 256 elements
+//    with two stages of loads in flight; weights are read as 2 rows x 512
+//    bytes per instruction and written to a wave-private LDS tile (rows
+//    padded by 16 bytes so the operand reads of 16 rows hit distinct banks),
+//    and the waves sharing a K range stage its activations once per stage
+//    (16 tokens x 256, zero-padded, times gamma when RMSNorm is fused, their
+//    squares summed), alternating between two LDS stages so a stage costs
+//    one barrier. Narrow projections (too few tiles to fill the chip) use 4
+//    waves per 64-row tile and split K over workgroups: each writes its
+//    float32 slice with plain stores and a small merge kernel (one workgroup
+//    per tile) adds the slices in split order and runs the epilogue. The
+//    stacked experts' SwiGLU uses 4-wave workgroups of two K ranges whose
+//    sums meet in LDS, three workgroups per compute unit.
+//  - Either way the results (lane: one weight row, four tokens) reach the
+//    epilogue shared with the v_dot2 kernel through an LDS tile.
 #include "gemv_tile.h"
 
 namespace tpk {
@@ -69,9 +67,14 @@ __global__ __launch_bounds__(RG * KS * 64) void gemv_mfma_kernel(GemvDev d) {
     constexpr int TSTEP = 2 * RG;               // tokens between them
     constexpr bool SWI = (EPI == EPI_SWIGLU);
     constexpr int HALF = RPT / 2;
+    // Activation stages in LDS: two let a stage be written while the other is
+    // still being read, so one barrier per stage suffices. The layout that
+    // packs three workgroups per compute unit keeps one (LDS decides how many
+    // fit).
+    constexpr int XB = (RG == 2 && KS == 2) ? 1 : 2;
     static_assert(!SWI || RG % 2 == 0, "a SwiGLU tile pairs gate and up waves");
     __shared__ __align__(16) uint16_t wl[RG * KS][16 * SK_PITCH];
-    __shared__ __align__(16) uint16_t xl[KS][SK_MT * SK_PITCH];
+    __shared__ __align__(16) uint16_t xl[XB][KS][SK_MT * SK_PITCH];
     __shared__ float res[SK_MT * RPT];
     __shared__ float ssl[KS][SK_MT];
 
@@ -119,7 +122,6 @@ __global__ __launch_bounds__(RG * KS * 64) void gemv_mfma_kernel(GemvDev d) {
         xrow[i] = reinterpret_cast<const uint16_t*>(a.x) + (size_t)(m0 + min(t, mvalid - 1)) * K;
     }
     const uint16_t* gam = reinterpret_cast<const uint16_t*>(a.gamma);
-    uint16_t* xg = xl[grp];
 
     struct Stage { uint4 w[SK_WL]; uint4 x[XV]; uint4 g; };
     auto issue = [&](Stage& b, int st) {
@@ -143,7 +145,12 @@ __global__ __launch_bounds__(RG * KS * 64) void gemv_mfma_kernel(GemvDev d) {
             __builtin_amdgcn_sched_barrier(0);
         }
         const bool kin = kbase + st * SK_SUB + ve < K;
-        if (st > 0) __syncthreads();           // every wave is done reading the previous stage
+        // With one activation stage, every wave must be done reading the
+        // previous one. With two, the barrier that ended the previous stage's
+        // writes also ended the reads of the one before it. The weight tile is
+        // the wave's own: its reads of the previous stage precede these writes.
+        if (XB == 1 && st > 0) __syncthreads();
+        uint16_t* xg = xl[st % XB][grp];
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             uint4 v = cur.x[i];
@@ -230,6 +237,204 @@ __global__ __launch_bounds__(RG * KS * 64) void gemv_mfma_kernel(GemvDev d) {
     gemv_epilogue<uint16_t, SK_MT, RPT, EPI, NORM, NT>(a, res, ssl[0], tile, m0, mvalid);
 }
 
+// Wide projections, one wave per K range. A workgroup of 8 waves covers ROWS
+// (32 or 16) weight rows over all of K (for SwiGLU the gate and up rows of
+// ROWS / 2 outputs); wave w takes the w-th eighth of K in stages of 128
+// elements. Each wave moves its stage of weights (ROWS rows x 256 bytes) from
+// HBM into its own LDS tile by DMA, two tiles alternating, and reads its
+// activation operands straight from memory (the 16 tokens' rows stay in L2;
+// their bytes are 16 / ROWS of the weights'). No wave waits for another until
+// the K ranges' sums meet in LDS, and no weight passes through registers on
+// its way to LDS. Rows are 256 bytes, unpadded: a row's 16-byte chunks are
+// XOR-swizzled by the row index, so the 16 rows of an operand read fall in
+// distinct banks. Chunks past K and rows past N are fetched out of their
+// buffer's range and arrive as zeros. 16-row workgroups serve projections
+// with too few 32-row tiles to fill the chip, without splitting K over
+// workgroups.
+constexpr int WD_NW = 8;                        // waves, one K range each
+constexpr int WD_SUB = 128;                     // K elements per stage
+constexpr int WD16_NBUF = 4;                    // stage tiles per wave with 16 rows (32 rows: 2, LDS-bound)
+constexpr unsigned WD_OOB = 0x80000000u;        // an offset past every buffer's range
+
+// s_waitcnt immediate waiting until at most n vector-memory operations are
+// outstanding (LDS and export counts left at their maxima).
+__host__ __device__ constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wd_view(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Weights are read once: the transfer is marked non-temporal (the nt bit of
+// the cache policy), like the streamed loads of the other kernels.
+__device__ __forceinline__ void wd_dma16(__amdgpu_buffer_rsrc_t r, unsigned off, uint16_t* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 2);
+}
+__device__ __forceinline__ uint4 wd_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int EPI, bool NORM, int NST, int ROWS>
+__global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
+    static_assert(ROWS == 16 || ROWS == 32, "one or two 16-row operand tiles");
+    constexpr int NT = WD_NW * 64;
+    constexpr bool SWI = (EPI == EPI_SWIGLU);
+    constexpr int NQ = ROWS / 4;                // transfers per stage, 4 rows x 256 bytes each
+    constexpr int NTT = ROWS / 16;              // 16-row operand tiles
+    constexpr int WD_STAGE = ROWS * WD_SUB;     // elements of a wave's stage
+    constexpr int VM = 4 + (NORM ? 4 : 0) + NQ; // vector-memory operations per stage
+    // A ring of NBUF stage tiles per wave, NBUF - 1 stages requested ahead;
+    // each tile of the ring is its own array, so the compiler can tell one
+    // stage's transfers from another stage's reads.
+    constexpr int NBUF = ROWS == 32 ? 2 : WD16_NBUF;
+    static_assert(NBUF >= 2 && NBUF <= 4 && VM * (NBUF - 1) <= 63, "the ring and the wait counter");
+    __shared__ __align__(16) uint16_t w0[WD_NW][WD_STAGE];
+    __shared__ __align__(16) uint16_t w1[WD_NW][WD_STAGE];
+    __shared__ __align__(16) uint16_t w2[WD_NW][NBUF > 2 ? WD_STAGE : 8];
+    __shared__ __align__(16) uint16_t w3[WD_NW][NBUF > 3 ? WD_STAGE : 8];
+    __shared__ float res[SK_MT * ROWS];
+    __shared__ float ssl[WD_NW][SK_MT];
+
+    const GemvArgs& a = d.a;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
+    const int tile = blockIdx.x, mb = d.mb0 + blockIdx.z;
+    const int K = a.K, N = a.N;
+    const int kw = wave * (NST * WD_SUB);       // first K element of this wave's range
+    const int m0 = mb * SK_MT;
+    const int mvalid = min(SK_MT, a.m - m0);
+    const int col = lane & 15, kg = lane >> 4;
+
+    // Weight views: for SwiGLU the gate rows and the up rows of outputs
+    // opt tile .. + opt - 1 (opt <= ROWS / 2), else rows opt tile .. +
+    // opt - 1 (opt <= ROWS); the rest of the tile is padding, fetched out
+    // of range.
+    constexpr int HALF = ROWS / 2;
+    const int opt = d.opt;
+    const int n0 = tile * opt;
+    const int nrows = min(N - n0, opt);
+    const int64_t rowb = (int64_t)K * 2;
+    const __amdgpu_buffer_rsrc_t wv0 =
+        wd_view(reinterpret_cast<const uint16_t*>(a.w) + (size_t)n0 * K, nrows * rowb);
+    const __amdgpu_buffer_rsrc_t wv1 =
+        SWI ? wd_view(reinterpret_cast<const uint16_t*>(a.w_up) + (size_t)n0 * K, nrows * rowb) : wv0;
+    // Transfer q moves rows 4q .. 4q + 3 of the tile: lane l fetches chunk
+    // (l & 15) ^ (row & 15) of row 4q + l / 16 into position l & 15 of it.
+    const int dr = lane >> 4;
+    int wrowb[NQ], wck[4];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int r = 4 * q + dr;
+        wrowb[q] = (SWI ? r % HALF : r) * K * 2;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wck[q] = ((lane & 15) ^ ((4 * q + dr) & 15)) * 8;
+    // Activation and gamma views: token col's row, chunk kg of each 32.
+    const __amdgpu_buffer_rsrc_t xv = wd_view(reinterpret_cast<const uint16_t*>(a.x) + (size_t)m0 * K, mvalid * rowb);
+    const __amdgpu_buffer_rsrc_t gv = wd_view(a.gamma, NORM ? rowb : 0);
+    const unsigned xrow = col * K * 2;
+
+    struct Act { uint4 x[4]; uint4 g[4]; };
+    auto issue = [&](Act& ac, uint16_t* dst, int st) {
+        const int k0 = kw + st * WD_SUB;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int k = k0 + s * 32 + kg * 8;
+            ac.x[s] = wd_load16(xv, k < K ? xrow + k * 2 : WD_OOB);
+            if (NORM) ac.g[s] = wd_load16(gv, k < K ? k * 2 : WD_OOB);
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int k = k0 + wck[q & 3];
+            wd_dma16(q < NQ / 2 ? wv0 : wv1, k < K ? wrowb[q] + k * 2 : WD_OOB, dst + q * 512);
+        }
+    };
+
+    float ss = 0.f;
+    f32x4_t acc[NTT];
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto run = [&](Act& cur, const uint16_t* tl) {
+        uint4 b[NTT][4];
+#pragma unroll
+        for (int t = 0; t < NTT; ++t)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int r = t * 16 + col;
+                b[t][s] = *reinterpret_cast<const uint4*>(&tl[r * WD_SUB + (((s * 4 + kg) ^ (r & 15)) * 8)]);
+            }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            uint4 xa = cur.x[s];
+            if (NORM) {
+                ss += vsumsq(xa, (uint16_t*)nullptr);
+                xa = vscale(xa, cur.g[s], (uint16_t*)nullptr);
+            }
+#pragma unroll
+            for (int t = 0; t < NTT; ++t) acc[t] = mfma16(xa, b[t][s], acc[t]);
+        }
+    };
+    // stage i's tile (i is a constant once the loops are unrolled)
+    auto tile_of = [&](int i) -> uint16_t* {
+        switch (i % NBUF) {
+            case 0: return w0[wave];
+            case 1: return w1[wave];
+            case 2: return w2[wave];
+            default: return w3[wave];
+        }
+    };
+    Act ac[NBUF];
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i)
+        if (i < NST) issue(ac[i], tile_of(i), i);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        // Stage st + NBUF - 1 reuses the tile and registers of stage st - 1,
+        // whose reads are complete.
+        if (st + NBUF - 1 < NST) issue(ac[(st + NBUF - 1) % NBUF], tile_of(st + NBUF - 1), st + NBUF - 1);
+        // this stage's loads and transfers are done when only the later
+        // stages' are outstanding
+        const int later = min(NBUF - 1, NST - 1 - st);
+        if (later == 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * VM));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * VM));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        __builtin_amdgcn_sched_barrier(0);
+        run(ac[st % NBUF], tile_of(st));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Sums of the K ranges, added in wave order (deterministic): every wave
+    // parks its 16 tokens x ROWS rows in its first tile (its own reads of it
+    // and transfers into it are complete).
+    float* park = reinterpret_cast<float*>(w0[wave]);
+#pragma unroll
+    for (int t = 0; t < NTT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) park[(4 * kg + j) * ROWS + t * 16 + col] = acc[t][j];
+    if (NORM) {
+        // lanes col, col + 16, col + 32, col + 48 hold token col's squares
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lane < 16) ssl[wave][lane] = ss;
+    }
+    __syncthreads();
+    for (int e = tid; e < SK_MT * ROWS; e += NT) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < WD_NW; ++w) v += reinterpret_cast<const float*>(w0[w])[e];
+        res[e] = v;
+    }
+    if (NORM && tid < SK_MT) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < WD_NW; ++w) v += ssl[w][tid];
+        ssl[0][tid] = v;
+    }
+    __syncthreads();
+    gemv_epilogue<uint16_t, SK_MT, ROWS, EPI, NORM, NT>(a, res, ssl[0], tile, m0, mvalid, opt);
+}
+
 // Split-K merge: one workgroup per output tile adds the tile's slices in
 // split order (a thread requests the slices of its outputs together) and runs
 // the epilogue.
@@ -277,6 +482,8 @@ __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
     gemv_epilogue<uint16_t, SK_MT, SK_RPT, EPI, NORM, NT>(d.a, res, ssl, tile, m0, mvalid);
 }
 
+constexpr int64_t WIDE_MIN_ROWS = 16;          // rows of the shortest wide tile
+
 GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
     GemvPlan p{};
     p.mfma = 1;
@@ -286,32 +493,45 @@ GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
     p.lds_bytes = 0;                            // static LDS only
     const bool swi = epi == EPI_SWIGLU;
     const int64_t mb = p.mblocks;
-    // Wide projections: one workgroup per tile of 16 outputs (SwiGLU: 16
-    // gate and 16 up rows; otherwise 32 rows), its K range split over 4 wave
-    // groups of 2 waves (2 groups for SwiGLU over 512 tiles or more) whose
-    // sums meet in LDS: no second kernel and no float32 slices in memory.
-    // Taken when that gives at least 128 (SwiGLU) or 192 workgroups;
-    // measured on replayed 8B MLP and 70B attention projection steps,
-    // narrower projections stream better as 64-row tiles split over
-    // workgroups.
+    // Wide projections: one workgroup of 8 waves per tile of rows, its K
+    // range split over the waves, whose sums meet in LDS: no second kernel
+    // and no float32 slices in memory. A tile holds as many outputs as make
+    // about 256 workgroups (one per compute unit, none idle; the rest of the
+    // tile is padding that is never fetched): up to 32 rows, or the gate and
+    // up rows of 16 outputs, in two 16-row operand tiles, and up to 16 rows
+    // (8 outputs) in one, down to WIDE_MIN_ROWS. SwiGLU over 512 tiles of
+    // 16 outputs or more (the stacked experts) takes 4-wave workgroups of two
+    // K ranges instead, three per compute unit. Otherwise 64-row tiles split
+    // over workgroups. Measured on replayed 8B MLP and 70B attention
+    // projection steps and the 70B layer: tiles of 10 rows (70B QKV, t=4)
+    // or 5 (t=8) lose to the split, by 0.3 and 3 us per call.
     const int64_t t2 = swi ? (N + 15) / 16 : (N + 31) / 32;
-    int rg = SK_NW, ks = 1;
-    if (t2 * mb >= (swi ? 128 : 192) && K <= 4 * SK_MAX_STAGES * SK_SUB) {
-        rg = 2;
-        // SwiGLU over many tiles (the stacked experts): two K ranges, so three
-        // 4-wave workgroups share a compute unit.
-        ks = (swi && t2 * mb >= 512 && K <= 2 * SK_MAX_STAGES * SK_SUB) ? 2 : 4;
+    const int64_t want = std::max<int64_t>(1, 256 / mb);
+    const int64_t per = (N + want - 1) / want;  // outputs per tile for ~256 workgroups
+    const int64_t cap16 = swi ? 8 : 16, cap32 = swi ? 16 : 32;
+    int rg = SK_NW, ks = 1, opt = swi ? 8 * SK_NW : 16 * SK_NW;
+    if (K <= 4 * SK_MAX_STAGES * SK_SUB) {
+        if (swi && t2 * mb >= 512 && K <= 2 * SK_MAX_STAGES * SK_SUB) {
+            rg = 2, ks = 2, opt = 16;
+        } else if (per > cap16) {
+            rg = 2, ks = 4, opt = (int)std::min(cap32, per);
+        } else if (per >= (swi ? WIDE_MIN_ROWS / 2 : WIDE_MIN_ROWS)) {
+            rg = 1, ks = 8, opt = (int)per;
+        }
     }
     p.rg = rg;
     p.ks = ks;
     p.nw = rg * ks;
     p.threads = p.nw * 64;
     p.rows_per_tile = 16 * rg;
-    p.out_per_tile = swi ? 8 * rg : 16 * rg;
+    p.out_per_tile = opt;
     p.n_tiles = (N + p.out_per_tile - 1) / p.out_per_tile;
     if (ks > 1) {
+        // a workgroup covers 4 kc elements of K (8 waves of kc / 2), or 2 kc
+        // (two K ranges of kc)
+        const int span = rg * ks == WD_NW ? 4 : ks;
         int kc = SK_SUB;
-        while (kc * ks < K) kc *= 2;            // at most SK_MAX_STAGES stages by the guard above
+        while (kc * span < K) kc *= 2;          // at most SK_MAX_STAGES stages by the guard above
         p.kc = kc;
         p.splits = 1;
         return p;
@@ -349,7 +569,10 @@ static hipError_t mfma_launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t
         GemvDev dl = d;
         dl.mb0 = mb0;
         dim3 grid(p.n_tiles, p.splits, min(p.mb_per_launch, p.mblocks - mb0));
-        hipLaunchKernelGGL((gemv_mfma_kernel<EPI, NORM, NST, RG, KS>), grid, dim3(RG * KS * 64), 0, s, dl);
+        if constexpr (RG * KS == WD_NW)         // 16 RG rows; 8 K ranges of NST stages of 128
+            hipLaunchKernelGGL((gemv_mfma_wide_kernel<EPI, NORM, NST, 16 * RG>), grid, dim3(WD_NW * 64), 0, s, dl);
+        else
+            hipLaunchKernelGGL((gemv_mfma_kernel<EPI, NORM, NST, RG, KS>), grid, dim3(RG * KS * 64), 0, s, dl);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
@@ -376,6 +599,7 @@ template <int EPI, bool NORM>
 static hipError_t mfma_launch_shape(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
     if (p.rg == SK_NW && p.ks == 1) return mfma_launch_kc<EPI, NORM, SK_NW, 1>(d, p, s);
     if (p.rg == 2 && p.ks == 4) return mfma_launch_kc<EPI, NORM, 2, 4>(d, p, s);
+    if (p.rg == 1 && p.ks == 8) return mfma_launch_kc<EPI, NORM, 1, 8>(d, p, s);
     if constexpr (EPI == EPI_SWIGLU) {
         if (p.rg == 2 && p.ks == 2) return mfma_launch_kc<EPI, NORM, 2, 2>(d, p, s);
     }

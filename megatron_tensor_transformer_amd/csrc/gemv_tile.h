@@ -11,6 +11,7 @@ namespace tpk {
 struct GemvDev {
     GemvArgs a;
     int kc, splits, n_tiles;
+    int opt;           // outputs per tile
     int mb0;           // first m-block of this launch
     float* part;       // [tiles*mblocks][S][MT*RPT]
     float* ssq;        // [tiles*mblocks][S][MT]
@@ -67,10 +68,11 @@ __device__ __forceinline__ uint4 vscale(const uint4& v, const uint4& g, float*) 
 // The epilogue of one output tile: res[m][RPT] are the full K sums of the
 // tile's rows for tokens m < mvalid (for SwiGLU the gate rows first, then the
 // up rows of the same outputs), ssl[m] the activations' sums of squares when
-// RMSNorm is fused.
+// RMSNorm is fused. A tile holds opt outputs (at most RPT, or RPT / 2 for
+// SwiGLU; rows past them are padding).
 template <typename T, int MT, int RPT, int EPI, bool NORM, int NT>
 __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, const float* res, const float* ssl, int tile, int m0,
-                                              int mvalid) {
+                                              int mvalid, int opt = EPI == EPI_SWIGLU ? RPT / 2 : RPT) {
     constexpr bool SWI = (EPI == EPI_SWIGLU);
     constexpr int HALF = RPT / 2;
     constexpr int OUTS = SWI ? HALF : RPT;
@@ -78,17 +80,18 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, const float* re
     const int N = a.N;
     for (int i = tid; i < mvalid * OUTS; i += NT) {
         const int m = i / OUTS, o = i - m * OUTS;
+        if (o >= opt) continue;
         const float inv = NORM ? 1.0f / sqrtf(ssl[m] / (float)a.K + a.eps) : 1.0f;
         const int row = m0 + m;
         if (SWI) {
-            const int n = tile * HALF + o;
+            const int n = tile * opt + o;
             if (n < N) {
                 const float g = res[m * RPT + o] * inv;
                 const float u = res[m * RPT + HALF + o] * inv;
                 store_out(a.y, (size_t)row * N + n, silu_f32(g) * u, (T*)nullptr);
             }
         } else {
-            const int n = tile * RPT + o;
+            const int n = tile * opt + o;
             if (n >= N) continue;
             const float v = res[m * RPT + o] * inv;
             if (EPI == EPI_PARTIAL) {

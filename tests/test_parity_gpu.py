@@ -420,6 +420,15 @@ LINEAR_CASES = [
     # stage, the longest K ranges (8192), and the fallbacks to 64-row tiles split over workgroups
     (16, 4096, 2040, "bf16"), (5, 2056, 6200, "bf16"), (12, 200, 4100, "bf16"), (16, 8200, 6150, "bf16"),
     (16, 8192, 6152, "bf16"), (7, 16384, 2100, "bf16"), (9, 1032, 8200, "bf16"), (5, 17000, 1030, "bf16"),
+    # 16-row wide tiles (4096 <= n < 6144 at one block of 16 tokens, or two blocks): the 8B down
+    # projection's shape, ragged n with K ending inside a stage, the longest K, K short of one stage per
+    # wave, two token blocks
+    (16, 3584, 4096, "bf16"), (11, 2040, 5000, "bf16"), (16, 8192, 4104, "bf16"), (6, 136, 6100, "bf16"),
+    (20, 1032, 2100, "bf16"),
+    # SwiGLU tiles of fewer outputs than rows, sized to fill 256 workgroups (13 outputs, the last tile
+    # ragged; 10), and the 70B QKV shard shapes at t=4 and t=8 (K ending inside a stage) that stay on
+    # 64-row tiles split over workgroups
+    (16, 1032, 3300, "bf16"), (16, 8192, 2560, "bf16"), (16, 4104, 1280, "bf16"), (7, 1032, 1500, "bf16"),
     # prefill GEMM with one to three K tiles (the pipeline's prologue alone), ragged and not
     (17, 8, 3, "bf16"), (20, 24, 50, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"), (300, 104, 520, "bf16"),
 ]
