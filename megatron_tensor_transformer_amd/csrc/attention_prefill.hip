@@ -195,6 +195,21 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     // each 16-wide d tile.
     const int tr_key = kq * PF_KW + kg * 4 + ((lane & 15) >> 2);
     const int tr_q = lane & 3;
+    // The lane's fragment offsets within a tile (elements), the same for
+    // every block: K rows 32 kq + col, chunk s * 4 + kg; V^T of d tile dt.
+    // The second 16 rows (keys) of either are 16 D further on, since both
+    // swizzles repeat every 16 rows.
+    int kfo[DS], vto[DT];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+        const int r = kq * PF_KW + col;
+        kfo[s] = r * D + k_chunk<D>(r, s * 4 + kg) * 8;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const int cc = dt * 2 + (tr_q >> 1);
+        vto[dt] = tr_key * D + v_chunk<D>(tr_key, cc) * 8 + (tr_q & 1) * 4;
+    }
     // Query blocks pair and nqb - 1 - pair (once when they coincide).
     for (int ph = 0; ph < 2; ++ph) {
         const int qblk = ph == 0 ? pair : nqb - 1 - pair;
@@ -220,6 +235,15 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
         }
 
         float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+        // Row sums of the rounded probabilities. With d = 128 on the matrix
+        // cores: an all-ones A operand times P^T gives every row's sum in
+        // each of the lane's four outputs, accumulated and rescaled like the
+        // outputs (fewer vector instructions; the 8 registers it takes would
+        // cost d = 64 a workgroup per compute unit, so there the lanes add
+        // their probabilities with v_dot2 and two permlane swaps).
+        constexpr bool MSUM = D == 128;
+        f32x4_t lacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
         f32x4_t ot[DT][2];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -244,10 +268,7 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int s = 0; s < DS; ++s)
 #pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int r = kq * PF_KW + t * 16 + col;
-                    kf[s][t] = *reinterpret_cast<const uint4*>(&kt[r * D + k_chunk<D>(r, s * 4 + kg) * 8]);
-                }
+                for (int t = 0; t < 2; ++t) kf[s][t] = *reinterpret_cast<const uint4*>(&kt[kfo[s] + t * 16 * D]);
             __builtin_amdgcn_sched_barrier(0);
 
             // S^T tiles: keys 32 kq + 16 t .. + 15 of the block x this wave's
@@ -267,9 +288,8 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
             // read now so that they land during the softmax.
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int c = dt * 2 + (tr_q >> 1), h = (tr_q & 1) * 4;
-                const uint2 lo = lds_read_tr16(&vtb[tr_key * D + v_chunk<D>(tr_key, c) * 8 + h]);
-                const uint2 hi = lds_read_tr16(&vtb[(tr_key + 16) * D + v_chunk<D>(tr_key + 16, c) * 8 + h]);
+                const uint2 lo = lds_read_tr16(&vtb[vto[dt]]);
+                const uint2 hi = lds_read_tr16(&vtb[vto[dt] + 16 * D]);
                 vf[dt] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -300,7 +320,12 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
                     const float mnew = fmaxf(mrun[rt], mx[rt]);
                     const float al = __builtin_amdgcn_exp2f(mrun[rt] - (mnew == -INFINITY ? 0.f : mnew));
                     mrun[rt] = mnew;
-                    lrun[rt] *= al;
+                    if (MSUM) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) lacc[rt][j] *= al;
+                    } else {
+                        lrun[rt] *= al;
+                    }
 #pragma unroll
                     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -319,20 +344,23 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
                     for (int h2 = 0; h2 < 2; ++h2) {
                         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][rt][2 * h2], c, -mref));
                         const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][rt][2 * h2 + 1], c, -mref));
-                        const uint32_t p = pack_bf16x2(e0, e1);
-                        sum = dot2_bf16(p, 0x3f803f80u, sum);
-                        pw[t][h2] = p;
+                        pw[t][h2] = pack_bf16x2(e0, e1);
+                        if (!MSUM) sum = dot2_bf16(pw[t][h2], 0x3f803f80u, sum);
                     }
-                lrun[rt] += pf_sum4(sum);
+                if (!MSUM) lrun[rt] += pf_sum4(sum);
                 pk[rt] = make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]);
             }
             __builtin_amdgcn_sched_barrier(0);
 
-            // O^T += V^T P^T.
+            // O^T += V^T P^T, and the row sums.
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = mfma16x32(vf[dt], pk[rt], ot[dt][rt]);
+            if (MSUM) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) lacc[rt] = mfma16x32(ones, pk[rt], lacc[rt]);
+            }
         };
 
         // One block for the workgroup. The next block's K and V go by DMA into
@@ -360,6 +388,10 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
         int kb = 0;
         for (; kb < nfull; ++kb) step(kb, false);
         for (; kb < nblk; ++kb) step(kb, true);
+        if (MSUM) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) lrun[rt] = lacc[rt][0];
+        }
 
         // Merge the key quarters by their log-sum-exp weights, in two rounds
         // through the idle tiles: quarters 2, 3 into 0, 1, then 1 into 0.
