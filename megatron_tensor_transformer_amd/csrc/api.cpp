@@ -404,6 +404,10 @@ tp_status tp_row_linear_partial_bf16(const void* a, const void* w, void* partial
 
 namespace {
 
+// Tokens up to which the router's logits and gates come from one fused launch
+// (every workgroup reads all of W_router, cheap for a decode batch).
+constexpr int64_t MOE_FUSED_ROUTER_MAX_M = 64;
+
 // MoE workspace: [header][u (normalised x)][logits][gates][expert activations][projection scratch].
 struct MoeWs {
     size_t u, logits, gates, act, lin, total;
@@ -475,11 +479,19 @@ tp_status tp_moe_shard_forward(const tp_moe_weights* w, const void* x, float* pa
         if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
         xin = u;
     }
-    // The router is replicated on every rank: logits = u @ W_router^T, float32.
-    TRY(run_linear(xin, w->w_router, nullptr, nullptr, 0.f, logits, m, hidden, n_experts, TP_BF16,
-                   tpk::EPI_PARTIAL, cnt, lin, s));
-    hipError_t e = tpk::moe_gates_launch(logits, gates, (int)m, n_experts, top_k, s);
-    if (e != hipSuccess) return hip_fail(e, "router gates launch");
+    // The router is replicated on every rank: logits = u @ W_router^T, float32,
+    // then the top-k gates. A decode batch takes both in one launch; larger
+    // batches form the logits as a projection.
+    hipError_t e;
+    if (m <= MOE_FUSED_ROUTER_MAX_M) {
+        e = tpk::moe_router_launch(xin, w->w_router, logits, gates, (int)m, (int)hidden, n_experts, top_k, s);
+        if (e != hipSuccess) return hip_fail(e, "router launch");
+    } else {
+        TRY(run_linear(xin, w->w_router, nullptr, nullptr, 0.f, logits, m, hidden, n_experts, TP_BF16,
+                       tpk::EPI_PARTIAL, cnt, lin, s));
+        e = tpk::moe_gates_launch(logits, gates, (int)m, n_experts, top_k, s);
+        if (e != hipSuccess) return hip_fail(e, "router gates launch");
+    }
     // Every expert's gate/up column block at once (rows stacked expert by expert).
     TRY(run_linear(xin, w->w_gate, w->w_up, nullptr, 0.f, act, m, hidden, ecols, TP_BF16, tpk::EPI_SWIGLU, cnt,
                    lin, s));

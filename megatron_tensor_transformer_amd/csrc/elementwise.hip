@@ -236,33 +236,113 @@ hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Router gates: per token, the top_k largest of its E logits (ties to the
-// lower expert index) get softmax weights over those k alone, the rest 0.
-// One thread per token; E is small.
+// Top-k routing of one token in one wave: lane e holds expert e's logit
+// (lanes past E hold nothing). The k experts with the largest logits are
+// chosen one at a time, the lowest index first among equal logits; their gates
+// are the softmax of their logits (exponentials relative to the largest,
+// added in expert order), every other gate 0.
+__device__ __forceinline__ void route_wave(float l, int E, int top_k, float* logits_row, float* gates_row) {
+    const int e = threadIdx.x & 63;
+    const bool valid = e < E;
+    bool chosen = false;
+    float mx0 = 0.f;
+    for (int j = 0; j < top_k; ++j) {
+        float v = (valid && !chosen) ? l : -INFINITY;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+        const uint64_t cand = __ballot(valid && !chosen && l == v);
+        const int best = __ffsll((unsigned long long)cand) - 1;
+        chosen = chosen || e == best;
+        if (j == 0) mx0 = v;
+    }
+    const float ex = chosen ? expf(l - mx0) : 0.f;
+    uint64_t mask = __ballot(chosen);
+    float den = 0.f;
+    while (mask) {
+        const int b = __ffsll((unsigned long long)mask) - 1;
+        den += __shfl(ex, b, 64);
+        mask &= mask - 1;
+    }
+    if (valid) {
+        if (logits_row) logits_row[e] = l;
+        gates_row[e] = chosen ? ex / den : 0.f;
+    }
+}
+
+// Gates from float32 logits [m, E]: one wave per token.
 __global__ __launch_bounds__(EW_THREADS) void moe_gates_kernel(const float* logits, float* gates, int m, int E,
                                                                int top_k) {
-    const int t = blockIdx.x * EW_THREADS + threadIdx.x;
-    if (t >= m) return;
-    const float* lg = logits + (size_t)t * E;
-    float* g = gates + (size_t)t * E;
-    uint64_t chosen = 0;                            // bit e: expert e selected (E <= 64)
-    float mx = 0.f;
-    for (int j = 0; j < top_k; ++j) {
-        int best = -1;
-        for (int e = 0; e < E; ++e)
-            if (!((chosen >> e) & 1) && (best < 0 || lg[e] > lg[best])) best = e;
-        chosen |= uint64_t(1) << best;
-        if (j == 0) mx = lg[best];
-    }
-    float den = 0.f;
-    for (int e = 0; e < E; ++e)
-        if ((chosen >> e) & 1) den += expf(lg[e] - mx);
-    for (int e = 0; e < E; ++e) g[e] = ((chosen >> e) & 1) ? expf(lg[e] - mx) / den : 0.f;
+    const int t = blockIdx.x * (EW_THREADS / 64) + (threadIdx.x >> 6);
+    if (t >= m) return;                             // whole waves
+    const int e = threadIdx.x & 63;
+    const float l = e < E ? logits[(size_t)t * E + e] : 0.f;
+    route_wave(l, E, top_k, nullptr, gates + (size_t)t * E);
 }
 
 hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t s) {
-    hipLaunchKernelGGL(moe_gates_kernel, dim3((m + EW_THREADS - 1) / EW_THREADS), dim3(EW_THREADS), 0, s, logits,
-                       gates, m, E, top_k);
+    constexpr int per = EW_THREADS / 64;
+    hipLaunchKernelGGL(moe_gates_kernel, dim3((m + per - 1) / per), dim3(EW_THREADS), 0, s, logits, gates, m, E,
+                       top_k);
+    return hipGetLastError();
+}
+
+// Router logits and gates of a few tokens in one launch: one workgroup per
+// token forms its E logits (u[t] . W_router[e], bf16 products summed in
+// float32: each thread over 8-element chunks tid, tid + 256, ..., then the
+// wave's lanes, then the 4 waves in order) and its first wave routes them.
+template <int EM>
+__global__ __launch_bounds__(EW_THREADS) void moe_router_kernel(const uint16_t* u, const uint16_t* w, float* logits,
+                                                                float* gates, int H, int E, int top_k) {
+    __shared__ float red[EW_THREADS / 64][EM];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint16_t* x = u + (size_t)t * H;
+    float acc[EM];
+#pragma unroll
+    for (int e = 0; e < EM; ++e) acc[e] = 0.f;
+    for (int c = tid; c < H / 8; c += EW_THREADS) {
+        const uint4 xv = reinterpret_cast<const uint4*>(x)[c];
+#pragma unroll
+        for (int e = 0; e < EM; ++e) {
+            if (e < E) {
+                const uint4 wv = reinterpret_cast<const uint4*>(w + (size_t)e * H)[c];
+                acc[e] = dot2_bf16(xv.x, wv.x, acc[e]);
+                acc[e] = dot2_bf16(xv.y, wv.y, acc[e]);
+                acc[e] = dot2_bf16(xv.z, wv.z, acc[e]);
+                acc[e] = dot2_bf16(xv.w, wv.w, acc[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+        if (e < E) {
+            float v = acc[e];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+            if (lane == 0) red[wave][e] = v;
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float l = 0.f;
+    if (lane < E) {
+#pragma unroll
+        for (int wv = 0; wv < EW_THREADS / 64; ++wv) l += red[wv][lane];
+    }
+    route_wave(l, E, top_k, logits + (size_t)t * E, gates + (size_t)t * E);
+}
+
+hipError_t moe_router_launch(const void* u, const void* w_router, float* logits, float* gates, int m, int H, int E,
+                             int top_k, hipStream_t s) {
+    const uint16_t* uu = reinterpret_cast<const uint16_t*>(u);
+    const uint16_t* ww = reinterpret_cast<const uint16_t*>(w_router);
+    if (E <= 8)
+        hipLaunchKernelGGL(moe_router_kernel<8>, dim3(m), dim3(EW_THREADS), 0, s, uu, ww, logits, gates, H, E, top_k);
+    else if (E <= 16)
+        hipLaunchKernelGGL(moe_router_kernel<16>, dim3(m), dim3(EW_THREADS), 0, s, uu, ww, logits, gates, H, E, top_k);
+    else if (E <= 32)
+        hipLaunchKernelGGL(moe_router_kernel<32>, dim3(m), dim3(EW_THREADS), 0, s, uu, ww, logits, gates, H, E, top_k);
+    else
+        hipLaunchKernelGGL(moe_router_kernel<64>, dim3(m), dim3(EW_THREADS), 0, s, uu, ww, logits, gates, H, E, top_k);
     return hipGetLastError();
 }
 

@@ -113,6 +113,11 @@ hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
 // and a[t, e * cols + i] *= gates[t, e] on bf16 expert activations
 // (cols a multiple of 8).
 hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t stream);
+// Router logits (written when logits is not null) and gates of m tokens in one
+// launch, from bf16 u [m, H] and W_router [E, H] (H a multiple of 8; few
+// tokens: one workgroup each reads all of W_router).
+hipError_t moe_router_launch(const void* u, const void* w_router, float* logits, float* gates, int m, int H, int E,
+                             int top_k, hipStream_t stream);
 hipError_t moe_scale_launch(void* a, const float* gates, int m, int E, int64_t cols, hipStream_t stream);
 
 // Block KV append: k, v columns of rows [batch * seq] of a [q | k | v] buffer

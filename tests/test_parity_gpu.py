@@ -349,6 +349,9 @@ MOE_CASES = [
     (512, 1024, 4, 2, 2, 5),
     (1024, 2816, 8, 2, 2, 16),
     (1024, 2048, 8, 1, 4, 3),
+    # the router's widest expert counts (64 experts, top 8; 32), and more tokens than the fused router
+    # launch takes (logits from a projection, gates from their own kernel)
+    (256, 256, 64, 8, 2, 7), (256, 512, 32, 2, 1, 33), (256, 512, 16, 4, 2, 80),
 ]
 
 
@@ -407,6 +410,33 @@ def test_moe_shard_bf16(case):
         check(f"rank{r} MoE partial", host(parts[r]), sr["partial"], TOL["bf16"])
     yref = L.moe_block(x, gamma, w_router, experts, k, gates=g0)["y"]
     check(f"sum of {t} MoE partials", host(out), yref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("m", [9, 70])
+def test_moe_router_ties(m):
+    """Experts with identical router rows get identical logits; the lower index wins the tie, on the fused
+    router (9 tokens) and on the projection + gates path (70 tokens)."""
+    H, I, E, k = 256, 256, 8, 3
+    x, gamma, w_router, experts = moe_inputs(91, H, I, E, m)
+    w_router = w_router.copy()
+    w_router[:, 2] = w_router[:, 1]                  # experts 1 and 2 tie
+    w_router[:, 6] = w_router[:, 5]                  # experts 5 and 6 tie
+    desc = tp.make_desc(H, I)
+    p = tp.tp_shard_plan(desc, 1, 0)
+    wg, wu, wd = moe_rank_phys(experts, p)
+    w = {"norm": dev(gamma, "bf16"), "w_router": dev(phys(w_router), "bf16"), "w_gate": dev(wg, "bf16"),
+         "w_up": dev(wu, "bf16"), "w_down": dev(wd, "bf16")}
+    part = empty((m, H), torch.float32)
+    g = empty((m, E), torch.float32)
+    lg = empty((m, E), torch.float32)
+    tp.tp_moe_shard_forward(w, dev(x, "bf16"), part, E, k, p.inter_cols, gates=g, logits=lg)
+    torch.cuda.synchronize()
+    lg0, g0 = host(lg), host(g)
+    assert np.array_equal(lg0[:, 1], lg0[:, 2]) and np.array_equal(lg0[:, 5], lg0[:, 6])
+    g_ref = L.moe_route(lg0, k)
+    assert np.array_equal(g0 > 0, g_ref > 0), "top-k selection differs"
+    assert np.max(np.abs(g0 - g_ref)) < 1e-5
+    assert np.all(np.count_nonzero(g0, axis=1) == k)
 
 
 # ---------------------------------------------------------------- ragged and edge shapes
