@@ -299,3 +299,18 @@ def test_layer_validation():
 def test_workspace_sizes_are_zero_for_bad_args():
     assert tp.tp_linear_workspace_bytes(0, 8, 8, tp.TP_BF16, 0) == 0
     assert tp.tp_attention_workspace_bytes(1, 3, 2, 128, 10) == 0
+
+
+def test_linear_workspace_follows_the_k_split_rule():
+    """Decode projections whose row tiles fill the chip keep all of K in one workgroup and need no
+    workspace; narrower ones, or K beyond one workgroup's reach, split K and need room for the slices."""
+    BF = tp.TP_BF16
+    for m, k, n in [(16, 3584, 4096),     # Llama-3-8B down (t=4): 256 tiles of 16 rows
+                    (16, 2048, 8192),     # 70B W_o (t=4): 256 tiles of 32 rows
+                    (16, 1024, 8192)]:    # 70B W_o (t=8)
+        assert tp.tp_linear_workspace_bytes(m, k, n, BF, 0) == 0, (m, k, n)
+    for m, k, n in [(16, 8192, 2560),     # 70B QKV (t=4): tiles of 10 rows would be too short
+                    (16, 8192, 1280),     # 70B QKV (t=8)
+                    (16, 8200, 8192),     # K past one workgroup's 8192
+                    (16, 57344, 4096)]:   # the stacked Mixtral down projection
+        assert tp.tp_linear_workspace_bytes(m, k, n, BF, 0) > 0, (m, k, n)
