@@ -45,7 +45,8 @@ struct GemvPlan {
     int mfma;      // 1: matrix-core kernel (bf16, 16-token blocks), 0: v_dot2 / fma kernel
     int mt;        // tokens per block (1, 2, 4, 8, 16)
     int nw;        // waves per workgroup
-    int rg, ks;    // matrix-core kernel: waves per K range (16 rows each), K ranges per workgroup
+    int rg, ks;    // matrix-core kernels: (4, 1) 64-row tiles split over workgroups, (2, 2) two K ranges of
+                   // 2 waves; (2, 4) and (1, 8) the wide kernel's 32- and 16-row tiles, 8 waves, one K range each
     int mblocks;   // ceil(m / mt)
     int mb_per_launch;  // m-blocks per launch, so a launch's tiles fit the counter header
     int rows_per_tile;  // weight rows a workgroup covers

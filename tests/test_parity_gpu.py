@@ -446,7 +446,7 @@ LINEAR_CASES = [
     (1, 8, 1, "bf16"), (3, 264, 130, "bf16"), (5, 4104, 77, "bf16"), (16, 8200, 300, "bf16"),
     (2, 16384, 64, "bf16"), (9, 1032, 257, "bf16"), (17, 520, 96, "bf16"), (40, 136, 40, "bf16"),
     (1, 4, 3, "f32"), (7, 260, 33, "f32"), (16, 1028, 129, "f32"), (33, 64, 40, "f32"), (4, 6148, 70, "f32"),
-    # wide outputs: K split over the wave groups of one workgroup, ragged n and K, K shorter than one
+    # wide outputs: K split over the 8 waves of one workgroup, ragged n and K, K shorter than one
     # stage, the longest K ranges (8192), and the fallbacks to 64-row tiles split over workgroups
     (16, 4096, 2040, "bf16"), (5, 2056, 6200, "bf16"), (12, 200, 4100, "bf16"), (16, 8200, 6150, "bf16"),
     (16, 8192, 6152, "bf16"), (7, 16384, 2100, "bf16"), (9, 1032, 8200, "bf16"), (5, 17000, 1030, "bf16"),
