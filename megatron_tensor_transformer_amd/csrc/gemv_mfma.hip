@@ -300,7 +300,7 @@ __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
     const int tile = blockIdx.x, mb = d.mb0 + blockIdx.z;
     const int K = a.K, N = a.N;
-    const int kw = wave * (NST * WD_SUB);       // first K element of this wave's range
+    const int kw = (blockIdx.y * WD_NW + wave) * (NST * WD_SUB);   // first K element of this wave's range
     const int m0 = mb * SK_MT;
     const int mvalid = min(SK_MT, a.m - m0);
     const int col = lane & 15, kg = lane >> 4;
@@ -432,28 +432,40 @@ __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
         ssl[0][tid] = v;
     }
     __syncthreads();
+    if (d.splits > 1) {
+        // K split over workgroups: this split's slice goes out with plain
+        // stores; the merge kernel that follows adds the slices in split
+        // order and runs the epilogue.
+        const int tile_id = blockIdx.z * d.n_tiles + tile;
+        const size_t sl = (size_t)tile_id * d.splits + blockIdx.y;
+        float* mine = d.part + sl * (SK_MT * ROWS);
+        for (int e = tid; e < mvalid * ROWS; e += NT) mine[e] = res[e];
+        if (NORM && tid < mvalid) d.ssq[sl * SK_MT + tid] = ssl[0][tid];
+        return;
+    }
     gemv_epilogue<uint16_t, SK_MT, ROWS, EPI, NORM, NT>(a, res, ssl[0], tile, m0, mvalid, opt);
 }
 
 // Split-K merge: one workgroup per output tile adds the tile's slices in
 // split order (a thread requests the slices of its outputs together) and runs
 // the epilogue.
-template <int EPI, bool NORM>
+template <int EPI, bool NORM, int RPT>
 __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
     // The plan splits K about four ways, so one batch of loads usually
     // covers every slice; the squared-sum slices of a fused RMSNorm travel in
-    // the same batch.
-    constexpr int NT = 256, PER = SK_MT * SK_RPT / NT, UNR = 4;
-    __shared__ float res[SK_MT * SK_RPT];
+    // the same batch. RPT: rows of a slice (64 from the narrow kernel, 32
+    // from the wide kernel split over workgroups).
+    constexpr int NT = 256, PER = SK_MT * RPT / NT, UNR = 4;
+    __shared__ float res[SK_MT * RPT];
     __shared__ float ssl[SK_MT];
     const int tid = threadIdx.x, tile = blockIdx.x, mb = d.mb0 + blockIdx.z;
     const int m0 = mb * SK_MT;
     const int mvalid = min(SK_MT, d.a.m - m0);
     const int S = d.splits;
     const int tile_id = blockIdx.z * d.n_tiles + tile;
-    const float* base = d.part + (size_t)tile_id * S * (SK_MT * SK_RPT);
+    const float* base = d.part + (size_t)tile_id * S * (SK_MT * RPT);
     const float* sqb = NORM ? d.ssq + (size_t)tile_id * S * SK_MT + min(tid, mvalid - 1) : nullptr;
-    const int live = mvalid * SK_RPT;
+    const int live = mvalid * RPT;
     float acc[PER], sq = 0.f;
 #pragma unroll
     for (int p = 0; p < PER; ++p) acc[p] = 0.f;
@@ -466,7 +478,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
         for (int p = 0; p < PER; ++p)
 #pragma unroll
             for (int u = 0; u < UNR; ++u)
-                v[p][u] = base[(size_t)min(sp0 + u, S - 1) * (SK_MT * SK_RPT) + min(tid + p * NT, live - 1)];
+                v[p][u] = base[(size_t)min(sp0 + u, S - 1) * (SK_MT * RPT) + min(tid + p * NT, live - 1)];
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
             if (sp0 + u < S) {
@@ -479,7 +491,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
     for (int p = 0; p < PER; ++p) res[tid + p * NT] = acc[p];
     if (NORM && tid < mvalid) ssl[tid] = sq;
     __syncthreads();
-    gemv_epilogue<uint16_t, SK_MT, SK_RPT, EPI, NORM, NT>(d.a, res, ssl, tile, m0, mvalid);
+    gemv_epilogue<uint16_t, SK_MT, RPT, EPI, NORM, NT>(d.a, res, ssl, tile, m0, mvalid, d.opt);
 }
 
 constexpr int64_t WIDE_MIN_ROWS = 16;          // rows of the shortest wide tile
@@ -551,6 +563,38 @@ GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
     while (kc < SK_MAX_STAGES * SK_SUB && wgs(kc) > lim) kc *= 2;
     while (kc > SK_SUB && wgs(kc) < 128 && wgs(kc / 2) <= lim) kc /= 2;
     while (kc > SK_SUB && kc / 2 >= K) kc /= 2;   // no stage past the end of K
+    // When that chunk is 1024 or shorter, a workgroup spends much of its time
+    // filling and draining; 8-wave workgroups of 16 to 32 rows stream longer
+    // K ranges: K split S ways (2 to 16), the fewest splits whose tiles,
+    // sized to about 256 workgroups, hold at least WIDE_MIN_ROWS rows and
+    // leave no split without K to cover; the merge kernel adds the slices.
+    // The 70B QKV shard at t=8 (1280 rows, K 8192): 4 splits of 20-row
+    // tiles, 557 -> 546 us per layer step; at t=4 (chunk 2048) two splits
+    // of 20-row tiles measured 1 us per step slower, so it stays here.
+    // SwiGLU keeps the 64-row tiles.
+    if (!swi && kc <= 4 * SK_SUB) {
+        for (int S2 = 2; S2 <= 16; S2 *= 2) {
+            const int64_t want2 = std::max<int64_t>(1, 256 / (mb * S2));
+            const int64_t per2 = (N + want2 - 1) / want2;
+            if (per2 > 32) break;               // more splits only lengthen the tiles
+            int kc2 = SK_SUB;
+            while (kc2 * 4 * S2 < K) kc2 *= 2;  // a workgroup covers 4 kc2 elements of K
+            if (kc2 > SK_MAX_STAGES * SK_SUB) continue;      // K too long for S2 splits
+            if (per2 < WIDE_MIN_ROWS || (int64_t)(S2 - 1) * 4 * kc2 >= K) continue;   // tiles too short, or a split idle
+            p.rg = 2;
+            p.ks = 4;
+            p.nw = WD_NW;
+            p.threads = WD_NW * 64;
+            p.rows_per_tile = 32;
+            p.out_per_tile = (int)per2;
+            p.n_tiles = (N + p.out_per_tile - 1) / p.out_per_tile;
+            p.kc = kc2;
+            p.splits = S2;
+            const size_t tl = (size_t)p.n_tiles * p.mb_per_launch;
+            p.ws_bytes = (tl * S2 * SK_MT * 32 * 4 + 255) / 256 * 256 + (tl * S2 * SK_MT * 4 + 255) / 256 * 256;
+            return p;
+        }
+    }
     const int S = (K + kc - 1) / kc;
     p.kc = kc;
     p.splits = S;
@@ -576,7 +620,8 @@ static hipError_t mfma_launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p.splits > 1) {
-            hipLaunchKernelGGL((gemv_mfma_merge_kernel<EPI, NORM>), dim3(p.n_tiles, 1, grid.z), dim3(256), 0, s, dl);
+            constexpr int SR = RG * KS == WD_NW ? 16 * RG : SK_RPT;     // rows of a slice
+            hipLaunchKernelGGL((gemv_mfma_merge_kernel<EPI, NORM, SR>), dim3(p.n_tiles, 1, grid.z), dim3(256), 0, s, dl);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -607,7 +652,7 @@ static hipError_t mfma_launch_shape(const GemvDev& d, const GemvPlan& p, hipStre
 }
 
 hipError_t gemv_mfma_launch(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
-    if (p.splits > 1 && p.ks != 1) return hipErrorInvalidValue;
+    if (p.splits > 1 && p.ks != 1 && p.rg * p.ks != WD_NW) return hipErrorInvalidValue;
     const bool nrm = d.a.norm != 0;
     switch (d.a.epi) {
         case EPI_STORE:

@@ -459,6 +459,10 @@ LINEAR_CASES = [
     # ragged; 10), and the 70B QKV shard shapes at t=4 and t=8 (K ending inside a stage) that stay on
     # 64-row tiles split over workgroups
     (16, 1032, 3300, "bf16"), (16, 8192, 2560, "bf16"), (16, 4104, 1280, "bf16"), (7, 1032, 1500, "bf16"),
+    # 8-wave tiles of 16 to 32 rows with K split over workgroups and merged (where 64-row tiles would
+    # stream chunks of 1024 or less): the 70B QKV shard at t=8, ragged n with K ending inside the second
+    # split; and the t=8 shape at 20 tokens, which takes the prefill GEMM
+    (16, 8192, 1280, "bf16"), (16, 6000, 2600, "bf16"), (20, 8192, 1280, "bf16"),
     # prefill GEMM with one to three K tiles (the pipeline's prologue alone), ragged and not
     (17, 8, 3, "bf16"), (20, 24, 50, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"), (300, 104, 520, "bf16"),
 ]
