@@ -241,7 +241,7 @@ __global__ __launch_bounds__(RG * KS * 64) void gemv_mfma_kernel(GemvDev d) {
 // (32 or 16) weight rows over all of K (for SwiGLU the gate and up rows of
 // ROWS / 2 outputs); wave w takes the w-th eighth of K in stages of 128
 // elements. Each wave moves its stage of weights (ROWS rows x 256 bytes) from
-// HBM into its own LDS tile by DMA, two tiles alternating, and reads its
+// HBM into its own ring of LDS tiles by DMA (two for 32 rows, four for 16), and reads its
 // activation operands straight from memory (the 16 tokens' rows stay in L2;
 // their bytes are 16 / ROWS of the weights'). No wave waits for another until
 // the K ranges' sums meet in LDS, and no weight passes through registers on
