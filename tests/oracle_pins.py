@@ -103,6 +103,22 @@ def pin_workload_shapes(rank_plan, ModelDesc):
     assert p["weight_elems"] == 855_638_016 // 8
 
 
+def pin_layer_weight_elements(layer_weight_elements, rank_plan, ModelDesc):
+    """One layer's projection weights: hand-evaluated counts for two public shapes, and the rank
+    shards partitioning them (no kv-head replication)."""
+    # 70B shape: 8192*(64+2*8)*128 (QKV) + 64*128*8192 (W_o) + 3*8192*28672 (gate, up, down)
+    d70 = ModelDesc(hidden=8192, intermediate=28672, n_q_heads=64, n_kv_heads=8, head_dim=128)
+    assert layer_weight_elements(d70) == 855_638_016
+    # Llama-3-8B shape: 4096*(32+2*8)*128 + 32*128*4096 + 3*4096*14336
+    d8 = ModelDesc(hidden=4096, intermediate=14336, n_q_heads=32, n_kv_heads=8, head_dim=128)
+    assert layer_weight_elements(d8) == 218_103_808
+    # an MLP-only block has no attention weights
+    assert layer_weight_elements(ModelDesc(hidden=256, intermediate=1024)) == 3 * 256 * 1024
+    for desc in (d70, d8):
+        for t in (1, 2, 4, 8):
+            assert sum(rank_plan(desc, t, r)["weight_elems"] for r in range(t)) == layer_weight_elements(desc)
+
+
 def pin_plan_errors(rank_plan, ModelDesc, PlanError):
     bad = [
         (ModelDesc(hidden=8, intermediate=8), 0, 0, "RANK"),
@@ -175,6 +191,22 @@ def pin_mlp_vs_naive(mlp_block):
         ref = naive.mlp(d["x"], d["w_gate"], d["w_up"], d["w_down"], d.get("gamma"), 1e-5)
         got = mlp_block(d["x"], d["w_gate"], d["w_up"], d["w_down"], d.get("gamma"), 1e-5)["y"]
         assert relerr(got, ref) < 1e-13, relerr(got, ref)
+
+
+def pin_attn_proj_block(attn_proj_block):
+    """QKV projections of x and W_o applied to a separate attention output, against the pure-Python
+    product. x and the attention output have the same shape but different values, and W_k, W_v differ,
+    so feeding x to W_o or swapping K and V disagrees with the loop."""
+    x = W.normal(71, 0, (3, 8))
+    attn_in = W.normal(71, 1, (3, 8))
+    w_q = W.normal(71, 2, (8, 8), 0.5)
+    w_k = W.normal(71, 3, (8, 4), 0.5)
+    w_v = W.normal(71, 4, (8, 4), 0.5)
+    w_o = W.normal(71, 5, (8, 8), 0.5)
+    got = attn_proj_block(x, attn_in, w_q, w_k, w_v, w_o)
+    for name, a, w in (("q", x, w_q), ("k", x, w_k), ("v", x, w_v), ("y", attn_in, w_o)):
+        ref = naive.matmul(a, w)
+        assert relerr(got[name], ref) < 1e-14, name
 
 
 def tiny_attention(seed=11, B=2, H=12, n_q=4, n_kv=2, d=3, cap=6):

@@ -51,12 +51,17 @@ def _all_sharded_pins():
     P.pin_sharded_layer(S.sharded_layer, L.layer)
 
 
+def _all_proj_pins():
+    P.pin_attn_proj_block(L.attn_proj_block)
+
+
 def _all_plan_pins():
     P.pin_kv_worked_example(plan.kv_elements_per_sequence, plan.kv_bytes_per_gpu)
     P.pin_weight_footprint(plan.weight_bytes_per_gpu)
     P.pin_head_blocks(plan.rank_plan, plan.ModelDesc)
     P.pin_workload_shapes(plan.rank_plan, plan.ModelDesc)
     P.pin_plan_errors(plan.rank_plan, plan.ModelDesc, plan.PlanError)
+    P.pin_layer_weight_elements(plan.layer_weight_elements, plan.rank_plan, plan.ModelDesc)
 
 
 _orig_rank_plan = plan.rank_plan
@@ -125,6 +130,21 @@ def _append_block_token_major(kc, vc, kn, vn, kv_len, n_kv, d):
 
 def _rank_attention_prefill_no_norm(x, w_q, w_k, w_v, w_o, kc, vc, kv_len, n_q, n_kv, d, p, gamma=None, eps=1e-5):
     return _orig_rank_attention_prefill(x, w_q, w_k, w_v, w_o, kc, vc, kv_len, n_q, n_kv, d, p, None, eps)
+
+
+def _attn_proj_x_to_wo(x, attn_in, w_q, w_k, w_v, w_o):
+    # feeds the layer input to W_o instead of the attention output
+    return {"q": L.linear(x, w_q), "k": L.linear(x, w_k), "v": L.linear(x, w_v), "y": L.linear(x, w_o)}
+
+
+def _attn_proj_kv_swapped(x, attn_in, w_q, w_k, w_v, w_o):
+    return {"q": L.linear(x, w_q), "k": L.linear(x, w_v), "v": L.linear(x, w_k), "y": L.linear(attn_in, w_o)}
+
+
+def _layer_weights_one_kv(desc):
+    # counts the kv heads once (K only) in the QKV weights
+    H, d = desc.hidden, desc.head_dim
+    return H * (desc.n_q_heads + desc.n_kv_heads) * d + desc.n_q_heads * d * H + 3 * H * desc.intermediate
 
 
 _orig_moe_route = L.moe_route
@@ -240,6 +260,8 @@ MUTATIONS = {
     "moe_route_picks_smallest": (L, "moe_route", _moe_route_smallest, _all_moe_pins),
     "moe_route_ties_to_higher_index": (L, "moe_route", _moe_route_ties_high, _all_moe_pins),
     "rank_moe_ignores_gate_weights": (S, "rank_moe", _rank_moe_no_gates, _all_moe_pins),
+    "attn_proj_feeds_x_to_w_o": (L, "attn_proj_block", _attn_proj_x_to_wo, _all_proj_pins),
+    "attn_proj_swaps_k_and_v": (L, "attn_proj_block", _attn_proj_kv_swapped, _all_proj_pins),
     # decomposition
     "sum_drops_last_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
         [np.asarray(p, float) for p in parts[:-1]] or [np.zeros_like(parts[0])], axis=0)
@@ -256,6 +278,7 @@ MUTATIONS = {
                             plan.kv_elements_per_sequence(L_, h, d, s) * b * B, _all_plan_pins),
     "weights_not_divided": (plan, "weight_bytes_per_gpu", lambda total, t: total, _all_plan_pins),
     "heads_shifted": (plan, "rank_plan", _plan_shift_heads, _all_plan_pins),
+    "layer_weights_count_kv_once": (plan, "layer_weight_elements", _layer_weights_one_kv, _all_plan_pins),
     "inter_block_swapped": (plan, "rank_plan", _plan_wrong_inter, _all_sharded_pins),
     "kv_replicated_round_robin": (plan, "rank_plan", _plan_replicate_round_robin, _all_sharded_pins),
 }

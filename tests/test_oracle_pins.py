@@ -120,3 +120,11 @@ def test_rank_moe():
 def test_kv_replication():
     P.pin_kv_replication(plan.rank_plan, plan.ModelDesc)
 
+
+
+def test_attn_proj_block():
+    P.pin_attn_proj_block(L.attn_proj_block)
+
+
+def test_layer_weight_elements():
+    P.pin_layer_weight_elements(plan.layer_weight_elements, plan.rank_plan, plan.ModelDesc)
