@@ -230,7 +230,8 @@ LayerWs layer_ws(const tp_model_desc* d, const tp_rank_plan* p, tp_stage stage, 
         const size_t l1 = linear_scratch(m, H, p->qkv_cols, dt, tpk::EPI_QKV, true);
         const size_t l2 = linear_scratch(m, p->o_rows, H, dt, tpk::EPI_PARTIAL, false);
         w.lin = l1 > l2 ? l1 : l2;
-        w.attn = round256(tpk::attn_plan((int)m, p->q_heads, p->kv_heads, d->head_dim, (int)d->seq_len).ws_bytes);
+        // sized for every kv_len up to the cache capacity
+        w.attn = round256(tpk::attn_ws_bound((int)m, p->q_heads, p->kv_heads, d->head_dim, (int)d->seq_len));
     } else {
         w.act1 = round256((size_t)m * p->inter_cols * esize(dt));  // SwiGLU output
         const size_t l1 = linear_scratch(m, H, p->inter_cols, dt, tpk::EPI_SWIGLU, true);
@@ -686,6 +687,13 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
             return run_linear(obuf, wts->w_o, nullptr, nullptr, 0.f, partial, m, plan->o_rows, H, dtype,
                               tpk::EPI_PARTIAL, cnt, lin, s);
         }
+        // Every check before the first launch: the attention plan of this kv_len
+        // must fit the scratch sized for the capacity.
+        const tpk::AttnPlan ap_len = tpk::attn_plan((int)m, plan->q_heads, plan->kv_heads, desc->head_dim,
+                                                    (int)kv->kv_len);
+        if (round256(ap_len.ws_bytes) > L.attn)
+            return fail(TP_ERR_WORKSPACE, "attention scratch of %zu bytes exceeds the %zu sized for capacity %lld",
+                        (size_t)round256(ap_len.ws_bytes), L.attn, (long long)kv->capacity);
         tpk::GemvArgs extra{};
         extra.k_cache = kv->k;
         extra.v_cache = kv->v;
@@ -701,8 +709,6 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         a.q = act1; a.k = kv->k; a.v = kv->v; a.out = obuf;
         a.capacity = kv->capacity; a.kv_len = (int)kv->kv_len;
         a.batch = (int)m; a.q_heads = plan->q_heads; a.kv_heads = plan->kv_heads; a.head_dim = desc->head_dim;
-        const tpk::AttnPlan ap_len = tpk::attn_plan(a.batch, a.q_heads, a.kv_heads, a.head_dim, a.kv_len);
-        if (round256(ap_len.ws_bytes) > L.attn) return fail(TP_ERR_WORKSPACE, "attention workspace too small");
         hipError_t e = tpk::attn_launch(a, ap_len, cnt, aws, s);
         if (e != hipSuccess) return hip_fail(e, "attention launch");
         return run_linear(obuf, wts->w_o, nullptr, nullptr, 0.f, partial, m, plan->o_rows, H, dtype,

@@ -347,6 +347,15 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(AttnDev d) {
     out[e] = (uint16_t)f32_to_bf16_bits(acc * s_inv);
 }
 
+// Scratch of n chunk partials per (sequence, kv head): running max and sum per
+// q head, then the unnormalised outputs; none for a single chunk.
+static size_t attn_chunk_bytes(long pairs, int n_chunks, int gq, int head_dim) {
+    if (n_chunks <= 1) return 0;
+    const size_t ml = ((size_t)pairs * n_chunks * gq * 2 * 4 + 255) / 256 * 256;
+    const size_t o = (size_t)pairs * n_chunks * gq * head_dim * 4;
+    return ml + (o + 255) / 256 * 256;
+}
+
 AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_len) {
     AttnPlan p{};
     const int gq = q_heads / kv_heads;
@@ -366,14 +375,21 @@ AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_le
     }
     p.chunk = passes_per_chunk * AT_PASS;
     p.n_chunks = n_chunks;
-    if (n_chunks > 1) {
-        const size_t ml = ((size_t)pairs * n_chunks * gq * 2 * 4 + 255) / 256 * 256;
-        const size_t o = (size_t)pairs * n_chunks * gq * head_dim * 4;
-        p.ws_bytes = ml + (o + 255) / 256 * 256;
-    } else {
-        p.ws_bytes = 0;
-    }
+    p.ws_bytes = attn_chunk_bytes(pairs, n_chunks, gq, head_dim);
     return p;
+}
+
+size_t attn_ws_bound(int batch, int q_heads, int kv_heads, int head_dim, int max_kv_len) {
+    // attn_plan's chunk count is at most the requested workgroups per (sequence,
+    // kv head), at most AT_MAX_CHUNKS and at most the passes of the longest
+    // cache; it is not monotone in kv_len, so bound it by all three.
+    const long pairs = (long)batch * kv_heads;
+    long n = (256 + pairs - 1) / pairs;
+    if (n < 1) n = 1;
+    if (n > AT_MAX_CHUNKS) n = AT_MAX_CHUNKS;
+    const long passes = (max_kv_len + AT_PASS - 1) / AT_PASS;
+    if (n > passes) n = passes;
+    return attn_chunk_bytes(pairs, (int)n, q_heads / kv_heads, head_dim);
 }
 
 template <int D, int GQ>

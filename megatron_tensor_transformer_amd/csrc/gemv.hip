@@ -82,7 +82,7 @@ __global__ __launch_bounds__(GEMV_NW * 64) void gemv_kernel(GemvDev d) {
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tile = blockIdx.x, split = blockIdx.y, mb = d.mb0 + blockIdx.z;
+    const int tile = d.tile0 + blockIdx.x, split = blockIdx.y, mb = d.mb0 + blockIdx.z;
     const int K = a.K, N = a.N;
     const int k0 = split * d.kc;
     const int klen = min(d.kc, K - k0);      // a multiple of VEC, at most XW
@@ -231,12 +231,19 @@ GemvPlan gemv_plan_dot2(int m, int K, int N, int is_bf16, int epi) {
     while (kc > 2 * step && (long)p.n_tiles * ((kround + kc - 1) / kc) * p.mblocks < target) kc -= step;
     int S = (K + kc - 1) / kc;
     p.mb_per_launch = p.mblocks;
+    p.tiles_per_launch = p.n_tiles;
     if (S > 1 && (size_t)p.n_tiles * p.mblocks > (size_t)WS_MAX_COUNTERS) {
-        // one counter per tile: run the m-blocks in launches that fit the header
-        p.mb_per_launch = WS_MAX_COUNTERS / p.n_tiles;
-        if (p.mb_per_launch < 1) p.mb_per_launch = 1;
+        // One counter per (tile, m-block) of a launch: run the m-blocks, and
+        // when the tiles alone are too many, ranges of tiles, in launches that
+        // fit the header.
+        if (p.n_tiles > WS_MAX_COUNTERS) {
+            p.tiles_per_launch = WS_MAX_COUNTERS;
+            p.mb_per_launch = 1;
+        } else {
+            p.mb_per_launch = WS_MAX_COUNTERS / p.n_tiles;
+        }
     }
-    const size_t tiles = (size_t)p.n_tiles * p.mb_per_launch;
+    const size_t tiles = (size_t)p.tiles_per_launch * p.mb_per_launch;
     p.kc = kc;
     p.splits = S;
     p.threads = GEMV_NW * 64;
@@ -277,12 +284,15 @@ static hipError_t launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
         lds_raised = true;
     }
     for (int mb0 = 0; mb0 < p.mblocks; mb0 += p.mb_per_launch) {
-        GemvDev dl = d;
-        dl.mb0 = mb0;
-        dim3 grid(p.n_tiles, p.splits, min(p.mb_per_launch, p.mblocks - mb0));
-        hipLaunchKernelGGL(kern, grid, dim3(p.threads), p.lds_bytes, s, dl);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        for (int t0 = 0; t0 < p.n_tiles; t0 += p.tiles_per_launch) {
+            GemvDev dl = d;
+            dl.mb0 = mb0;
+            dl.tile0 = t0;
+            dim3 grid(min(p.tiles_per_launch, p.n_tiles - t0), p.splits, min(p.mb_per_launch, p.mblocks - mb0));
+            hipLaunchKernelGGL(kern, grid, dim3(p.threads), p.lds_bytes, s, dl);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }
@@ -312,7 +322,7 @@ hipError_t gemv_launch(const GemvArgs& a, const GemvPlan& p, unsigned* counters,
     d.n_tiles = p.n_tiles;
     d.opt = p.out_per_tile;
     if (p.splits > 1) {
-        const size_t tiles = (size_t)p.n_tiles * p.mb_per_launch;
+        const size_t tiles = (size_t)p.tiles_per_launch * p.mb_per_launch;
         char* b = reinterpret_cast<char*>(scratch);
         const size_t part = (tiles * p.splits * p.mt * p.rows_per_tile * 4 + 255) / 256 * 256;
         d.cnt = counters;

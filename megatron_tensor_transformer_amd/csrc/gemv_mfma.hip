@@ -496,7 +496,7 @@ __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
 
 constexpr int64_t WIDE_MIN_ROWS = 16;          // rows of the shortest wide tile
 
-GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
+static GemvPlan plan_mfma(int m, int K, int N, int epi) {
     GemvPlan p{};
     p.mfma = 1;
     p.mt = SK_MT;
@@ -604,6 +604,12 @@ GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
         const size_t ssq = tl * S * SK_MT * 4;
         p.ws_bytes = (part + 255) / 256 * 256 + (ssq + 255) / 256 * 256;
     }
+    return p;
+}
+
+GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
+    GemvPlan p = plan_mfma(m, K, N, epi);
+    p.tiles_per_launch = p.n_tiles;             // slices are indexed by tile; no counters
     return p;
 }
 

@@ -13,7 +13,8 @@ struct GemvDev {
     int kc, splits, n_tiles;
     int opt;           // outputs per tile
     int mb0;           // first m-block of this launch
-    float* part;       // [tiles*mblocks][S][MT*RPT]
+    int tile0;         // first row tile of this launch (v_dot2 kernel)
+    float* part;       // [tiles*mblocks][S][MT*RPT], tiles and m-blocks of one launch
     float* ssq;        // [tiles*mblocks][S][MT]
     unsigned* cnt;     // [tiles*mblocks]
 };
@@ -125,7 +126,9 @@ __device__ __forceinline__ void gemv_finish(const GemvDev& d, float* res, float*
                                             int split, int m0, int mvalid) {
     const GemvArgs& a = d.a;
     const int tid = threadIdx.x;
-    const int tile_id = blockIdx.z * d.n_tiles + tile;
+    // slot of this (tile, m-block) among the launch's: the counters and slices
+    // of one launch never exceed the header and the scratch the plan sized
+    const int tile_id = blockIdx.z * gridDim.x + blockIdx.x;
     if (d.splits > 1) {
         float* base = d.part + (size_t)tile_id * d.splits * (MT * RPT);
         float* mine = base + (size_t)split * (MT * RPT);

@@ -49,6 +49,7 @@ struct GemvPlan {
                    // 2 waves; (2, 4) and (1, 8) the wide kernel's 32- and 16-row tiles, 8 waves, one K range each
     int mblocks;   // ceil(m / mt)
     int mb_per_launch;  // m-blocks per launch, so a launch's tiles fit the counter header
+    int tiles_per_launch;  // row tiles per launch (all of them unless the counters would not fit)
     int rows_per_tile;  // weight rows a workgroup covers
     int out_per_tile;   // outputs a workgroup covers
     int n_tiles;
@@ -96,6 +97,8 @@ struct AttnPlan {
     size_t ws_bytes;   // scratch bytes after the header; 0 when n_chunks == 1
 };
 AttnPlan attn_plan(int batch, int q_heads, int kv_heads, int head_dim, int kv_len);
+// Largest attn_plan(...).ws_bytes over every kv_len in 1..max_kv_len.
+size_t attn_ws_bound(int batch, int q_heads, int kv_heads, int head_dim, int max_kv_len);
 hipError_t attn_launch(const AttnArgs& a, const AttnPlan& p, unsigned* counters, void* scratch, hipStream_t stream);
 
 // Prefill projection on bf16 MFMA: y = epilogue(x @ W^T) for large m.

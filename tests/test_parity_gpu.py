@@ -13,6 +13,7 @@ import megatron_tensor_transformer_amd as tp
 import workloads as W
 from gpu_helpers import TOL, check, dev, host, phys, say
 from oracle import layer as L
+from oracle import plan as OP
 from oracle import sharded as S
 
 pytestmark = pytest.mark.gpu
@@ -183,17 +184,23 @@ def test_attn_projections_bf16():
 
 # ---------------------------------------------------------------- 70B-shaped MLP prefill, t=4, 4096 tokens
 
-@pytest.mark.timeout(600)
+def mlp_rows_f64(x, wg, wu, wd, chunk=1024):
+    """The MLP block of the oracle (float64, BLAS products) over row chunks of x."""
+    return np.concatenate([L.mlp_block(x[i:i + chunk], wg, wu, wd)["y"] for i in range(0, x.shape[0], chunk)])
+
+
+@pytest.mark.timeout(900)
 def test_mlp_prefill_bf16():
+    """Every row of every rank's partial and of their sum, at the full 70B-shaped prefill size."""
     wl = W.WORKLOADS[4]
     H, I, t, M = wl.hidden, wl.intermediate, wl.t, wl.tokens[0]
     say("drawing the 70B-shaped MLP weights")
     inp = W.mlp_inputs(4, H, I, M, "bf16")
     desc = tp.make_desc(H, I)
+    odesc = OP.ModelDesc(hidden=H, intermediate=I)
     x = dev(inp["x"], "bf16")
     rows = np.unique(np.concatenate([[0, 1, 2047, 2048, M - 1], np.random.default_rng(4).choice(M, 27, False)]))
-    xs = inp["x"][rows]
-    parts = []
+    parts, refs = [], []
     for r in range(t):
         p = tp.tp_shard_plan(desc, t, r)
         wg, wu, wd = [dev(a, "bf16") for a in mlp_rank_phys(inp, p)]
@@ -201,14 +208,25 @@ def test_mlp_prefill_bf16():
         tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, {"w_gate": wg, "w_up": wu, "w_down": wd}, x, part)
         torch.cuda.synchronize()
         del wg, wu, wd
-        rr = S.rank_mlp(xs, inp["w_gate"], inp["w_up"], inp["w_down"], tp.plan_dict(p))
-        check(f"rank{r} partial (sampled rows)", host(part)[rows], rr["partial"], TOL["bf16"])
+        # the rank's partial is the MLP block of its own column / row blocks (the oracle's planner slices)
+        op = OP.rank_plan(odesc, t, r)
+        b, c = op["inter_begin"], op["inter_cols"]
+        say(f"oracle: rank {r} over all {M} rows")
+        ref_r = mlp_rows_f64(inp["x"], L.f64(inp["w_gate"][:, b:b + c]), L.f64(inp["w_up"][:, b:b + c]),
+                             L.f64(inp["w_down"][b:b + c, :]))
+        check(f"rank{r} partial (all rows)", host(part), ref_r, TOL["bf16"])
+        if r == 0:
+            rr = S.rank_mlp(inp["x"][rows], inp["w_gate"], inp["w_up"], inp["w_down"], op)
+            check("rank0 partial (sampled rows, sharded oracle)", host(part)[rows], rr["partial"], TOL["bf16"])
         parts.append(part)
+        refs.append(ref_r)
     out = empty((M, H), torch.float32)
     tp.tp_partial_sum(parts, out)
     torch.cuda.synchronize()
-    ref = L.mlp_block(xs, inp["w_gate"], inp["w_up"], inp["w_down"])
-    check("sum of 4 partials (sampled rows)", host(out)[rows], ref["y"], TOL["bf16"])
+    # the rank-order float64 sum of the rank blocks equals the unsharded block (pinned on the oracle)
+    check("sum of 4 partials (all rows)", host(out), S.sum_partials(refs), TOL["bf16"])
+    ref = L.mlp_block(inp["x"][rows], inp["w_gate"], inp["w_up"], inp["w_down"])
+    check("sum of 4 partials (sampled rows, unsharded)", host(out)[rows], ref["y"], TOL["bf16"])
 
 
 # ---------------------------------------------------------------- 70B-shaped full layer decode, t=8
@@ -261,12 +279,20 @@ def test_full_layer_decode_bf16():
               TOL["bf16"])
         check(f"rank{r} appended v", host(vc)[:, :, S_ - 1], ref["attn"]["v_cache"][:, kb:kb + kn, S_ - 1],
               TOL["bf16"])
-    sr = S.rank_attention(a["x"], a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], S_, nq, nkv,
-                          d, tp.plan_dict(plans[0]), a["gamma"], wl.eps)
-    check("rank0 attention partial", host(attn_parts[0]), sr["partial"], TOL["bf16"])
-    check("h = x + sum of 8 attention partials", host(h), ref["h"], TOL["bf16"])
+    # every rank's partials against the sharded oracle (its own planner), then their sums before the residual
+    odesc = OP.ModelDesc(hidden=H, intermediate=I, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, seq_len=S_, batch=B)
+    hh = host(h)
+    for r in range(t):
+        op = OP.rank_plan(odesc, t, r)
+        sr = S.rank_attention(a["x"], a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], S_, nq,
+                              nkv, d, op, a["gamma"], wl.eps)
+        check(f"rank{r} attention partial", host(attn_parts[r]), sr["partial"], TOL["bf16"])
+        mr = S.rank_mlp(hh, w["w_gate"], w["w_up"], w["w_down"], op, w["gamma2"], wl.eps)
+        check(f"rank{r} MLP partial at the GPU's h", host(mlp_parts[r]), mr["partial"], TOL["bf16"])
+    check("sum of 8 attention partials", sum(host(q) for q in attn_parts), ref["attn"]["y"], TOL["bf16"])
+    check("h = x + sum of 8 attention partials", hh, ref["h"], TOL["bf16"])
     # the MLP stage against the oracle evaluated at the h the GPU produced
-    mref = L.mlp_block(host(h), w["w_gate"], w["w_up"], w["w_down"], w["gamma2"], wl.eps)
+    mref = L.mlp_block(hh, w["w_gate"], w["w_up"], w["w_down"], w["gamma2"], wl.eps)
     mparts = sum(host(q) for q in mlp_parts)
     check("sum of 8 MLP partials at the GPU's h", mparts, mref["y"], TOL["bf16"])
     check("layer output", host(out), ref["out"], TOL["bf16"])

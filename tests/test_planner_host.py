@@ -1,0 +1,69 @@
+"""The library's launch planners, queried on the host through a small C++ probe
+(tests/plan_probe.cpp, linked against libtpshard.so; no GPU call is made).
+
+- Split-K decode projections on the v_dot2 kernel keep one completion counter
+  per (row tile, m-block) of a launch: a launch must never use more counters
+  than the workspace header holds, however many row tiles the output has.
+- The decode attention's split-KV scratch depends on kv_len in a way that is
+  not monotone, so the layer workspace sizes it by a bound over every kv_len up
+  to the cache capacity; the bound must cover each kv_len.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "megatron_tensor_transformer_amd")
+
+
+@pytest.fixture(scope="module")
+def probe(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if not gxx:
+        pytest.skip("g++ not available")
+    exe = str(tmp_path_factory.mktemp("probe") / "plan_probe")
+    cmd = [gxx, "-O1", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I", os.path.join(PKG, "csrc"), os.path.join(ROOT, "tests", "plan_probe.cpp"), "-o", exe,
+           "-L", PKG, "-ltpshard", f"-Wl,-rpath,{PKG}", "-L/opt/rocm/lib", "-lamdhip64"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+
+    def run(lines):
+        r = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True, check=True,
+                           timeout=300)
+        out = []
+        for ln in r.stdout.splitlines():
+            out.append({k: int(v) for k, v in (kv.split("=") for kv in ln.split())})
+        assert len(out) == len(lines)
+        return out
+    return run
+
+
+def test_split_k_counters_fit_the_header(probe):
+    queries = []
+    for bf in (0, 1):
+        for epi in ((0, 1, 2, 3) if bf else (0, 1, 2)):
+            for m in (1, 2, 3, 4, 5, 8, 16):
+                for K in (256, 4096, 8192, 8200, 17000):
+                    for N in (8, 1000, 70000, 128256, 150000):
+                        queries.append((m, K, N, bf, epi))
+    plans = probe([f"gemv {m} {K} {N} {bf} {epi}" for m, K, N, bf, epi in queries])
+    big = 0
+    for q, p in zip(queries, plans):
+        assert 1 <= p["tiles_per_launch"] <= p["n_tiles"], (q, p)
+        if p["splits"] > 1 and not p["mfma"]:
+            assert p["tiles_per_launch"] * p["mb_per_launch"] <= p["header_counters"], (q, p)
+            # the scratch holds every slice of one launch
+            assert p["ws_bytes"] >= p["tiles_per_launch"] * p["mb_per_launch"] * p["splits"] * p["mt"] * \
+                p["rows_per_tile"] * 4, (q, p)
+            big += p["n_tiles"] > p["header_counters"]
+    assert big > 0      # the sweep reaches outputs with more row tiles than counters
+
+
+@pytest.mark.parametrize("batch,q_heads,kv_heads,head_dim,capacity", [
+    (16, 8, 1, 128, 2176), (1, 8, 1, 128, 66000), (16, 8, 1, 128, 8192), (20, 8, 1, 128, 3000),
+    (3, 4, 2, 64, 300), (40, 16, 2, 128, 1000), (2, 8, 8, 128, 9999)])
+def test_attention_scratch_bound_covers_every_kv_len(probe, batch, q_heads, kv_heads, head_dim, capacity):
+    (r,) = probe([f"attn {batch} {q_heads} {kv_heads} {head_dim} {capacity}"])
+    assert r["max_ws"] <= r["bound"], r
