@@ -1,31 +1,40 @@
 """Throughput of one GPU's tensor-parallel layer shards on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload mlp_decode|attn_proj|mlp_prefill|layer_decode] [--tokens M] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens M] [--no-cpu]
 
 Workloads (synthetic, seeded inputs already in HBM; every rank shard of the
 tensor-parallel group runs on the one device, then the on-device sum of the t
 partials):
 
-  mlp_decode (default)  Llama-3-8B-shaped MLP block, hidden 4096, intermediate
+  headline (default)    the metric's two halves on their largest single-GPU
+                        configurations, one JSON line: decode tokens/s and HBM
+                        GB/s of the 70B-shaped full layer decode (below,
+                        ``value``), and TFLOP/s of the 70B-shaped MLP prefill
+                        (below, under ``prefill``), plus the streaming-read
+                        rate of buffers the size of the decode launches.
+  layer_decode          70B-shaped full layer, t=8, batch 16, KV cache of 8192
+                        tokens: per rank RMSNorm + QKV (+ KV append), GQA decode
+                        attention, W_o partial; sum + residual; RMSNorm +
+                        gate/up + SwiGLU, down partial; sum + residual.
+  mlp_prefill           70B-shaped MLP block, hidden 8192, intermediate 28672,
+                        t=4, 4096 tokens (MFMA GEMMs); metric in TFLOP/s.
+  mlp_decode            Llama-3-8B-shaped MLP block, hidden 4096, intermediate
                         14336, t=4, 16 tokens, RMSNorm in front: per rank fused
                         RMSNorm + gate/up + SwiGLU, then the down row-partial.
   attn_proj             70B-shaped attention projections, hidden 8192, 64 q / 8
                         kv heads of 128, t=4, 16 tokens: per rank the QKV column
                         projection and the W_o row-partial.
-  mlp_prefill           70B-shaped MLP block, hidden 8192, intermediate 28672,
-                        t=4, 4096 tokens (MFMA GEMMs); metric in TFLOP/s.
-  layer_decode          70B-shaped full layer, t=8, batch 16, KV cache of 8192
-                        tokens: per rank RMSNorm + QKV (+ KV append), GQA decode
-                        attention, W_o partial; sum + residual; RMSNorm +
-                        gate/up + SwiGLU, down partial; sum + residual.
+  attn_prefill, layer_prefill, moe_decode
+                        the prefill attention shard, the full layer over
+                        2 x 2048 new tokens, the Mixtral-shaped MoE decode block.
+  hbm_read              the plain streaming-read rate alone.
 
 One step is one pass of that whole path; K steps are replayed from HIP graphs
 and timed between two events. Prints one JSON line. ``value`` is the step's
-throughput; ``roofline`` rates the dominant kernel by its algorithmic bytes
-(or flops) over its average duration, from HIP events around back-to-back
-launches on the stream it runs on; ``cpu_baseline`` times the float64 CPU
-oracle on a bounded sample of the same workload.
+throughput; ``roofline`` rates the dominant kernel (the longest, measured) by
+its algorithmic bytes (or flops) over its average duration, from HIP events
+around back-to-back launches on the stream it runs on; ``cpu_baseline`` times
+the float64 CPU oracle on a bounded sample of the same workload.
 
 ``--calibrate-copy`` adds a plain 256 MiB device copy before the timed region;
 hardware-counter runs use it to scale FETCH_SIZE / WRITE_SIZE to bytes.
@@ -60,9 +69,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mlp_decode",
-                    choices=["mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill",
-                             "layer_prefill", "moe_decode"])
+    ap.add_argument("--workload", default="headline",
+                    choices=["headline", "mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill",
+                             "layer_prefill", "moe_decode", "hbm_read"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of the timed step (default: the workload's)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true")
@@ -101,7 +110,7 @@ def main():
     torch = ctx.torch
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     torch.cuda.set_device(0)
-    bench = {"mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
+    bench = {"headline": bench_headline, "hbm_read": bench_hbm_read, "mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
              "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill,
              "layer_prefill": bench_layer_prefill, "moe_decode": bench_moe_decode}[args.workload]
     if args.calibrate_copy:
@@ -218,15 +227,21 @@ def projection_kernel(m, dtype="bf16", wide=False):
     return "gemv_kernel (v_dot2 decode projection)"
 
 
-def source_digest():
-    """Digest of the kernel sources; hardware-counter figures are only reported while it matches."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "megatron_tensor_transformer_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+def code_digest():
+    """Digest of the library's device code (the .hip_fatbin section of libtpshard.so): hardware-counter
+    figures are only reported while the kernels they were taken on are the ones loaded."""
+    import struct
+    path = os.path.join(ROOT, "megatron_tensor_transformer_amd", "libtpshard.so")
+    with open(path, "rb") as f:
+        data = f.read()
+    shoff = struct.unpack_from("<Q", data, 0x28)[0]
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    names = secs[shstrndx][4]
+    for name, _typ, _flags, _addr, off, size in secs:
+        if data[names + name:data.index(b"\0", names + name)] == b".hip_fatbin":
+            return hashlib.sha256(data[off:off + size]).hexdigest()[:16]
+    return None
 
 
 def counted_traffic(kernel_key):
@@ -246,7 +261,7 @@ def counted_traffic(kernel_key):
                 continue
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != source_digest():
+    if vals.get("code_digest") != code_digest():
         return None
     try:
         fetch_scale = COPY_BYTES / (float(vals["copy.FETCH_SIZE_KiB"]) * 1024.0)
@@ -283,6 +298,25 @@ def repeat_for(seconds, fn):
         el = time.perf_counter() - t0
         if el >= seconds:
             return n, el
+
+
+def time_legs(ctx, legs, unit, single_thread=()):
+    """Time each CPU leg {name: (fn, units per run)} for a bounded share of --cpu-seconds on the BLAS
+    threads, and the legs named in ``single_thread`` again on one thread."""
+    from threadpoolctl import threadpool_limits
+    runs = [(name, fn, per, None) for name, (fn, per) in legs.items()]
+    runs += [(name + "_1thread", legs[name][0], legs[name][1], 1) for name in single_thread]
+    share = ctx.args.cpu_seconds / len(runs)
+    out = {}
+    for name, fn, per, threads in runs:
+        if threads is None:
+            n, el = repeat_for(share, fn)
+        else:
+            with threadpool_limits(limits=threads):
+                n, el = repeat_for(share, fn)
+        out[name] = {unit: n * per / el, "runs": n, "seconds": el, "threads": threads or blas_threads()}
+        log(f"[bench] CPU oracle {name}: {out[name][unit]:.4g} {unit}")
+    return out
 
 
 def result(ctx, value, unit, ms_step, config, extra):
@@ -401,14 +435,27 @@ def bench_mlp_decode(ctx):
               "weight_copies_rotated": copies_n}
     res = result(ctx, M * args.steps / (total_ms * 1e-3), "tokens/s", ms_step, config, extra)
     if not args.no_cpu:
-        from oracle import sharded as S
+        from oracle import layer as L
+        from oracle import plan as OP
         xs = inp["x"][:M]
-        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
-        n, el = repeat_for(args.cpu_seconds, lambda: S.sharded_mlp(xs, inp["w_gate"], inp["w_up"], inp["w_down"], t,
-                                                                    inp["gamma"], wl.eps))
-        res["cpu_baseline"] = {"value": M * n / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-                               "sample": f"{n} full steps (all {t} rank shards in float64 + sum) of {M} tokens, "
-                                         f"{el:.1f} s"}
+        od = OP.ModelDesc(hidden=H, intermediate=I)
+
+        def rank(r):
+            op = OP.rank_plan(od, t, r)
+            b, c = op["inter_begin"], op["inter_cols"]
+            return L.mlp_block(xs, inp["w_gate"][:, b:b + c], inp["w_up"][:, b:b + c], inp["w_down"][b:b + c],
+                               inp["gamma"], wl.eps)["y"]
+
+        legs = time_legs(ctx, {"one_rank_shard": (lambda: rank(0), M),
+                               "all_ranks_and_sum": (lambda: sum(rank(r) for r in range(t)), M),
+                               "unsharded_block": (lambda: L.mlp_block(xs, inp["w_gate"], inp["w_up"], inp["w_down"],
+                                                                       inp["gamma"], wl.eps)["y"], M)},
+                         "tokens_per_s", single_thread=("one_rank_shard", "all_ranks_and_sum"))
+        res["cpu_baseline"] = {"value": legs["all_ranks_and_sum"]["tokens_per_s"], "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"float64 oracle (BLAS products), the whole step: all {t} rank shards + sum "
+                                         f"of {M} tokens; legs also one rank and the unsharded block, and on one "
+                                         f"thread", "legs": legs, "host": host_info()}
     return res
 
 
@@ -488,20 +535,36 @@ def bench_attn_proj(ctx):
     res = result(ctx, M * args.steps / (total_ms * 1e-3), "tokens/s", ms_step, config, extra)
     if not args.no_cpu:
         from oracle import layer as L
-        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
-        n, el = repeat_for(args.cpu_seconds, lambda: L.attn_proj_block(a["x"], attn_in, a["w_q"], a["w_k"], a["w_v"],
-                                                                        a["w_o"]))
-        res["cpu_baseline"] = {"value": M * n / el, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-                               "sample": f"{n} unsharded float64 projection blocks of {M} tokens (the sum of the "
-                                         f"{t} shards' work), {el:.1f} s"}
+        from oracle import plan as OP
+        od = OP.ModelDesc(hidden=H, n_q_heads=nq, n_kv_heads=nkv, head_dim=d)
+
+        def rank(r):
+            op = OP.rank_plan(od, t, r)
+            qs = slice(op["q_head_begin"] * d, (op["q_head_begin"] + op["q_heads"]) * d)
+            ks = slice(op["kv_head_begin"] * d, (op["kv_head_begin"] + op["kv_heads"]) * d)
+            return L.attn_proj_block(a["x"], attn_in[:, qs], a["w_q"][:, qs], a["w_k"][:, ks], a["w_v"][:, ks],
+                                     a["w_o"][qs, :])["y"]
+
+        legs = time_legs(ctx, {"one_rank_shard": (lambda: rank(0), M),
+                               "all_ranks_and_sum": (lambda: sum(rank(r) for r in range(t)), M),
+                               "unsharded_block": (lambda: L.attn_proj_block(a["x"], attn_in, a["w_q"], a["w_k"],
+                                                                             a["w_v"], a["w_o"]), M)},
+                         "tokens_per_s", single_thread=("one_rank_shard", "all_ranks_and_sum"))
+        res["cpu_baseline"] = {"value": legs["all_ranks_and_sum"]["tokens_per_s"], "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"float64 oracle (BLAS products), the whole step: all {t} rank shards + sum "
+                                         f"of {M} tokens; legs also one rank and the unsharded block, and on one "
+                                         f"thread", "legs": legs, "host": host_info()}
     return res
 
 
-def bench_mlp_prefill(ctx):
+def prefill_mlp_gpu(ctx):
+    """The 70B-shaped MLP prefill block: all t rank shards + the sum, graph-replayed; the gate/up and
+    down GEMMs of one rank timed with events. Returns (result fields, config, inputs)."""
     torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
     wl = W.WORKLOADS[4]
     H, I, t = wl.hidden, wl.intermediate, wl.t
-    M = args.tokens or wl.tokens[0]
+    M = args.tokens if (args.tokens and args.workload == "mlp_prefill") else wl.tokens[0]
     log(f"[bench] drawing {wl.name}")
     inp = W.mlp_inputs(4, H, I, M, "bf16")
     desc = tp.make_desc(H, I)
@@ -545,9 +608,11 @@ def bench_mlp_prefill(ctx):
     step_flops = t * (g_fl + d_fl)
     tflops = step_flops * args.steps / (total_ms * 1e-3) / 1e12
     g_tf = g_fl / (g_t[0] * 1e-3) / 1e12
-    extra = {
+    fields = {
+        "tflops": tflops, "ms_per_step": ms_step,
         "tokens_per_s": M * args.steps / (total_ms * 1e-3),
         "pct_mfma_peak": 100 * tflops / BF16_PEAK_TFLOPS,
+        "step_flops": step_flops,
         "per_rank": {"gateup_us": g_t[0] * 1e3, "gateup_TFLOPs": g_tf, "down_us": d_t[0] * 1e3,
                      "down_TFLOPs": d_fl / (d_t[0] * 1e-3) / 1e12, "flops": g_fl + d_fl},
         "roofline": {"kernel": projection_kernel(M) + ": gate/up + SwiGLU, one rank shard", "bound": "mfma",
@@ -557,25 +622,60 @@ def bench_mlp_prefill(ctx):
     }
     config = {"workload": f"70B-shaped MLP prefill block, all t={t} rank shards + on-device sum of partials",
               "hidden": H, "intermediate": I, "t": t, "tokens": M}
-    res = result(ctx, tflops, "TFLOP/s", ms_step, config, extra)
-    if not args.no_cpu:
-        from oracle import sharded as S
-        rows = 16
-        xs = inp["x"][:rows]
-        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
-        n, el = repeat_for(args.cpu_seconds, lambda: S.sharded_mlp(xs, inp["w_gate"], inp["w_up"], inp["w_down"], t))
-        res["cpu_baseline"] = {"value": n * t * 2.0 * rows * 3 * H * I_r / el / 1e12, "unit": "TFLOP/s",
+    return fields, config, inp
+
+
+def prefill_mlp_cpu(ctx, inp, rows=256):
+    """The float64 oracle on the prefill MLP block over the first ``rows`` tokens: (i) one rank's shard,
+    (ii) all t shards + the rank-order sum, (iii) the unsharded block; TFLOP/s of each."""
+    from oracle import layer as L
+    from oracle import plan as OP
+    wl = ctx.W.WORKLOADS[4]
+    H, I, t = wl.hidden, wl.intermediate, wl.t
+    xs = inp["x"][:rows]
+    od = OP.ModelDesc(hidden=H, intermediate=I)
+
+    def rank(r):
+        op = OP.rank_plan(od, t, r)
+        b, c = op["inter_begin"], op["inter_cols"]
+        return L.mlp_block(xs, inp["w_gate"][:, b:b + c], inp["w_up"][:, b:b + c], inp["w_down"][b:b + c])["y"]
+
+    fl_all = 6.0 * rows * H * I
+    legs = {
+        "one_rank_shard": (lambda: rank(0), fl_all / t),
+        "all_ranks_and_sum": (lambda: sum(rank(r) for r in range(t)), fl_all),
+        "unsharded_block": (lambda: L.mlp_block(xs, inp["w_gate"], inp["w_up"], inp["w_down"])["y"], fl_all),
+    }
+    out = {}
+    for name, (fn, fl) in legs.items():
+        n, el = repeat_for(ctx.args.cpu_seconds / 3, fn)
+        out[name] = {"TFLOPs": n * fl / el / 1e12, "runs": n, "seconds": el, "flops_per_run": fl}
+        log(f"[bench] CPU oracle, prefill MLP {name}: {out[name]['TFLOPs'] * 1e3:.2f} GFLOP/s")
+    return out, f"the first {rows} of the {inp['x'].shape[0]} tokens"
+
+
+def bench_mlp_prefill(ctx):
+    fields, config, inp = prefill_mlp_gpu(ctx)
+    extra = {k: v for k, v in fields.items() if k not in ("tflops", "ms_per_step")}
+    res = result(ctx, fields["tflops"], "TFLOP/s", fields["ms_per_step"], config, extra)
+    if not ctx.args.no_cpu:
+        legs, sample = prefill_mlp_cpu(ctx, inp)
+        res["cpu_baseline"] = {"value": legs["all_ranks_and_sum"]["TFLOPs"], "unit": "TFLOP/s",
                                "cores": blas_threads(), "kind": "oracle",
-                               "sample": f"{n} float64 steps (all {t} rank shards + sum) over the first {rows} of "
-                                         f"the {M} tokens, {el:.1f} s"}
+                               "sample": f"float64 oracle, all {config['t']} rank shards + sum over {sample}",
+                               "legs": legs, "host": host_info()}
     return res
 
 
-def bench_layer_decode(ctx):
+def decode_layer_gpu(ctx):
+    """The 70B-shaped layer decode (t=8, batch 16, KV 8192): every rank's attention stage, the sum with the
+    residual, every rank's MLP stage, the sum with the residual, graph-replayed. One rank's shard and each
+    of its projections and its attention are also timed with events, rotating over the t ranks' weights.
+    Returns (result fields, config, inputs)."""
     torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
     wl = W.WORKLOADS[5]
     H, I, nq, nkv, d, t, S_ = wl.hidden, wl.intermediate, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t, wl.kv_len
-    B = args.tokens or wl.tokens[0]
+    B = args.tokens if (args.tokens and args.workload == "layer_decode") else wl.tokens[0]
     log(f"[bench] drawing {wl.name}")
     a = W.attention_inputs(5, H, nq, nkv, d, B, S_, "bf16", "random")
     mi = W.mlp_inputs(5, H, I, B, "bf16", "random")
@@ -600,9 +700,7 @@ def bench_layer_decode(ctx):
     h = torch.empty(B, H, dtype=torch.bfloat16, device="cuda")
     out = torch.empty(B, H, dtype=torch.bfloat16, device="cuda")
     p0 = plans[0]
-    q = torch.empty(B, p0.q_heads * d, dtype=torch.bfloat16, device="cuda").normal_()
-    o = torch.empty_like(q)
-    aw = tp.workspace(tp.tp_attention_workspace_bytes(B, p0.q_heads, p0.kv_heads, d, S_))
+    qc, orows, I_r, kv_r, q_r = p0.qkv_cols, p0.o_rows, p0.inter_cols, p0.kv_heads, p0.q_heads
 
     def step(i):
         for r, p in enumerate(plans):
@@ -614,53 +712,213 @@ def bench_layer_decode(ctx):
             tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], h, parts[r], ws=ws)
         tp.tp_partial_sum(parts, out, residual=h)
 
-    def attn(i):
-        rw = ranks[i % t]
-        tp.tp_decode_attention(q, rw["k"], rw["v"], o, S_, p0.q_heads, ws=aw)
+    # one rank's pieces, each rotating over the t ranks' weights (2.3 GB in all: HBM, not the cache)
+    yq = torch.empty(B, qc, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(B, orows, dtype=torch.bfloat16, device="cuda").normal_()
+    o = torch.empty_like(q)
+    act = torch.empty(B, I_r, dtype=torch.bfloat16, device="cuda")
+    part = torch.empty(B, H, device="cuda")
+    hn = torch.empty(B, H, dtype=torch.bfloat16, device="cuda").normal_()
+    aw = tp.workspace(tp.tp_attention_workspace_bytes(B, q_r, kv_r, d, S_))
 
-    for i in range(16):
-        attn(i)
-    at = event_time_ms(torch, attn, max(4 * t, 32))
-    kv_bytes = 2 * B * p0.kv_heads * S_ * d * 2 + 2 * B * p0.q_heads * d * 2
-    log(f"[bench] attention {at[0] * 1e3:.2f} us ({kv_bytes / (at[0] * 1e-3) / 1e9:.0f} GB/s)")
+    def shard(i):
+        rw, p = ranks[i % t], plans[i % t]
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_ATTN, rw, x, parts[i % t],
+                                  kv={"k": rw["k"], "v": rw["v"], "kv_len": S_}, ws=ws)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, rw, hn, parts[i % t], ws=ws)
+
+    pieces = {
+        "qkv": (lambda i: tp.tp_column_linear(x, ranks[i % t]["w_qkv"], yq, gamma=g1, eps=wl.eps, ws=ws),
+                qc * H * 2 + B * H * 2 + H * 2 + B * qc * 2,
+                projection_kernel(B) + " + merge: RMSNorm + QKV column projection"),
+        "attention": (lambda i: tp.tp_decode_attention(q, ranks[i % t]["k"], ranks[i % t]["v"], o, S_, q_r, ws=aw),
+                      2 * B * kv_r * S_ * d * 2 + 2 * B * q_r * d * 2,
+                      "attn_decode_kernel + attn_merge_kernel: split-KV GQA decode attention"),
+        "w_o": (lambda i: tp.tp_row_linear_partial(o, ranks[i % t]["w_o"], part, ws=ws),
+                H * orows * 2 + B * orows * 2 + B * H * 4,
+                projection_kernel(B, wide=True) + ": W_o row partial"),
+        "gate_up": (lambda i: tp.tp_column_linear(hn, ranks[i % t]["w_gate"], act, w_up=ranks[i % t]["w_up"], gamma=g2,
+                                                  eps=wl.eps, ws=ws),
+                    2 * I_r * H * 2 + B * H * 2 + H * 2 + B * I_r * 2,
+                    projection_kernel(B, wide=True) + ": RMSNorm + gate/up + SwiGLU"),
+        "down": (lambda i: tp.tp_row_linear_partial(act, ranks[i % t]["w_down"], part, ws=ws),
+                 H * I_r * 2 + B * I_r * 2 + B * H * 4,
+                 projection_kernel(B, wide=True) + ": down row partial"),
+    }
+    nl = 4 * t
+    kernels = {}
+    for name, (fn, nbytes, kname) in pieces.items():
+        for i in range(2 * t):
+            fn(i)
+        tm = event_time_ms(torch, fn, nl)
+        kernels[name] = roofline_hbm(kname + ", one rank", f"{name}_layer_decode_b{B}", nbytes, *tm)
+        log(f"[bench] {name}: {tm[0] * 1e3:.2f} us ({kernels[name]['achieved']:.0f} GB/s)")
+    for i in range(2 * t):
+        shard(i)
+    sh = event_time_ms(torch, shard, nl)
+    w_rank = (qc * H + H * orows + 3 * I_r * H) * 2
+    kv_rank = 2 * B * kv_r * S_ * d * 2
+    io_rank = 2 * B * H * 2 + 2 * B * H * 4 + 2 * H * 2 + 2 * B * kv_r * d * 2
+    rank_bytes = w_rank + kv_rank + io_rank
+    log(f"[bench] rank shard: {sh[0] * 1e3:.2f} us ({rank_bytes / (sh[0] * 1e-3) / 1e9:.0f} GB/s)")
     total_ms = time_steps(ctx, step, 1)
     ms_step = total_ms / args.steps
-    w_rank = (p0.qkv_cols * H + H * p0.o_rows + 3 * p0.inter_cols * H) * 2
-    kv_rank = 2 * B * p0.kv_heads * S_ * d * 2
-    rank_bytes = w_rank + kv_rank
-    extra = {
+    dom = max(kernels, key=lambda k: kernels[k]["us_mean"])
+    from megatron_tensor_transformer_amd import step_model
+    fields = {
+        "tokens_per_s": B * args.steps / (total_ms * 1e-3), "ms_per_step": ms_step,
         "step_GBps": t * rank_bytes / (ms_step * 1e-3) / 1e9,
-        "per_rank": {"weight_bytes": w_rank, "kv_bytes": kv_rank, "step_us_per_rank": ms_step * 1e3 / t,
-                     "attention_us": at[0] * 1e3},
-        "roofline": roofline_hbm("attn_decode_kernel + attn_merge_kernel (split-KV GQA decode attention, one rank)",
-                                 f"attention_layer_decode_b{B}", kv_bytes, *at),
+        "step_pct_hbm_peak": 100 * t * rank_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "rank_shard": {"bytes": rank_bytes, "weight_bytes": w_rank, "kv_bytes": kv_rank, "io_bytes": io_rank,
+                       "us_mean": sh[0] * 1e3, "us_median": sh[1] * 1e3, "us_min": sh[2] * 1e3,
+                       "GBps": rank_bytes / (sh[0] * 1e-3) / 1e9,
+                       "pct_hbm_peak": 100 * rank_bytes / (sh[0] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                       "tokens_per_s_one_layer_shard": B / (sh[0] * 1e-3)},
+        "kernels": kernels,
+        "dominant_kernel": dom,
+        "roofline": kernels[dom],
+        # extrapolation, not a measurement: 80 such layers, all t shards on one GPU in turn
+        "extrapolated_80_layer_tokens_per_s": B / (80 * ms_step * 1e-3),
+        # a model, not a measurement: the t-GPU step predicted from this one-GPU layer time
+        "step_model_80_layers": step_model.predict(ms_step * 1e-3, layers=80, hidden=H, tokens=B, max_t=t),
     }
     config = {"workload": f"70B-shaped full layer decode, all t={t} rank shards (attention and MLP stages) + "
                           f"on-device sums with residual", "hidden": H, "intermediate": I, "q_heads": nq,
               "kv_heads": nkv, "head_dim": d, "t": t, "batch": B, "kv_len": S_}
-    # A model, not a measurement: the t-GPU decode step predicted from this
-    # one-GPU layer time (all t shards run in turn) for 80 such layers.
-    from megatron_tensor_transformer_amd import step_model
-    extra["step_model_80_layers"] = step_model.predict(ms_step * 1e-3, layers=80, hidden=H, tokens=B, max_t=t)
-    res = result(ctx, B * args.steps / (total_ms * 1e-3), "tokens/s", ms_step, config, extra)
-    if not args.no_cpu:
-        from oracle import sharded as S
-        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
-        pd = tp.plan_dict(p0)
-        xa = a["x"]
+    return fields, config, (a, mi)
 
-        def one_rank():
-            S.rank_attention(xa, a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], S_, nq, nkv, d,
-                             pd, a["gamma"], wl.eps)
-            S.rank_mlp(xa, mi["w_gate"], mi["w_up"], mi["w_down"], pd, mi["gamma"], wl.eps)
 
-        n, el = repeat_for(args.cpu_seconds, one_rank)
-        res["cpu_baseline"] = {"value": B * n / (el * t), "unit": "tokens/s", "cores": blas_threads(),
-                               "kind": "oracle",
-                               "sample": f"{n} float64 passes of rank 0's shard (attention + MLP stages) over the "
-                                         f"batch of {B}, {el:.1f} s; scaled by 1/{t} for the {t} ranks of a step"}
+def decode_layer_cpu(ctx, inputs):
+    """The float64 oracle on the 70B-shaped layer decode step (all 16 tokens): (i) one rank's shard (its
+    attention and MLP blocks on its own heads and columns), (ii) all t shards with the rank-order sums
+    and residuals, (iii) the unsharded layer; tokens/s of each."""
+    from oracle import layer as L
+    from oracle import plan as OP
+    a, mi = inputs
+    wl = ctx.W.WORKLOADS[5]
+    H, I, nq, nkv, d, t, S_ = wl.hidden, wl.intermediate, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.t, wl.kv_len
+    B = a["x"].shape[0]
+    od = OP.ModelDesc(hidden=H, intermediate=I, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, seq_len=S_, batch=B)
+    ops = [OP.rank_plan(od, t, r) for r in range(t)]
+
+    def attn_rank(op, x):
+        qs = slice(op["q_head_begin"] * d, (op["q_head_begin"] + op["q_heads"]) * d)
+        ks = slice(op["kv_head_begin"] * d, (op["kv_head_begin"] + op["kv_heads"]) * d)
+        hs = slice(op["kv_head_begin"], op["kv_head_begin"] + op["kv_heads"])
+        return L.attention_block(x, a["w_q"][:, qs], a["w_k"][:, ks], a["w_v"][:, ks], a["w_o"][qs, :],
+                                 a["k_cache"][:, hs], a["v_cache"][:, hs], S_, op["q_heads"], op["kv_heads"], d,
+                                 a["gamma"], wl.eps)["y"]
+
+    def mlp_rank(op, h):
+        b, c = op["inter_begin"], op["inter_cols"]
+        return L.mlp_block(h, mi["w_gate"][:, b:b + c], mi["w_up"][:, b:b + c], mi["w_down"][b:b + c],
+                           mi["gamma"], wl.eps)["y"]
+
+    def one_rank():
+        mlp_rank(ops[0], L.f64(a["x"]) + attn_rank(ops[0], a["x"]))
+
+    def all_ranks():
+        h = L.f64(a["x"]) + sum(attn_rank(op, a["x"]) for op in ops)
+        return h + sum(mlp_rank(op, h) for op in ops)
+
+    w = {"gamma1": a["gamma"], "w_q": a["w_q"], "w_k": a["w_k"], "w_v": a["w_v"], "w_o": a["w_o"],
+         "gamma2": mi["gamma"], "w_gate": mi["w_gate"], "w_up": mi["w_up"], "w_down": mi["w_down"]}
+    legs = {"one_rank_shard": one_rank, "all_ranks_and_sums": all_ranks,
+            "unsharded_layer": lambda: L.layer(a["x"], w, a["k_cache"], a["v_cache"], S_, nq, nkv, d, wl.eps)}
+    out = {}
+    for name, fn in legs.items():
+        n, el = repeat_for(ctx.args.cpu_seconds / 3, fn)
+        out[name] = {"tokens_per_s": B * n / el, "runs": n, "seconds": el}
+        log(f"[bench] CPU oracle, layer decode {name}: {out[name]['tokens_per_s']:.1f} tokens/s")
+    return out
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_available": len(os.sched_getaffinity(0)), "blas_threads": blas_threads()}
+
+
+def bench_layer_decode(ctx):
+    fields, config, inputs = decode_layer_gpu(ctx)
+    extra = {k: v for k, v in fields.items() if k not in ("tokens_per_s", "ms_per_step")}
+    res = result(ctx, fields["tokens_per_s"], "tokens/s", fields["ms_per_step"], config, extra)
+    if not ctx.args.no_cpu:
+        legs = decode_layer_cpu(ctx, inputs)
+        res["cpu_baseline"] = {"value": legs["all_ranks_and_sums"]["tokens_per_s"], "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": "float64 oracle (BLAS products), the whole step: all 8 rank shards + "
+                                         "sums + residuals over the batch of 16", "legs": legs, "host": host_info()}
     return res
 
+
+def hbm_read_ceiling(ctx, sizes=(58_974_208, 117_833_728, 1 << 30)):
+    """The plain streaming-read rate of buffers the size of the decode launches (and 1 GiB), each
+    buffer read once per launch, rotating over enough copies to stay out of the 256 MB cache."""
+    torch, tp = ctx.torch, ctx.tp
+    flag = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = {}
+    for nb in sizes:
+        copies = max(2, -(-(768 << 20) // nb))
+        bufs = [torch.empty(nb // 4, dtype=torch.int32, device="cuda").fill_(i + 1) for i in range(copies)]
+
+        def rd(i):
+            tp.tp_hbm_stream_read(bufs[i % copies], flag)
+
+        for i in range(2 * copies):
+            rd(i)
+        n = max(4 * copies, 16) if nb < (1 << 28) else 8
+        tm = event_time_ms(torch, rd, n)
+        out[str(nb)] = {"GBps": nb / (tm[0] * 1e-3) / 1e9, "us_mean": tm[0] * 1e3, "us_min": tm[2] * 1e3,
+                        "buffers_rotated": copies}
+        log(f"[bench] streaming read of {nb / 1e6:.1f} MB: {out[str(nb)]['GBps']:.0f} GB/s")
+        del bufs
+    torch.cuda.synchronize()
+    return out
+
+
+def bench_hbm_read(ctx):
+    """The streaming-read reference alone."""
+    ceiling = hbm_read_ceiling(ctx)
+    big = ceiling[str(1 << 30)]
+    config = {"workload": "plain streaming read of device buffers (1 GiB and decode-launch sizes)"}
+    return result(ctx, big["GBps"], "GB/s", big["us_mean"] * 1e-3, config, {"hbm_read_ceiling": ceiling})
+
+
+def bench_headline(ctx):
+    """The metric's two halves on their largest single-GPU configurations: the 70B-shaped full layer
+    decode shard (t=8, batch 16, KV 8192) for decode tokens/s and HBM GB/s, and the 70B-shaped MLP
+    prefill shard (t=4, 4096 tokens) for TFLOP/s against the bf16 matrix-core peak."""
+    args = ctx.args
+    dec, dcfg, dinputs = decode_layer_gpu(ctx)
+    pre, pcfg, pinp = prefill_mlp_gpu(ctx)
+    ceiling = hbm_read_ceiling(ctx)
+    config = {"workload": "70B-shaped full layer decode shard (t=8, batch 16, KV cache 8192; all 8 rank shards "
+                          "+ on-device sums) and 70B-shaped MLP prefill shard (t=4, 4096 tokens; all 4 rank shards "
+                          "+ on-device sum)",
+              "decode": dcfg, "prefill": pcfg}
+    extra = {k: v for k, v in dec.items() if k not in ("tokens_per_s", "ms_per_step")}
+    extra["prefill"] = pre
+    extra["prefill_ms_per_step"] = pre["ms_per_step"]
+    extra["hbm_read_ceiling"] = ceiling
+    res = result(ctx, dec["tokens_per_s"], "tokens/s", dec["ms_per_step"], config, extra)
+    if not args.no_cpu:
+        dlegs = decode_layer_cpu(ctx, dinputs)
+        plegs, psample = prefill_mlp_cpu(ctx, pinp)
+        res["cpu_baseline"] = {"value": dlegs["all_ranks_and_sums"]["tokens_per_s"], "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": "float64 oracle with BLAS products on the decode step: all 8 rank shards "
+                                         "+ sums + residuals over the batch of 16 (legs: one rank's shard, all "
+                                         "ranks, the unsharded layer); prefill legs over " + psample,
+                               "legs": dlegs, "prefill_legs": plegs, "host": host_info()}
+    return res
 
 
 def causal_flops(batch, seq, kv_len, q_heads, d):
@@ -731,11 +989,15 @@ def bench_attn_prefill(ctx):
         kr = inp["k_cache"][:1, p0.kv_head_begin:p0.kv_head_begin + p0.kv_heads]
         vr = inp["v_cache"][:1, p0.kv_head_begin:p0.kv_head_begin + p0.kv_heads]
         log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
-        n, el = repeat_for(args.cpu_seconds, lambda: S.rank_prefill_attention(qs, kr, vr, kv_len, nq, nkv, d, pd))
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):     # the sharded oracle's einsum products run on one thread
+            n, el = repeat_for(args.cpu_seconds, lambda: S.rank_prefill_attention(qs, kr, vr, kv_len, nq, nkv, d,
+                                                                                  pd))
         sfl = causal_flops(1, n_tail, kv_len, p0.q_heads, d)
-        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"{n} float64 passes of rank 0's shard over the last {n_tail} tokens of "
+                               "sample": f"{n} float64 passes (sharded oracle, numpy einsum on one thread) of rank 0's "
+                                         f"shard over the last {n_tail} tokens of "
                                          f"sequence 0 (each sees about {kv_len} keys), {el:.1f} s"}
     return res
 
@@ -828,12 +1090,15 @@ def bench_layer_prefill(ctx):
             S.rank_mlp(xs.reshape(n_tail, H) + at["partial"].reshape(n_tail, H), mi["w_gate"], mi["w_up"],
                        mi["w_down"], pd, mi["gamma"], wl.eps)
 
-        n, el = repeat_for(args.cpu_seconds, one_rank)
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):     # the sharded oracle's einsum products run on one thread
+            n, el = repeat_for(args.cpu_seconds, one_rank)
         sfl = (2.0 * n_tail * H * p0.qkv_cols + causal_flops(1, n_tail, kv_len, p0.q_heads, d)
                + 2.0 * n_tail * p0.o_rows * H + 2.0 * n_tail * H * 3 * p0.inter_cols)
-        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"{n} float64 passes of rank 0's shard (attention and MLP stages) over "
+                               "sample": f"{n} float64 passes (sharded oracle, numpy einsum on one thread) of rank "
+                                         f"0's shard (attention and MLP stages) over "
                                          f"the last {n_tail} tokens of sequence 0 (each sees about {kv_len} keys), "
                                          f"{el:.1f} s"}
     return res
@@ -904,10 +1169,12 @@ def bench_moe_decode(ctx):
             gates = L.moe_route(L.linear(L.rmsnorm(xs, inp["gamma"], wl.eps), inp["w_router"]), k)
             S.rank_moe(xs, inp["gamma"], inp["w_router"], inp["experts"], gates, tp.plan_dict(plans[0]), wl.eps)
 
-        n, el = repeat_for(args.cpu_seconds, one_rank)
-        res["cpu_baseline"] = {"value": n_tok * n / (el * t), "unit": "tokens/s", "cores": blas_threads(),
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):     # the sharded oracle's einsum products run on one thread
+            n, el = repeat_for(args.cpu_seconds, one_rank)
+        res["cpu_baseline"] = {"value": n_tok * n / (el * t), "unit": "tokens/s", "cores": 1,
                                "kind": "oracle",
-                               "sample": f"{n} float64 passes of rank 0's MoE shard (router + all {E} experts) over "
+                               "sample": f"{n} float64 passes (sharded oracle, numpy einsum on one thread) of rank 0's MoE shard (router + all {E} experts) over "
                                          f"{n_tok} of the {M} tokens, {el:.1f} s; scaled by 1/{t} for the {t} ranks"}
     return res
 

@@ -350,6 +350,17 @@ tp_status tp_moe_shard_forward(const tp_moe_weights* weights, const void* x, flo
                                float* logits_out, int64_t m, int64_t hidden, int32_t n_experts, int32_t top_k,
                                int64_t inter_cols, float eps, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * tp_hbm_stream_read - measurement helper, not a step of the layer: reads
+ * bytes of device memory at buf once with 128-bit non-temporal loads (the
+ * practical HBM read rate a decode projection's weight stream is compared
+ * with; "Tensor parallel scaling curves", The scaling math: decode is bound by
+ * reading the weights). flag: device, 4 bytes, written only in the unlikely
+ * case that the folded words equal never. bytes must be a positive multiple
+ * of 16 (TP_ERR_SHAPE); buf and flag 16-byte aligned (TP_ERR_ALIGN).
+ */
+tp_status tp_hbm_stream_read(const void* buf, size_t bytes, void* flag, uint32_t never, void* stream);
+
 /* Name of a status code, e.g. "TP_ERR_SHAPE". */
 const char* tp_status_name(tp_status status);
 

@@ -37,7 +37,7 @@ STATUS = ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_
 EXPORTS = ["tp_shard_plan", "tp_linear_workspace_bytes", "tp_column_linear", "tp_swiglu",
            "tp_row_linear_partial", "tp_partial_sum", "tp_row_linear_partial_bf16", "tp_partial_sum_bf16",
            "tp_attention_workspace_bytes", "tp_decode_attention",
-           "tp_prefill_attention", "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_status_name", "tp_last_error"]
+           "tp_prefill_attention", "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_hbm_stream_read", "tp_status_name", "tp_last_error"]
 
 
 class tp_model_desc(ctypes.Structure):
@@ -91,6 +91,7 @@ _SIGS = {
     "tp_layer_shard_forward": (_I32, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
                                       ctypes.POINTER(tp_rank_weights), _P, ctypes.POINTER(tp_kv_view), _P, _I64,
                                       _I32, _P, _SZ, _P]),
+    "tp_hbm_stream_read": (_I32, [_P, _SZ, _P, ctypes.c_uint32, _P]),
     "tp_status_name": (ctypes.c_char_p, [_I32]),
     "tp_last_error": (ctypes.c_char_p, []),
 }
@@ -313,3 +314,11 @@ def tp_layer_shard_forward(desc: tp_model_desc, plan: tp_rank_plan, stage: int, 
                                       ctypes.byref(kvv) if kvv is not None else None, _ptr(partial), m, dt, wp, wn,
                                       _stream(stream)))
     return partial
+
+
+# ------------------------------------------------------------------ measurement helper
+
+def tp_hbm_stream_read(buf: torch.Tensor, flag: torch.Tensor, never: int = 0x9E3779B9, stream=None) -> None:
+    """Read every byte of buf once (the practical HBM read rate); flag: a 4-byte device word."""
+    _check(lib.tp_hbm_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(flag), never,
+                                  _stream(stream)))

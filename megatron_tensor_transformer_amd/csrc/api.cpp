@@ -585,6 +585,17 @@ tp_status tp_prefill_attention(const void* q, const void* k, const void* v, void
     return ok();
 }
 
+tp_status tp_hbm_stream_read(const void* buf, size_t bytes, void* flag, uint32_t never, void* stream) {
+    TRY(check_ptr(buf, "buf"));
+    TRY(check_ptr(flag, "flag"));
+    if (bytes == 0 || bytes % 16) return fail(TP_ERR_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
+    if (overlaps(flag, 4, buf, bytes)) return fail(TP_ERR_ALIAS, "flag lies inside buf");
+    hipError_t e = tpk::stream_read_launch(buf, (int64_t)(bytes / 16), reinterpret_cast<unsigned*>(flag), never,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
+    return ok();
+}
+
 size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage, int64_t m,
                                 tp_dtype dtype) {
     if (!desc || !plan || m < 1 || (stage != TP_STAGE_ATTN && stage != TP_STAGE_MLP)) return 0;

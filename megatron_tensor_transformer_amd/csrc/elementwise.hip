@@ -372,3 +372,42 @@ hipError_t moe_scale_launch(void* a, const float* gates, int m, int E, int64_t c
 }
 
 }  // namespace tpk
+
+namespace tpk {
+
+// Plain streaming read of a buffer, the reference point for the decode
+// kernels' bandwidth: every lane keeps SR_UNR 128-bit non-temporal loads in
+// flight over a grid-stride loop and folds them into one word. The word is
+// stored only if it equals a value the caller passes and never expects, so
+// the loads stay live and the kernel writes (almost) nothing.
+constexpr int SR_UNR = 8;
+
+__global__ __launch_bounds__(EW_THREADS) void stream_read_kernel(const uint4* __restrict__ p, int64_t n16,
+                                                                 unsigned* out, unsigned never) {
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+    int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + (SR_UNR - 1) * stride < n16; i += SR_UNR * stride) {
+        uint4 v[SR_UNR];
+#pragma unroll
+        for (int u = 0; u < SR_UNR; ++u) v[u] = load_stream_u4(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < SR_UNR; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = load_stream_u4(p + i);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == never) out[0] = acc;
+}
+
+hipError_t stream_read_launch(const void* buf, int64_t n16, unsigned* out, unsigned never, hipStream_t s) {
+    int64_t blocks = (n16 + (int64_t)EW_THREADS * SR_UNR - 1) / ((int64_t)EW_THREADS * SR_UNR);
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(EW_THREADS), 0, s,
+                       reinterpret_cast<const uint4*>(buf), n16, out, never);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

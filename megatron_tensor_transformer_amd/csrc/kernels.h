@@ -150,4 +150,8 @@ struct PrefillArgs {
 };
 hipError_t prefill_attn_launch(const PrefillArgs& a, hipStream_t stream);
 
+// Plain streaming read of n16 128-bit words (the practical HBM read rate);
+// out[0] is written only if the folded words equal never.
+hipError_t stream_read_launch(const void* buf, int64_t n16, unsigned* out, unsigned never, hipStream_t stream);
+
 }  // namespace tpk

@@ -314,3 +314,13 @@ def test_linear_workspace_follows_the_k_split_rule():
                     (16, 8200, 8192),     # K past one workgroup's 8192
                     (16, 57344, 4096)]:   # the stacked Mixtral down projection
         assert tp.tp_linear_workspace_bytes(m, k, n, BF, 0) > 0, (m, k, n)
+
+
+def test_hbm_stream_read_validation():
+    f = tp.lib.tp_hbm_stream_read
+    assert tp.STATUS[f(None, 16, 4096, 0, None)] == "TP_ERR_NULL"
+    assert tp.STATUS[f(4096, 16, None, 0, None)] == "TP_ERR_NULL"
+    assert tp.STATUS[f(4097, 16, 8192, 0, None)] == "TP_ERR_ALIGN"
+    assert tp.STATUS[f(4096, 0, 8192, 0, None)] == "TP_ERR_SHAPE"
+    assert tp.STATUS[f(4096, 24, 8192, 0, None)] == "TP_ERR_SHAPE"
+    assert tp.STATUS[f(4096, 64, 4112, 0, None)] == "TP_ERR_ALIAS"
