@@ -65,6 +65,9 @@ typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 /* Bytes of shared completion counters at the start of every workspace. */
 #define TP_WORKSPACE_HEADER 32768
 
+/* Bytes of the per-GPU scratch tp_layer_shard_forward_static uses (16 MiB). */
+#define TP_STATIC_SCRATCH_BYTES 16777216
+
 typedef enum tp_status {
     TP_OK = 0,
     TP_ERR_NULL = 1,        /* a required pointer is NULL */
@@ -304,6 +307,29 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
                                  const tp_rank_weights* weights, const void* in, const tp_kv_view* kv,
                                  float* partial, int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes,
                                  void* stream);
+
+/*
+ * tp_layer_shard_forward_static - tp_layer_shard_forward for callers that
+ * cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and kernels, with
+ * the workspace taken from a library-owned device array of
+ * TP_STATIC_SCRATCH_BYTES per GPU instead of a caller's buffer. It calls no
+ * allocating routine. The caller still passes inputs and outputs.
+ * - A call whose workspace (tp_layer_workspace_bytes) exceeds
+ *   TP_STATIC_SCRATCH_BYTES returns TP_ERR_WORKSPACE before any HIP call.
+ *   Decode stages of the 70B-shaped layer at t=8 over 16 sequences need
+ *   about 2 MB; long prefill blocks need more and take the workspace entry
+ *   point.
+ * - The first call on a device looks the array up with that device current
+ *   and enqueues one small kernel on the caller's stream that zeroes its
+ *   counter header; every call leaves the header zero again.
+ * - Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (different streams without ordering, or several host threads)
+ *   race on it and must not be issued.
+ */
+tp_status tp_layer_shard_forward_static(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                                        const tp_rank_weights* weights, const void* in, const tp_kv_view* kv,
+                                        float* partial, int64_t m, tp_dtype dtype, void* stream);
 
 /*
  * Mixture of experts. "Tensor Parallelism Fundamentals", section "Sizing

@@ -37,7 +37,7 @@ STATUS = ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_
 EXPORTS = ["tp_shard_plan", "tp_linear_workspace_bytes", "tp_column_linear", "tp_swiglu",
            "tp_row_linear_partial", "tp_partial_sum", "tp_row_linear_partial_bf16", "tp_partial_sum_bf16",
            "tp_attention_workspace_bytes", "tp_decode_attention",
-           "tp_prefill_attention", "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_hbm_stream_read", "tp_status_name", "tp_last_error"]
+           "tp_prefill_attention", "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_layer_shard_forward_static", "tp_hbm_stream_read", "tp_status_name", "tp_last_error"]
 
 
 class tp_model_desc(ctypes.Structure):
@@ -91,6 +91,9 @@ _SIGS = {
     "tp_layer_shard_forward": (_I32, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
                                       ctypes.POINTER(tp_rank_weights), _P, ctypes.POINTER(tp_kv_view), _P, _I64,
                                       _I32, _P, _SZ, _P]),
+    "tp_layer_shard_forward_static": (_I32, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
+                                             ctypes.POINTER(tp_rank_weights), _P, ctypes.POINTER(tp_kv_view), _P,
+                                             _I64, _I32, _P]),
     "tp_hbm_stream_read": (_I32, [_P, _SZ, _P, ctypes.c_uint32, _P]),
     "tp_status_name": (ctypes.c_char_p, [_I32]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -313,6 +316,22 @@ def tp_layer_shard_forward(desc: tp_model_desc, plan: tp_rank_plan, stage: int, 
     _check(lib.tp_layer_shard_forward(ctypes.byref(desc), ctypes.byref(plan), stage, ctypes.byref(w), _ptr(inp),
                                       ctypes.byref(kvv) if kvv is not None else None, _ptr(partial), m, dt, wp, wn,
                                       _stream(stream)))
+    return partial
+
+
+def tp_layer_shard_forward_static(desc: tp_model_desc, plan: tp_rank_plan, stage: int,
+                                  weights: Dict[str, torch.Tensor], inp: torch.Tensor, partial: torch.Tensor,
+                                  kv: Optional[Dict] = None, stream=None) -> torch.Tensor:
+    """tp_layer_shard_forward with the library's per-GPU static scratch in place of a workspace."""
+    m = inp.shape[0]
+    w = tp_rank_weights(*[_ptr(weights.get(n)) for n in
+                          ("attn_norm", "w_qkv", "w_o", "mlp_norm", "w_gate", "w_up", "w_down")])
+    kvv = None
+    if kv is not None:
+        kvv = tp_kv_view(_ptr(kv["k"]), _ptr(kv["v"]), kv["k"].shape[2], kv["kv_len"], kv.get("new_tokens", 1))
+    _check(lib.tp_layer_shard_forward_static(ctypes.byref(desc), ctypes.byref(plan), stage, ctypes.byref(w),
+                                             _ptr(inp), ctypes.byref(kvv) if kvv is not None else None,
+                                             _ptr(partial), m, _dtype_code(inp), _stream(stream)))
     return partial
 
 

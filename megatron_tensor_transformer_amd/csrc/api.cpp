@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -610,9 +611,14 @@ size_t tp_layer_workspace_bytes(const tp_model_desc* desc, const tp_rank_plan* p
     return dec > pre ? dec : pre;
 }
 
-tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
-                                 const tp_rank_weights* wts, const void* in, const tp_kv_view* kv, float* partial,
-                                 int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The layer stage. With dry set, every check runs and nothing is enqueued.
+tp_status layer_forward_impl(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                             const tp_rank_weights* wts, const void* in, const tp_kv_view* kv, float* partial,
+                             int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes, void* stream, bool dry) {
     TRY(check_dtype(dtype));
     TRY(check_plan(desc, plan));
     if (!wts) return fail(TP_ERR_NULL, "weights is NULL");
@@ -676,6 +682,7 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         void* lin = b + L.act1 + L.act2;
         void* aws = b + L.act1 + L.act2 + L.lin;
         if (S > 1) {
+            if (dry) return ok();
             // A block of S tokens per sequence: [q | k | v] of every token, the
             // block's k, v into the cache, causal attention reading q from the
             // projected rows, W_o partial.
@@ -705,6 +712,7 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         if (round256(ap_len.ws_bytes) > L.attn)
             return fail(TP_ERR_WORKSPACE, "attention scratch of %zu bytes exceeds the %zu sized for capacity %lld",
                         (size_t)round256(ap_len.ws_bytes), L.attn, (long long)kv->capacity);
+        if (dry) return ok();
         tpk::GemvArgs extra{};
         extra.k_cache = kv->k;
         extra.v_cache = kv->v;
@@ -735,6 +743,7 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
         return fail(TP_ERR_ALIGN, "inter_cols=%lld not a multiple of %zu", (long long)plan->inter_cols, vec_elems(dtype));
     const LayerWs L = layer_ws(desc, plan, stage, m, dtype, false);
     TRY(check_ws(ws, ws_bytes, L.total));
+    if (dry) return ok();
     char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
     unsigned* cnt = ws_counters(ws);
     void* abuf = b;
@@ -743,6 +752,78 @@ tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* 
                    tpk::EPI_SWIGLU, cnt, lin, s));
     return run_linear(abuf, wts->w_down, nullptr, nullptr, 0.f, partial, m, plan->inter_cols, H, dtype,
                       tpk::EPI_PARTIAL, cnt, lin, s);
+}
+
+// Scratch of tp_layer_shard_forward_static: one array per GPU, held until
+// the process ends. Its device address is looked up once per device (with
+// that device current) and kept here; host code never passes the array's
+// name to a kernel, only that address.
+static __device__ __align__(256) unsigned char scratch[TP_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_cleared[kMaxDevices] = {};
+
+tp_status static_scratch(int dev, void** ptr) {
+    if (dev < 0 || dev >= kMaxDevices) return fail(TP_ERR_HIP, "device ordinal %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "static scratch address lookup");
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_layer_shard_forward(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                                 const tp_rank_weights* wts, const void* in, const tp_kv_view* kv, float* partial,
+                                 int64_t m, tp_dtype dtype, void* ws, size_t ws_bytes, void* stream) {
+    return layer_forward_impl(desc, plan, stage, wts, in, kv, partial, m, dtype, ws, ws_bytes, stream, false);
+}
+
+tp_status tp_layer_shard_forward_static(const tp_model_desc* desc, const tp_rank_plan* plan, tp_stage stage,
+                                        const tp_rank_weights* wts, const void* in, const tp_kv_view* kv,
+                                        float* partial, int64_t m, tp_dtype dtype, void* stream) {
+    // The call's workspace must fit the static scratch: refuse before any HIP call.
+    if (desc && plan && (stage == TP_STAGE_ATTN || stage == TP_STAGE_MLP) && m >= 1 &&
+        (dtype == TP_F32 || dtype == TP_BF16)) {
+        const bool pre = stage == TP_STAGE_ATTN && kv && kv->new_tokens > 1;
+        const size_t need = layer_ws(desc, plan, stage, m, dtype, pre).total;
+        if (need > TP_STATIC_SCRATCH_BYTES)
+            return fail(TP_ERR_WORKSPACE, "this call needs %zu bytes of scratch, beyond the %d bytes of the static "
+                        "scratch; call tp_layer_shard_forward with a workspace instead", need,
+                        TP_STATIC_SCRATCH_BYTES);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    void* ws = nullptr;
+    TRY(static_scratch(dev, &ws));
+    TRY(layer_forward_impl(desc, plan, stage, wts, in, kv, partial, m, dtype, ws, TP_STATIC_SCRATCH_BYTES, stream,
+                           true));
+    {
+        // The counter header must start at zero; every call leaves it zero, so
+        // it is cleared once per device, by a kernel on the caller's stream
+        // ordered before this call's work (a graph may capture it).
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_cleared[dev]) {
+            e = tpk::fill_zero_launch(ws, tpk::WS_HEADER, (hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "static scratch clear");
+            g_scratch_cleared[dev] = true;
+        }
+    }
+    return layer_forward_impl(desc, plan, stage, wts, in, kv, partial, m, dtype, ws, TP_STATIC_SCRATCH_BYTES, stream,
+                              false);
 }
 
 }  // extern "C"

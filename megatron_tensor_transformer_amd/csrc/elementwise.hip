@@ -411,3 +411,22 @@ hipError_t stream_read_launch(const void* buf, int64_t n16, unsigned* out, unsig
 }
 
 }  // namespace tpk
+
+namespace tpk {
+
+// Zero n16 128-bit words with vector stores (a kernel, so a caller may
+// capture it in a graph).
+__global__ __launch_bounds__(EW_THREADS) void fill_zero_kernel(uint4* p, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * EW_THREADS;
+    for (int64_t i = (int64_t)blockIdx.x * EW_THREADS + threadIdx.x; i < n16; i += stride)
+        p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t fill_zero_launch(void* p, size_t bytes, hipStream_t s) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(ew_blocks(n16)), dim3(EW_THREADS), 0, s, reinterpret_cast<uint4*>(p),
+                       n16);
+    return hipGetLastError();
+}
+
+}  // namespace tpk

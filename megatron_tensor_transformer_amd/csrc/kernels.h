@@ -154,4 +154,7 @@ hipError_t prefill_attn_launch(const PrefillArgs& a, hipStream_t stream);
 // out[0] is written only if the folded words equal never.
 hipError_t stream_read_launch(const void* buf, int64_t n16, unsigned* out, unsigned never, hipStream_t stream);
 
+// Zero bytes (a multiple of 16) of device memory with a kernel.
+hipError_t fill_zero_launch(void* p, size_t bytes, hipStream_t stream);
+
 }  // namespace tpk

@@ -324,3 +324,17 @@ def test_hbm_stream_read_validation():
     assert tp.STATUS[f(4096, 0, 8192, 0, None)] == "TP_ERR_SHAPE"
     assert tp.STATUS[f(4096, 24, 8192, 0, None)] == "TP_ERR_SHAPE"
     assert tp.STATUS[f(4096, 64, 4112, 0, None)] == "TP_ERR_ALIAS"
+
+
+def test_static_entry_refuses_calls_beyond_its_scratch():
+    """A 2 x 2048-token prefill block of the 70B layer at t=8 needs more than the static scratch; the
+    allocation-free entry point refuses it before any HIP call."""
+    d = tp.make_desc(8192, 28672, 64, 8, 128, n_layers=1, seq_len=2048, batch=2)
+    p = tp.tp_shard_plan(d, 8, 0)
+    assert tp.tp_layer_workspace_bytes(d, p, tp.TP_STAGE_ATTN, 4096, tp.TP_BF16) > 16 * MB
+    w = tp.tp_rank_weights(A, A, A, A, A, A, A)
+    kv = tp.tp_kv_view(A + 4096 * MB, A + 5000 * MB, 2048, 2048, 2048)
+    st = tp.lib.tp_layer_shard_forward_static(ctypes.byref(d), ctypes.byref(p), tp.TP_STAGE_ATTN, ctypes.byref(w),
+                                              A + 64 * MB, ctypes.byref(kv), A + 512 * MB, 4096, tp.TP_BF16, None)
+    assert tp.STATUS[st] == "TP_ERR_WORKSPACE"
+    assert "static scratch" in tp.lib.tp_last_error().decode()
