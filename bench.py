@@ -220,7 +220,7 @@ def projection_kernel(m, dtype="bf16", wide=False):
     one K range per wave."""
     if dtype == "bf16" and m > 16:
         return "gemm_bf16_kernel (MFMA prefill GEMM)"
-    if dtype == "bf16" and m >= 5:
+    if dtype == "bf16" and m >= 2:
         if wide:
             return "gemv_mfma_wide_kernel (matrix-core decode projection, one K range per wave)"
         return "gemv_mfma_kernel (matrix-core decode projection)"

@@ -61,7 +61,7 @@ struct GemvPlan {
 };
 
 // Smallest bf16 token count that goes to the matrix-core kernel.
-constexpr int GEMV_MFMA_MIN_M = 5;
+constexpr int GEMV_MFMA_MIN_M = 2;
 GemvPlan gemv_plan(int m, int K, int N, int is_bf16, int epi);        // picks one of the two below
 GemvPlan gemv_plan_dot2(int m, int K, int N, int is_bf16, int epi);
 GemvPlan gemv_plan_mfma(int m, int K, int N, int epi);                // bf16 only

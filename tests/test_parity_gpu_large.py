@@ -176,7 +176,7 @@ SPLIT_TILE_CASES = [
     (1, 4608, 70000, "bf16", "col"),
     (1, 4608, 70000, "bf16", "row"),
     (4, 4096, 70000, "f32", "col"),
-    (2, 4608, 140000, "bf16", "swiglu"),
+    (1, 4608, 140000, "bf16", "swiglu"),
 ]
 
 

@@ -2,7 +2,7 @@
 the workspace entry point (tp_layer_shard_forward) through the C ABI.
 
 Both stages of one rank shard, twice in a row on the same GPU: first 16
-sequences (matrix-core decode projections), then 3 (the v_dot2 projections,
+sequences (matrix-core decode projections), then 1 (the v_dot2 projections,
 whose split-K completion counters live in the static scratch's header). The
 two entry points run the same kernels, so their outputs must agree bitwise;
 both are also checked against the float64 oracle (2e-2 of max |ref|).
@@ -33,7 +33,7 @@ def _rank_weights(a, mi, p):
             "w_down": dev(phys(mi["w_down"][b:b + c, :]), "bf16")}
 
 
-@pytest.mark.parametrize("batches", [(16, 3)])
+@pytest.mark.parametrize("batches", [(16, 1)])
 def test_static_scratch_matches_workspace_entry(batches):
     assert torch.cuda.is_available()
     for call, B in enumerate(batches):
