@@ -24,9 +24,11 @@ partials):
   attn_proj             70B-shaped attention projections, hidden 8192, 64 q / 8
                         kv heads of 128, t=4, 16 tokens: per rank the QKV column
                         projection and the W_o row-partial.
-  attn_prefill, layer_prefill, moe_decode
+  attn_prefill, layer_prefill, moe_decode, moe_prefill
                         the prefill attention shard, the full layer over
-                        2 x 2048 new tokens, the Mixtral-shaped MoE decode block.
+                        2 x 2048 new tokens, the Mixtral-shaped MoE block at
+                        16 decode tokens and at 4096 prefill tokens (each
+                        expert over its routed tokens; TFLOP/s of routed flops).
   hbm_read              the plain streaming-read rate alone.
 
 One step is one pass of that whole path; K steps are replayed from HIP graphs
@@ -71,7 +73,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill",
-                             "layer_prefill", "moe_decode", "hbm_read"])
+                             "layer_prefill", "moe_decode", "moe_prefill", "hbm_read"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of the timed step (default: the workload's)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true")
@@ -112,7 +114,8 @@ def main():
     torch.cuda.set_device(0)
     bench = {"headline": bench_headline, "hbm_read": bench_hbm_read, "mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
              "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill,
-             "layer_prefill": bench_layer_prefill, "moe_decode": bench_moe_decode}[args.workload]
+             "layer_prefill": bench_layer_prefill, "moe_decode": bench_moe_decode,
+             "moe_prefill": bench_moe_prefill}[args.workload]
     if args.calibrate_copy:
         calibrate_copy(torch)
     res = bench(ctx)
@@ -1126,7 +1129,7 @@ def bench_moe_decode(ctx):
                       "w_down": ctx.dev(np.concatenate([ctx.phys(d[b:b + c]) for _, _, d in inp["experts"]],
                                                        axis=1))})
     x = ctx.dev(inp["x"])
-    ws = tp.workspace(max(tp.tp_moe_workspace_bytes(M, H, E, cols, True),
+    ws = tp.workspace(max(tp.tp_moe_workspace_bytes(M, H, E, k, cols, True),
                           tp.tp_linear_workspace_bytes(M, H, E * cols, tp.TP_BF16, tp.TP_LINEAR_SWIGLU)))
     parts = [torch.empty(M, H, device="cuda") for _ in range(t)]
     out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
@@ -1176,6 +1179,90 @@ def bench_moe_decode(ctx):
                                "kind": "oracle",
                                "sample": f"{n} float64 passes (sharded oracle, numpy einsum on one thread) of rank 0's MoE shard (router + all {E} experts) over "
                                          f"{n_tok} of the {M} tokens, {el:.1f} s; scaled by 1/{t} for the {t} ranks"}
+    return res
+
+
+def bench_moe_prefill(ctx):
+    """The Mixtral-8x7B-shaped MoE FFN prefill shard (t=2, 4096 tokens): each expert over the tokens
+    routed to it. Throughput counts the routed flops (each token's top_k experts), not the dense ones."""
+    torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
+    wl = W.WORKLOADS[9]
+    H, I, t, E, k = wl.hidden, wl.intermediate, wl.t, W.MOE_EXPERTS, W.MOE_TOP_K
+    M = args.tokens or wl.tokens[0]
+    log(f"[bench] drawing {wl.name}")
+    inp = W.moe_inputs(9, H, I, E, M, "bf16", progress=lambda e: log(f"[bench]   expert {e} drawn"))
+    desc = tp.make_desc(H, I)
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    cols = plans[0].inter_cols
+    gam, rtr = ctx.dev(inp["gamma"]), ctx.dev(ctx.phys(inp["w_router"]))
+    ranks = []
+    for p in plans:
+        b, c = p.inter_begin, p.inter_cols
+        log(f"[bench] staging rank {p.rank}'s stacked experts")
+        ranks.append({"norm": gam, "w_router": rtr,
+                      "w_gate": ctx.dev(np.concatenate([ctx.phys(g[:, b:b + c]) for g, _, _ in inp["experts"]])),
+                      "w_up": ctx.dev(np.concatenate([ctx.phys(u[:, b:b + c]) for _, u, _ in inp["experts"]])),
+                      "w_down": ctx.dev(np.concatenate([ctx.phys(d[b:b + c]) for _, _, d in inp["experts"]],
+                                                       axis=1))})
+    x = ctx.dev(inp["x"])
+    ws = tp.workspace(tp.tp_moe_workspace_bytes(M, H, E, k, cols, True))
+    parts = [torch.empty(M, H, device="cuda") for _ in range(t)]
+    out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    gates = torch.empty(M, E, device="cuda")
+
+    def step(i):
+        for r in range(t):
+            tp.tp_moe_shard_forward(ranks[r], x, parts[r], E, k, cols, eps=wl.eps, ws=ws)
+        tp.tp_partial_sum(parts, out)
+
+    def shard(i):
+        tp.tp_moe_shard_forward(ranks[i % t], x, parts[i % t], E, k, cols, eps=wl.eps, gates=gates, ws=ws)
+
+    for i in range(2 * t):
+        shard(i)
+    torch.cuda.synchronize()
+    routed = int((gates > 0).sum().item())                      # = M * k
+    fl_rank = 2.0 * routed * H * 2 * cols + 2.0 * routed * cols * H + 2.0 * M * H * E
+    sh = event_time_ms(torch, shard, 2 * t, reps=3)
+    tf = fl_rank / (sh[0] * 1e-3) / 1e12
+    log(f"[bench] MoE shard {sh[0] * 1e3:.1f} us ({tf:.0f} TFLOP/s routed)")
+    total_ms = time_steps(ctx, step, 1)
+    ms_step = total_ms / args.steps
+    tflops = t * fl_rank * args.steps / (total_ms * 1e-3) / 1e12
+    extra = {
+        "tokens_per_s": M * args.steps / (total_ms * 1e-3),
+        "pct_mfma_peak": 100 * tflops / BF16_PEAK_TFLOPS,
+        "per_rank": {"shard_us": sh[0] * 1e3, "routed_flops": fl_rank, "dense_flops": fl_rank * E / k,
+                     "tokens_routed_per_expert": [int(v) for v in (gates > 0).sum(0).tolist()]},
+        "roofline": {"kernel": "one rank's MoE shard call (router projection and gates, token lists, grouped "
+                               "gate/up + SwiGLU GEMM, grouped down GEMM, slot sum)", "bound": "mfma",
+                     "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
+                     "traffic": None, "flops_per_launch": fl_rank, "us_mean": sh[0] * 1e3, "us_median": sh[1] * 1e3,
+                     "us_min": sh[2] * 1e3},
+    }
+    config = {"workload": f"Mixtral-8x7B-shaped MoE FFN prefill block, all t={t} rank shards + on-device sum, "
+                          f"each expert over its routed tokens", "hidden": H, "intermediate": I, "experts": E,
+              "top_k": k, "t": t, "tokens": M}
+    res = result(ctx, tflops, "TFLOP/s", ms_step, config, extra)
+    if not args.no_cpu:
+        from oracle import layer as L
+        from oracle import plan as OP
+        n_tok = 64
+        xs = inp["x"][:n_tok]
+        gl = gates[:n_tok].cpu().numpy().astype(np.float64)
+        op = OP.rank_plan(OP.ModelDesc(hidden=H, intermediate=I), t, 0)
+        b, c = op["inter_begin"], op["inter_cols"]
+        ex0 = [(g[:, b:b + c], u[:, b:b + c], d[b:b + c]) for g, u, d in inp["experts"]]
+        log(f"[bench] CPU oracle for ~{args.cpu_seconds:.0f} s")
+        n, el = repeat_for(args.cpu_seconds, lambda: L.moe_block(xs, inp["gamma"], inp["w_router"], ex0, k,
+                                                                  gates=gl))
+        sfl = fl_rank * n_tok / M
+        res["cpu_baseline"] = {"value": n * sfl / el / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} float64 passes (BLAS products) of rank 0's MoE shard over {n_tok} of "
+                                         f"the {M} tokens with the GPU's routing, {el:.1f} s; counted on routed flops "
+                                         f"(the oracle computes every expert densely, {E // k}x those)",
+                               "host": host_info()}
     return res
 
 

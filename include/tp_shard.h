@@ -349,7 +349,11 @@ tp_status tp_layer_shard_forward_static(const tp_model_desc* desc, const tp_rank
  * The caller sums the t ranks' partials with tp_partial_sum; all ranks must
  * see the same gates (the router weights are identical on every rank).
  * Experts a token is not routed to carry gate 0, so the result is the sum
- * over its top_k experts; every expert's weights are read each call.
+ * over its top_k experts. Up to 64 tokens (a decode batch) every expert is
+ * computed for every token (its weights are read anyway); above that, with
+ * top_k <= 8, each expert runs only over the tokens routed to it (grouped
+ * GEMMs over per-expert token lists: top_k / E of the dense flops), and a
+ * token's top_k expert outputs are added in expert order.
  */
 typedef struct tp_moe_weights {
     const void* norm;      /* [H] gamma in front of the router and experts, or NULL */
@@ -359,8 +363,9 @@ typedef struct tp_moe_weights {
     const void* w_down;    /* [H, E * inter_cols]: expert e's columns e*inter_cols .. (e+1)*inter_cols - 1 */
 } tp_moe_weights;
 
-/* Workspace bytes of tp_moe_shard_forward (has_norm: weights->norm != NULL). */
-size_t tp_moe_workspace_bytes(int64_t m, int64_t hidden, int32_t n_experts, int64_t inter_cols,
+/* Workspace bytes of tp_moe_shard_forward (has_norm: weights->norm != NULL);
+ * 0 for invalid sizes. */
+size_t tp_moe_workspace_bytes(int64_t m, int64_t hidden, int32_t n_experts, int32_t top_k, int64_t inter_cols,
                               int32_t has_norm);
 
 /*

@@ -83,7 +83,7 @@ _SIGS = {
     "tp_attention_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I64]),
     "tp_decode_attention": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P, _SZ, _P]),
     "tp_prefill_attention": (_I32, [_P, _P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I64, _I64, _I32, _P]),
-    "tp_moe_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I64, _I32]),
+    "tp_moe_workspace_bytes": (_SZ, [_I64, _I64, _I32, _I32, _I64, _I32]),
     "tp_moe_shard_forward": (_I32, [ctypes.POINTER(tp_moe_weights), _P, _P, _P, _P, _I64, _I64, _I32, _I32, _I64,
                                     _F, _P, _SZ, _P]),
     "tp_layer_workspace_bytes": (_SZ, [ctypes.POINTER(tp_model_desc), ctypes.POINTER(tp_rank_plan), _I32,
@@ -272,8 +272,9 @@ def tp_prefill_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out:
     return out
 
 
-def tp_moe_workspace_bytes(m: int, hidden: int, n_experts: int, inter_cols: int, has_norm: bool = True) -> int:
-    return lib.tp_moe_workspace_bytes(m, hidden, n_experts, inter_cols, int(bool(has_norm)))
+def tp_moe_workspace_bytes(m: int, hidden: int, n_experts: int, top_k: int, inter_cols: int,
+                           has_norm: bool = True) -> int:
+    return lib.tp_moe_workspace_bytes(m, hidden, n_experts, top_k, inter_cols, int(bool(has_norm)))
 
 
 def tp_moe_shard_forward(weights: Dict[str, torch.Tensor], x: torch.Tensor, partial: torch.Tensor, n_experts: int,
@@ -284,7 +285,7 @@ def tp_moe_shard_forward(weights: Dict[str, torch.Tensor], x: torch.Tensor, part
     m, H = x.shape
     w = tp_moe_weights(*[_ptr(weights.get(n)) for n in ("norm", "w_router", "w_gate", "w_up", "w_down")])
     if ws is None:
-        ws = workspace(tp_moe_workspace_bytes(m, H, n_experts, inter_cols, weights.get("norm") is not None),
+        ws = workspace(tp_moe_workspace_bytes(m, H, n_experts, top_k, inter_cols, weights.get("norm") is not None),
                        x.device)
     wp, wn = _ws(ws)
     _check(lib.tp_moe_shard_forward(ctypes.byref(w), _ptr(x), _ptr(partial), _ptr(gates), _ptr(logits), m, H,

@@ -409,26 +409,42 @@ namespace {
 // Tokens up to which the router's logits and gates come from one fused launch
 // (every workgroup reads all of W_router, cheap for a decode batch).
 constexpr int64_t MOE_FUSED_ROUTER_MAX_M = 64;
+// Larger batches compute each expert over its own tokens (grouped GEMMs),
+// when a token's experts fit the partial sum's eight inputs.
+constexpr int MOE_GROUPED_MAX_K = 8;
 
-// MoE workspace: [header][u (normalised x)][logits][gates][expert activations][projection scratch].
+bool moe_grouped(int64_t m, int32_t top_k) { return m > MOE_FUSED_ROUTER_MAX_M && top_k <= MOE_GROUPED_MAX_K; }
+
+// MoE workspace: [header][u (normalised x)][logits][gates] then, for a decode
+// batch, [expert activations, every expert][projection scratch]; for a grouped
+// batch, [slots][lists][counts][activations, packed by expert][slot partials
+// [top_k, m, H] float32][projection scratch].
 struct MoeWs {
-    size_t u, logits, gates, act, lin, total;
+    size_t u, logits, gates, act, lin, slots, lists, counts, parts, total;
 };
 
-MoeWs moe_ws(int64_t m, int64_t H, int32_t E, int64_t cols, bool norm) {
+MoeWs moe_ws(int64_t m, int64_t H, int32_t E, int64_t cols, bool norm, int32_t top_k) {
     MoeWs w{};
     const int64_t ecols = (int64_t)E * cols;
     w.u = norm ? round256((size_t)m * H * 2) : 0;
     w.logits = round256((size_t)m * E * 4);
     w.gates = round256((size_t)m * E * 4);
-    w.act = round256((size_t)m * ecols * 2);
     size_t l = linear_scratch(m, H, E, TP_BF16, tpk::EPI_PARTIAL, false);
-    const size_t l2 = linear_scratch(m, H, ecols, TP_BF16, tpk::EPI_SWIGLU, false);
-    const size_t l3 = linear_scratch(m, ecols, H, TP_BF16, tpk::EPI_PARTIAL, false);
-    if (l2 > l) l = l2;
-    if (l3 > l) l = l3;
+    if (moe_grouped(m, top_k)) {
+        w.slots = round256((size_t)m * E * 4);
+        w.lists = round256((size_t)m * E * 4);
+        w.counts = round256((size_t)E * 4);
+        w.act = round256((size_t)m * top_k * cols * 2);
+        w.parts = round256((size_t)top_k * m * H * 4);
+    } else {
+        w.act = round256((size_t)m * ecols * 2);
+        const size_t l2 = linear_scratch(m, H, ecols, TP_BF16, tpk::EPI_SWIGLU, false);
+        const size_t l3 = linear_scratch(m, ecols, H, TP_BF16, tpk::EPI_PARTIAL, false);
+        if (l2 > l) l = l2;
+        if (l3 > l) l = l3;
+    }
     w.lin = l;
-    w.total = tpk::WS_HEADER + w.u + w.logits + w.gates + w.act + w.lin;
+    w.total = tpk::WS_HEADER + w.u + w.logits + w.gates + w.slots + w.lists + w.counts + w.act + w.parts + w.lin;
     return w;
 }
 
@@ -436,9 +452,11 @@ MoeWs moe_ws(int64_t m, int64_t H, int32_t E, int64_t cols, bool norm) {
 
 extern "C" {
 
-size_t tp_moe_workspace_bytes(int64_t m, int64_t hidden, int32_t n_experts, int64_t inter_cols, int32_t has_norm) {
+size_t tp_moe_workspace_bytes(int64_t m, int64_t hidden, int32_t n_experts, int32_t top_k, int64_t inter_cols,
+                              int32_t has_norm) {
     if (m < 1 || hidden < 1 || n_experts < 1 || n_experts > 64 || inter_cols < 1) return 0;
-    return moe_ws(m, hidden, n_experts, inter_cols, has_norm != 0).total;
+    if (top_k < 1 || top_k > n_experts) return 0;
+    return moe_ws(m, hidden, n_experts, inter_cols, has_norm != 0, top_k).total;
 }
 
 tp_status tp_moe_shard_forward(const tp_moe_weights* w, const void* x, float* partial, float* gates_out,
@@ -464,16 +482,28 @@ tp_status tp_moe_shard_forward(const tp_moe_weights* w, const void* x, float* pa
     const int64_t ecols = (int64_t)n_experts * inter_cols;
     const size_t np = (size_t)m * hidden * 4;
     if (overlaps(partial, np, x, (size_t)m * hidden * 2)) return fail(TP_ERR_ALIAS, "partial overlaps x");
-    const MoeWs L = moe_ws(m, hidden, n_experts, inter_cols, w->norm != nullptr);
+    const MoeWs L = moe_ws(m, hidden, n_experts, inter_cols, w->norm != nullptr, top_k);
     TRY(check_ws(ws, ws_bytes, L.total));
     if (overlaps(ws, ws_bytes, partial, np)) return fail(TP_ERR_ALIAS, "workspace overlaps partial");
     char* b = reinterpret_cast<char*>(ws) + tpk::WS_HEADER;
     unsigned* cnt = ws_counters(ws);
     void* u = b;
-    float* logits = logits_out ? logits_out : reinterpret_cast<float*>(b + L.u);
-    float* gates = gates_out ? gates_out : reinterpret_cast<float*>(b + L.u + L.logits);
-    void* act = b + L.u + L.logits + L.gates;
-    void* lin = b + L.u + L.logits + L.gates + L.act;
+    b += L.u;
+    float* logits = logits_out ? logits_out : reinterpret_cast<float*>(b);
+    b += L.logits;
+    float* gates = gates_out ? gates_out : reinterpret_cast<float*>(b);
+    b += L.gates;
+    int* slots = reinterpret_cast<int*>(b);
+    b += L.slots;
+    int* lists = reinterpret_cast<int*>(b);
+    b += L.lists;
+    int* counts = reinterpret_cast<int*>(b);
+    b += L.counts;
+    void* act = b;
+    b += L.act;
+    float* parts = reinterpret_cast<float*>(b);
+    b += L.parts;
+    void* lin = b;
     hipStream_t s = (hipStream_t)stream;
     const void* xin = x;
     if (w->norm) {
@@ -491,8 +521,38 @@ tp_status tp_moe_shard_forward(const tp_moe_weights* w, const void* x, float* pa
     } else {
         TRY(run_linear(xin, w->w_router, nullptr, nullptr, 0.f, logits, m, hidden, n_experts, TP_BF16,
                        tpk::EPI_PARTIAL, cnt, lin, s));
-        e = tpk::moe_gates_launch(logits, gates, (int)m, n_experts, top_k, s);
+        e = tpk::moe_gates_launch(logits, gates, (int)m, n_experts, top_k, s, moe_grouped(m, top_k) ? slots : nullptr);
         if (e != hipSuccess) return hip_fail(e, "router gates launch");
+    }
+    if (moe_grouped(m, top_k)) {
+        // Each expert over its own tokens: the token lists, gate/up + SwiGLU on
+        // the gathered rows (activations packed expert after expert), down on
+        // the packed rows into the token's slot times its gate, then the top_k
+        // slots of every token added in slot (expert) order.
+        e = tpk::moe_lists_launch(slots, lists, counts, (int)m, n_experts, s);
+        if (e != hipSuccess) return hip_fail(e, "expert token lists launch");
+        tpk::GemmGroups gg{};
+        gg.counts = counts; gg.lists = lists; gg.slots = slots; gg.gates = gates; gg.G = n_experts;
+        gg.rows_total = (int)(m * top_k);
+        tpk::GemmArgs ga{};
+        ga.x = xin; ga.w = w->w_gate; ga.w_up = w->w_up; ga.y = act;
+        ga.M = (int)m; ga.N = (int)inter_cols; ga.K = (int)hidden; ga.epi = tpk::EPI_SWIGLU;
+        gg.b_group_stride = inter_cols * hidden;
+        gg.ldb = (int)hidden;
+        e = tpk::gemm_grouped_launch(ga, gg, s);
+        if (e != hipSuccess) return hip_fail(e, "grouped expert gate/up launch");
+        tpk::GemmArgs gd{};
+        gd.x = act; gd.w = w->w_down; gd.y = parts;
+        gd.M = (int)m; gd.N = (int)hidden; gd.K = (int)inter_cols; gd.epi = tpk::EPI_PARTIAL;
+        gg.b_group_stride = inter_cols;
+        gg.ldb = (int)ecols;
+        e = tpk::gemm_grouped_launch(gd, gg, s);
+        if (e != hipSuccess) return hip_fail(e, "grouped expert down launch");
+        tpk::PartialPtrs ps{};
+        for (int k = 0; k < top_k; ++k) ps.p[k] = parts + (size_t)k * m * hidden;
+        e = tpk::partial_sum_launch(ps, top_k, nullptr, partial, m * hidden, 0, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "expert slot sum launch");
+        return ok();
     }
     // Every expert's gate/up column block at once (rows stacked expert by expert).
     TRY(run_linear(xin, w->w_gate, w->w_up, nullptr, 0.f, act, m, hidden, ecols, TP_BF16, tpk::EPI_SWIGLU, cnt,

@@ -241,7 +241,8 @@ hipError_t kv_append_launch(const KvAppendArgs& a, hipStream_t s) {
 // chosen one at a time, the lowest index first among equal logits; their gates
 // are the softmax of their logits (exponentials relative to the largest,
 // added in expert order), every other gate 0.
-__device__ __forceinline__ void route_wave(float l, int E, int top_k, float* logits_row, float* gates_row) {
+__device__ __forceinline__ void route_wave(float l, int E, int top_k, float* logits_row, float* gates_row,
+                                           int* slots_row = nullptr) {
     const int e = threadIdx.x & 63;
     const bool valid = e < E;
     bool chosen = false;
@@ -256,7 +257,8 @@ __device__ __forceinline__ void route_wave(float l, int E, int top_k, float* log
         if (j == 0) mx0 = v;
     }
     const float ex = chosen ? expf(l - mx0) : 0.f;
-    uint64_t mask = __ballot(chosen);
+    const uint64_t chosen_mask = __ballot(chosen);
+    uint64_t mask = chosen_mask;
     float den = 0.f;
     while (mask) {
         const int b = __ffsll((unsigned long long)mask) - 1;
@@ -266,23 +268,61 @@ __device__ __forceinline__ void route_wave(float l, int E, int top_k, float* log
     if (valid) {
         if (logits_row) logits_row[e] = l;
         gates_row[e] = chosen ? ex / den : 0.f;
+        // rank of this expert among the chosen ones, in expert order
+        if (slots_row) slots_row[e] = chosen ? __popcll(chosen_mask & ((1ull << e) - 1ull)) : -1;
     }
 }
 
 // Gates from float32 logits [m, E]: one wave per token.
-__global__ __launch_bounds__(EW_THREADS) void moe_gates_kernel(const float* logits, float* gates, int m, int E,
-                                                               int top_k) {
+__global__ __launch_bounds__(EW_THREADS) void moe_gates_kernel(const float* logits, float* gates, int* slots, int m,
+                                                               int E, int top_k) {
     const int t = blockIdx.x * (EW_THREADS / 64) + (threadIdx.x >> 6);
     if (t >= m) return;                             // whole waves
     const int e = threadIdx.x & 63;
     const float l = e < E ? logits[(size_t)t * E + e] : 0.f;
-    route_wave(l, E, top_k, nullptr, gates + (size_t)t * E);
+    route_wave(l, E, top_k, nullptr, gates + (size_t)t * E, slots ? slots + (size_t)t * E : nullptr);
 }
 
-hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t s) {
+hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t s, int* slots) {
     constexpr int per = EW_THREADS / 64;
-    hipLaunchKernelGGL(moe_gates_kernel, dim3((m + per - 1) / per), dim3(EW_THREADS), 0, s, logits, gates, m, E,
-                       top_k);
+    hipLaunchKernelGGL(moe_gates_kernel, dim3((m + per - 1) / per), dim3(EW_THREADS), 0, s, logits, gates, slots, m,
+                       E, top_k);
+    return hipGetLastError();
+}
+
+// Token lists per expert: one workgroup per expert walks the tokens in order,
+// 256 at a time; the routed ones are compacted by a ballot, the lanes below in
+// the wave (mbcnt) and the waves before in the workgroup, so the list is in
+// ascending token order.
+__global__ __launch_bounds__(EW_THREADS) void moe_lists_kernel(const int* slots, int* lists, int* counts, int m,
+                                                               int E) {
+    constexpr int NW = EW_THREADS / 64;
+    __shared__ int wave_n[NW];
+    const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int* list = lists + (size_t)e * m;
+    int base = 0;
+    for (int t0 = 0; t0 < m; t0 += EW_THREADS) {
+        const int t = t0 + tid;
+        const bool sel = t < m && slots[(size_t)t * E + e] >= 0;
+        const uint64_t bal = __ballot(sel);
+        const int below = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_n[wave] = __popcll(bal);
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            before += w < wave ? wave_n[w] : 0;
+            total += wave_n[w];
+        }
+        if (sel) list[base + before + below] = t;
+        base += total;
+        __syncthreads();
+    }
+    if (tid == 0) counts[e] = base;
+}
+
+hipError_t moe_lists_launch(const int* slots, int* lists, int* counts, int m, int E, hipStream_t s) {
+    hipLaunchKernelGGL(moe_lists_kernel, dim3(E), dim3(EW_THREADS), 0, s, slots, lists, counts, m, E);
     return hipGetLastError();
 }
 

@@ -22,6 +22,14 @@
 // matching gate and up accumulators, so silu(gate) * up is formed in registers
 // and only the activation is written.
 //
+// Grouped launches (mixture of experts): the same tiles over each expert's own
+// tokens, whose counts are read on the device; a workgroup finds its expert
+// and tile row from them, and workgroups past the last expert's tiles return
+// before any transfer. Gate/up gathers the expert's token rows
+// through its list and packs the activations expert after expert; down reads
+// those packed rows and writes each row, times the token's gate, to the
+// token's slot (its rank among its experts) of a [top_k, M, N] buffer.
+//
 // MFMA operand layout (32x32x16): lane l supplies row (l % 32) of A and column
 // (l % 32) of B, 8 consecutive k each, the two lane halves covering k 0-7 and
 // 8-15. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
@@ -48,6 +56,8 @@ struct GemmDev {
     void* y;
     int M, N, K;
     int tiles_m, tiles_n;
+    int ldb;              // B row stride (elements): K unless grouped
+    GemmGroups grp;       // grouped launches only
 };
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
@@ -63,7 +73,7 @@ __device__ __forceinline__ void dma16(const uint16_t* src, unsigned char* lds_ba
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-template <int EPI>
+template <int EPI, bool GRP>
 __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     constexpr bool SWI = (EPI == EPI_SWIGLU);
     constexpr int BN_OUT = SWI ? GM_BN / 2 : GM_BN;
@@ -80,20 +90,50 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     // each XCD gets a contiguous run of tiles. Then groups of GM_GROUP_M tile
     // rows sweep the tile columns together, so the A rows of a group and the
     // B columns in flight stay in that XCD's L2.
-    const int nblocks = d.tiles_m * d.tiles_n;
-    const int per_xcd = nblocks / 8;
-    int pid = blockIdx.x;
-    if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
-    const int per_group = GM_GROUP_M * d.tiles_n;
-    const int group = pid / per_group;
-    const int first_m = group * GM_GROUP_M;
-    const int gsize = min(d.tiles_m - first_m, GM_GROUP_M);
-    const int tm = first_m + (pid % per_group) % gsize;
-    const int tn = (pid % per_group) / gsize;
+    // A grouped launch learns each group's row count on the device. Its grid
+    // covers the most tile rows the groups can need (sum of counts / 256 + G)
+    // times the tile columns; workgroup (rt, tn) takes tile row rt of the
+    // groups' rows laid end to end, tile column tn. Numbered row by row, the
+    // live tiles are spread over all XCDs by the round-robin dispatch.
+    int tm = 0, tn;
+    int g = 0, M = d.M, grow0 = 0;
+    if (GRP) {
+        int rt = (int)blockIdx.x / d.tiles_n;
+        tn = (int)blockIdx.x % d.tiles_n;
+        g = -1;
+        for (int e = 0; e < d.grp.G; ++e) {
+            const int c = d.grp.counts[e];
+            const int nt = (c + GM_BM - 1) / GM_BM;
+            if (g < 0) {
+                if (rt < nt) {
+                    g = e;
+                    tm = rt;
+                    M = c;
+                } else {
+                    rt -= nt;
+                    grow0 += c;
+                }
+            }
+        }
+        if (g < 0) return;      // past the last group's tiles
+    } else {
+        const int nblocks = d.tiles_m * d.tiles_n;
+        const int per_xcd = nblocks / 8;
+        int pid = blockIdx.x;
+        if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
+        const int per_group = GM_GROUP_M * d.tiles_n;
+        const int group = pid / per_group;
+        const int first_m = group * GM_GROUP_M;
+        const int gsize = min(d.tiles_m - first_m, GM_GROUP_M);
+        tm = first_m + (pid % per_group) % gsize;
+        tn = (pid % per_group) / gsize;
+    }
     const int m0 = tm * GM_BM;
     const int n0 = tn * BN_OUT;
-    const int M = d.M, N = d.N, K = d.K;
+    const int N = d.N, K = d.K;
     const int KT = (K + GM_BK - 1) / GM_BK;
+    const uint16_t* wb = d.w + (GRP ? (size_t)g * d.grp.b_group_stride : 0);
+    const uint16_t* wub = SWI ? d.w_up + (GRP ? (size_t)g * d.grp.b_group_stride : 0) : nullptr;
 
     // Chunks this thread moves per K tile: transfer j of wave w fills slots
     // p = (j * 8 + w) * 64 + lane of each tile, i.e. row p / 8, slot p % 8,
@@ -108,17 +148,20 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
         const int p = (j * 8 + wave) * 64 + lane;
         const int row = p >> 3;
         kc[j] = ((p & 7) ^ ((row >> 1) & 7)) * 8;
-        a_src[j] = d.x + (size_t)min(m0 + row, M - 1) * K + kc[j];
+        const int r = min(m0 + row, M - 1);
+        int arow = r;
+        if (GRP) arow = SWI ? d.grp.lists[(size_t)g * d.M + r] : grow0 + r;   // gathered tokens / packed rows
+        a_src[j] = d.x + (size_t)arow * K + kc[j];
         int bn;
         const uint16_t* base;
         if (SWI) {
             bn = n0 + (row & 127);
-            base = row < 128 ? d.w : d.w_up;
+            base = row < 128 ? wb : wub;
         } else {
             bn = n0 + row;
-            base = d.w;
+            base = wb;
         }
-        b_src[j] = base + (size_t)min(bn, N - 1) * K + kc[j];
+        b_src[j] = base + (size_t)min(bn, N - 1) * d.ldb + kc[j];
     }
     // Chunks past K (ragged last tile) are fetched from a clamped in-bounds
     // offset and zeroed in LDS once they have landed.
@@ -214,19 +257,28 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
             if (SWI) {
                 const int col = n0 + wn * 32 + col_l;
                 if (col < N) {
-                    const float g = acc[i][0][r], u = acc[i][1][r];
-                    reinterpret_cast<uint16_t*>(d.y)[(size_t)row * N + col] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+                    const float gt = acc[i][0][r], u = acc[i][1][r];
+                    const size_t orow = GRP ? (size_t)grow0 + row : (size_t)row;   // grouped: packed rows
+                    reinterpret_cast<uint16_t*>(d.y)[orow * N + col] = (uint16_t)f32_to_bf16_bits(silu_f32(gt) * u);
                 }
             } else {
+                size_t orow = (size_t)row;
+                float scl = 1.0f;
+                if (GRP) {
+                    // token of this row, its slot among its experts, its gate
+                    const int t = d.grp.lists[(size_t)g * d.M + row];
+                    orow = (size_t)d.grp.slots[(size_t)t * d.grp.G + g] * d.M + t;
+                    scl = d.grp.gates[(size_t)t * d.grp.G + g];
+                }
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const int col = n0 + wn * 64 + j * 32 + col_l;
                     if (col >= N) continue;
                     const float v = acc[i][j][r];
                     if (EPI == EPI_PARTIAL)
-                        reinterpret_cast<float*>(d.y)[(size_t)row * N + col] = v;
+                        reinterpret_cast<float*>(d.y)[orow * N + col] = GRP ? v * scl : v;
                     else
-                        reinterpret_cast<uint16_t*>(d.y)[(size_t)row * N + col] = (uint16_t)f32_to_bf16_bits(v);
+                        reinterpret_cast<uint16_t*>(d.y)[orow * N + col] = (uint16_t)f32_to_bf16_bits(v);
                 }
             }
         }
@@ -238,9 +290,9 @@ bool gemm_supported(int M, int N, int K, int epi) {
     return M > 0 && N > 0 && K > 0 && (K % 8) == 0 && epi != EPI_QKV;
 }
 
-template <int EPI>
+template <int EPI, bool GRP>
 static hipError_t gemm_launch_t(const GemmDev& d, hipStream_t s) {
-    hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, dim3(d.tiles_m * d.tiles_n), dim3(GM_NT), 0, s, d);
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, GRP>), dim3(d.tiles_m * d.tiles_n), dim3(GM_NT), 0, s, d);
     return hipGetLastError();
 }
 
@@ -254,10 +306,30 @@ hipError_t gemm_launch(const GemmArgs& a, hipStream_t s) {
     const int bn_out = a.epi == EPI_SWIGLU ? GM_BN / 2 : GM_BN;
     d.tiles_m = (a.M + GM_BM - 1) / GM_BM;
     d.tiles_n = (a.N + bn_out - 1) / bn_out;
+    d.ldb = a.K;
     switch (a.epi) {
-        case EPI_STORE: return gemm_launch_t<EPI_STORE>(d, s);
-        case EPI_PARTIAL: return gemm_launch_t<EPI_PARTIAL>(d, s);
-        case EPI_SWIGLU: return gemm_launch_t<EPI_SWIGLU>(d, s);
+        case EPI_STORE: return gemm_launch_t<EPI_STORE, false>(d, s);
+        case EPI_PARTIAL: return gemm_launch_t<EPI_PARTIAL, false>(d, s);
+        case EPI_SWIGLU: return gemm_launch_t<EPI_SWIGLU, false>(d, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t gemm_grouped_launch(const GemmArgs& a, const GemmGroups& g, hipStream_t s) {
+    GemmDev d{};
+    d.x = reinterpret_cast<const uint16_t*>(a.x);
+    d.w = reinterpret_cast<const uint16_t*>(a.w);
+    d.w_up = reinterpret_cast<const uint16_t*>(a.w_up);
+    d.y = a.y;
+    d.M = a.M; d.N = a.N; d.K = a.K;
+    const int bn_out = a.epi == EPI_SWIGLU ? GM_BN / 2 : GM_BN;
+    d.tiles_m = (g.rows_total + GM_BM - 1) / GM_BM + g.G;   // sum over groups of ceil(count / 256), at most
+    d.tiles_n = (a.N + bn_out - 1) / bn_out;
+    d.ldb = g.ldb;
+    d.grp = g;
+    switch (a.epi) {
+        case EPI_PARTIAL: return gemm_launch_t<EPI_PARTIAL, true>(d, s);
+        case EPI_SWIGLU: return gemm_launch_t<EPI_SWIGLU, true>(d, s);
     }
     return hipErrorInvalidValue;
 }

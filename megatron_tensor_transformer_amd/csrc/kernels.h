@@ -113,10 +113,35 @@ struct GemmArgs {
 bool gemm_supported(int M, int N, int K, int epi);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
 
+// Grouped prefill projections of a mixture of experts: G independent GEMMs,
+// one per expert g, whose row counts live on the device (counts[g] <= M).
+// Rows of group g are packed after those of groups 0..g-1 (offset = the sum
+// of the earlier counts). Column-parallel gate/up + SwiGLU (EPI_SWIGLU): A
+// rows gathered through lists[g * M + r] from x [M, K]; B = w (and w_up) +
+// g * b_group_stride, rows of ldb elements; y [sum of counts, N] packed.
+// Row-parallel down (EPI_PARTIAL): A = x rows offset + r (packed); B as
+// above; row r of group g is token t = lists[g * M + r] and is written,
+// times gates[t * G + g], to y[(slots[t * G + g] * M + t) * N + n].
+struct GemmGroups {
+    const int* counts;      // [G]
+    const int* lists;       // [G][M] token indices in ascending order
+    const int* slots;       // [M][G] rank of expert g among the token's experts, -1 if not chosen
+    const float* gates;     // [M][G]
+    int64_t b_group_stride; // elements between consecutive groups' B blocks
+    int ldb;                // B row stride (elements)
+    int G;
+    int rows_total;         // sum of the counts (M * top_k): bounds the groups' row tiles
+};
+hipError_t gemm_grouped_launch(const GemmArgs& a, const GemmGroups& g, hipStream_t stream);
+
 // Mixture of experts: top-k router gates from float32 logits [m, E] (E <= 64),
 // and a[t, e * cols + i] *= gates[t, e] on bf16 expert activations
 // (cols a multiple of 8).
-hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t stream);
+hipError_t moe_gates_launch(const float* logits, float* gates, int m, int E, int top_k, hipStream_t stream,
+                            int* slots = nullptr);
+// Per-expert token lists from the routing slots [m, E]: lists[e * m + i] the
+// i-th token (ascending) routed to expert e, counts[e] how many.
+hipError_t moe_lists_launch(const int* slots, int* lists, int* counts, int m, int E, hipStream_t stream);
 // Router logits (written when logits is not null) and gates of m tokens in one
 // launch, from bf16 u [m, H] and W_router [E, H] (H a multiple of 8; few
 // tokens: one workgroup each reads all of W_router).

@@ -200,7 +200,7 @@ def test_bf16_partial_validation():
 
 def test_moe_validation():
     w = tp.tp_moe_weights(A, A + 64 * MB, A + 128 * MB, A + 1024 * MB, A + 2048 * MB)
-    need = tp.tp_moe_workspace_bytes(16, 4096, 8, 7168, True)
+    need = tp.tp_moe_workspace_bytes(16, 4096, 8, 2, 7168, True)
     assert need > 16 * 8 * 7168 * 2
 
     def f(weights=w, x=A + 3000 * MB, part=A + 3100 * MB, g=None, lg=None, m=16, H=4096, E=8, k=2, cols=7168,
@@ -217,7 +217,13 @@ def test_moe_validation():
     assert f(part=A + 3000 * MB + 256) == "TP_ERR_ALIAS"
     assert f(wsn=need - 256) == "TP_ERR_WORKSPACE"
     assert f(g=A + 5) == "TP_ERR_ALIGN"
-    assert tp.tp_moe_workspace_bytes(16, 4096, 0, 7168, True) == 0
+    assert tp.tp_moe_workspace_bytes(16, 4096, 0, 1, 7168, True) == 0
+    assert tp.tp_moe_workspace_bytes(16, 4096, 8, 9, 7168, True) == 0
+    # above 64 tokens each expert runs over its own tokens: activations for m * top_k rows, and the
+    # top_k slot partials
+    big = tp.tp_moe_workspace_bytes(4096, 4096, 8, 2, 7168, True)
+    assert big >= 4096 * 2 * 7168 * 2 + 2 * 4096 * 4096 * 4
+    assert big < 4096 * 8 * 7168 * 2 + 2 * 4096 * 4096 * 4 + (64 << 20)
 
 
 def attn(q=A, k=A + 64 * MB, v=A + 128 * MB, out=A + 192 * MB, B=16, qh=8, kvh=1, d=128, cap=8192, L=8192,

@@ -204,3 +204,129 @@ def test_split_k_more_tiles_than_counters(case):
     if mode == "swiglu":
         ref = L.swiglu(ref, L.linear(x, wu.T))
     check(f"{mode} m={m} k={k} n={n} {dt}", host(y), ref, TOL[dt])
+
+
+# ---------------------------------------------------------------- MoE over per-expert token lists (prefill)
+
+def _moe_inputs(seed, H, I, E, m):
+    inp = W.moe_inputs(seed, H, I, E, m, "bf16")
+    return inp["x"], inp["gamma"], inp["w_router"], inp["experts"]
+
+
+def _moe_rank_phys(experts, p):
+    b, c = p.inter_begin, p.inter_cols
+    wg = np.concatenate([phys(g[:, b:b + c]) for g, _, _ in experts], axis=0)
+    wu = np.concatenate([phys(u[:, b:b + c]) for _, u, _ in experts], axis=0)
+    wd = np.concatenate([phys(d[b:b + c, :]) for _, _, d in experts], axis=1)
+    return wg, wu, wd
+
+
+def _run_moe(x, gamma, w_router, experts, E, k, t, H, I):
+    m = x.shape[0]
+    desc = tp.make_desc(H, I)
+    xd, gd, rd = dev(x, "bf16"), dev(gamma, "bf16"), dev(phys(w_router), "bf16")
+    parts, gates, logits, plans = [], [], [], []
+    for r in range(t):
+        p = tp.tp_shard_plan(desc, t, r)
+        wg, wu, wd = _moe_rank_phys(experts, p)
+        w = {"norm": gd, "w_router": rd, "w_gate": dev(wg, "bf16"), "w_up": dev(wu, "bf16"),
+             "w_down": dev(wd, "bf16")}
+        part = empty((m, H), torch.float32)
+        g = empty((m, E), torch.float32)
+        lg = empty((m, E), torch.float32)
+        tp.tp_moe_shard_forward(w, xd, part, E, k, p.inter_cols, gates=g, logits=lg)
+        torch.cuda.synchronize()
+        del w, wg, wu, wd
+        parts.append(part); gates.append(g); logits.append(lg); plans.append(p)
+    out = empty((m, H), torch.float32)
+    tp.tp_partial_sum(parts, out)
+    torch.cuda.synchronize()
+    return parts, gates, logits, out
+
+
+def _check_routing(gates, logits, k, E, t):
+    lg0, g0 = host(logits[0]), host(gates[0])
+    for r in range(1, t):
+        assert np.array_equal(host(gates[r]), g0), "ranks disagree on the routing"
+    # the routing decision taken in the kernel's precision: top-k of the GPU's logits
+    g_ref = L.moe_route(lg0, k)
+    assert np.array_equal(g0 > 0, g_ref > 0), "top-k selection differs"
+    assert np.max(np.abs(g0 - g_ref)) < 1e-5
+    return g0
+
+
+GROUPED_MOE_CASES = [
+    # hidden, intermediate (per expert), experts, top_k, t, tokens
+    (512, 1024, 8, 2, 2, 300),       # ragged expert counts, one tile each
+    (1024, 2816, 8, 2, 2, 1000),     # several expert tiles, ragged K of neither
+    (256, 512, 4, 1, 1, 600),        # top-1
+    (256, 512, 8, 8, 1, 130),        # every expert for every token: eight slots
+    (384, 784, 16, 3, 2, 257),       # 16 experts, top-3, a token past one 256-row tile
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", GROUPED_MOE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_moe_grouped_bf16(case):
+    H, I, E, k, t, m = case
+    x, gamma, w_router, experts = _moe_inputs(110 + E + k, H, I, E, m)
+    parts, gates, logits, out = _run_moe(x, gamma, w_router, experts, E, k, t, H, I)
+    ref = L.moe_block(x, gamma, w_router, experts, k)
+    check("router logits", host(logits[0]), ref["logits"], TOL["bf16"])
+    g0 = _check_routing(gates, logits, k, E, t)
+    odesc = OP.ModelDesc(hidden=H, intermediate=I)
+    small = m * H * I * E <= 2e9      # the sharded oracle's einsum products run on one thread
+    for r in range(t):
+        op = OP.rank_plan(odesc, t, r)
+        if small:
+            pr = S.rank_moe(x, gamma, w_router, experts, g0, op)["partial"]
+        else:
+            b, c = op["inter_begin"], op["inter_cols"]
+            ex_r = [(g[:, b:b + c], u[:, b:b + c], d[b:b + c, :]) for g, u, d in experts]
+            pr = L.moe_block(x, gamma, w_router, ex_r, k, gates=g0)["y"]
+        check(f"rank{r} MoE partial", host(parts[r]), pr, TOL["bf16"])
+    yref = L.moe_block(x, gamma, w_router, experts, k, gates=g0)["y"]
+    check(f"sum of {t} MoE partials", host(out), yref, TOL["bf16"])
+
+
+@pytest.mark.timeout(600)
+def test_moe_grouped_idle_and_full_experts():
+    """A router that sends every token to experts 0 and 1: those two run over all 600 tokens (three
+    row tiles), the other six over none."""
+    H, I, E, k, t, m = 256, 512, 8, 2, 2, 600
+    x, gamma, w_router, experts = _moe_inputs(131, H, I, E, m)
+    x = W.to_bf16(np.abs(x) + 1.0)
+    w_router = W.to_bf16(np.concatenate([np.full((H, 1), 0.05), np.full((H, 1), 0.03),
+                                         W.normal(131, 40, (H, E - 2), 0.001)], axis=1).astype(np.float32))
+    gamma = np.ones(H, np.float32)
+    parts, gates, logits, out = _run_moe(x, gamma, w_router, experts, E, k, t, H, I)
+    g0 = _check_routing(gates, logits, k, E, t)
+    assert np.all(g0[:, 0] > 0) and np.all(g0[:, 1] > 0) and not np.any(g0[:, 2:])
+    yref = L.moe_block(x, gamma, w_router, experts, k, gates=g0)["y"]
+    check("sum of 2 MoE partials", host(out), yref, TOL["bf16"])
+
+
+@pytest.mark.timeout(900)
+def test_moe_grouped_mixtral_prefill():
+    """The Mixtral-8x7B-shaped MoE FFN shard (hidden 4096, 8 experts of intermediate 14336, top-2, t=2)
+    over 4096 prefill tokens, every row: each rank's partial against the oracle's MoE block on that
+    rank's column / row blocks of every expert (BLAS products, the GPU's routing), and their sum."""
+    H, I, E, k, t, m = 4096, 14336, 8, 2, 2, 4096
+    say("drawing the Mixtral-shaped experts")
+    x, gamma, w_router, experts = _moe_inputs(9, H, I, E, m)
+    parts, gates, logits, out = _run_moe(x, gamma, w_router, experts, E, k, t, H, I)
+    g0 = _check_routing(gates, logits, k, E, t)
+    counts = np.count_nonzero(g0, axis=0)
+    say(f"  tokens per expert: {counts.tolist()}")
+    odesc = OP.ModelDesc(hidden=H, intermediate=I)
+    refs = []
+    for r in range(t):
+        op = OP.rank_plan(odesc, t, r)
+        b, c = op["inter_begin"], op["inter_cols"]
+        ex_r = [(L.f64(g[:, b:b + c]), L.f64(u[:, b:b + c]), L.f64(d[b:b + c, :])) for g, u, d in experts]
+        say(f"oracle: rank {r}")
+        yr = L.moe_block(x, gamma, w_router, ex_r, k, gates=g0)["y"]
+        check(f"rank{r} MoE partial (all rows)", host(parts[r]), yr, TOL["bf16"])
+        refs.append(yr)
+        del ex_r
+    check("sum of 2 MoE partials (all rows)", host(out), S.sum_partials(refs), TOL["bf16"])

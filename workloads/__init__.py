@@ -113,6 +113,9 @@ WORKLOADS: Dict[int, Workload] = {
     8: Workload(8, "Mixtral-8x7B-shaped MoE FFN decode shard, bf16, hidden 4096, 8 experts x intermediate "
                    "14336, top-2, t=2, 16 tokens", "bf16", hidden=4096, intermediate=14336, t=2, tokens=(16,),
                 norm=True),
+    9: Workload(9, "Mixtral-8x7B-shaped MoE FFN prefill shard, bf16, hidden 4096, 8 experts x intermediate "
+                   "14336, top-2, t=2, 4096 tokens", "bf16", hidden=4096, intermediate=14336, t=2, tokens=(4096,),
+                norm=True),
     7: Workload(7, "70B-shaped full layer prefill shard, bf16, t=8, batch 2 x 2048 tokens",
                 "bf16", hidden=8192, intermediate=28672, t=8, tokens=(4096,), n_q_heads=64, n_kv_heads=8,
                 head_dim=128, kv_len=2048, norm=True),
