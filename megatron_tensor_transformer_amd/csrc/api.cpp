@@ -92,15 +92,21 @@ bool use_gemm(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi) {
     return dt == TP_BF16 && epi != tpk::EPI_QKV && m > kGemvMaxM && tpk::gemm_supported((int)m, (int)n, (int)k, epi);
 }
 
-// Scratch bytes (after the counter header) a projection needs: the normalised
-// activations on the GEMM path with a norm, the split-K slices on the GEMV path.
+// Scratch bytes (after the counter header) a projection needs: on the GEMM
+// path the normalised activations (with a norm) and the K-range sums of its
+// last partial round of tiles; on the GEMV path the split-K slices.
+size_t gemm_norm_bytes(int64_t m, int64_t k, tp_dtype dt, bool norm) {
+    return norm ? round256((size_t)m * k * esize(dt)) : 0;
+}
+
 size_t linear_scratch(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
-    if (use_gemm(m, k, n, dt, epi)) return norm ? round256((size_t)m * k * esize(dt)) : 0;
+    if (use_gemm(m, k, n, dt, epi))
+        return gemm_norm_bytes(m, k, dt, norm) + round256(tpk::gemm_scratch_bytes((int)m, (int)n, (int)k, epi));
     return round256(tpk::gemv_plan((int)m, (int)k, (int)n, dt == TP_BF16, epi).ws_bytes);
 }
 
 bool linear_needs_ws(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
-    if (use_gemm(m, k, n, dt, epi)) return norm;
+    if (use_gemm(m, k, n, dt, epi)) return linear_scratch(m, k, n, dt, epi, norm) > 0;
     return tpk::gemv_plan((int)m, (int)k, (int)n, dt == TP_BF16, epi).splits > 1;
 }
 
@@ -125,6 +131,7 @@ tp_status run_linear(const void* x, const void* w, const void* w_up, const void*
         tpk::GemmArgs g{};
         g.x = xin; g.w = w; g.w_up = w_up; g.y = y;
         g.M = (int)m; g.N = (int)n; g.K = (int)k; g.epi = epi;
+        g.scratch = scratch ? reinterpret_cast<char*>(scratch) + gemm_norm_bytes(m, k, dt, norm) : nullptr;
         hipError_t e = tpk::gemm_launch(g, s);
         if (e != hipSuccess) return hip_fail(e, "MFMA GEMM launch");
         return ok();

@@ -34,6 +34,8 @@
 // (l % 32) of B, 8 consecutive k each, the two lane halves covering k 0-7 and
 // 8-15. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l % 32.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -58,6 +60,11 @@ struct GemmDev {
     int tiles_m, tiles_n;
     int ldb;              // B row stride (elements): K unless grouped
     GemmGroups grp;       // grouped launches only
+    // Tail split (ungrouped): workgroups past full_tiles take one of split
+    // K ranges of kts K tiles of a tail tile and store their float32 sums to
+    // part; gemm_tail_kernel adds them and runs the epilogue.
+    int full_tiles, split, kts;
+    float* part;          // [tail tiles][split][GM_BM][GM_BN]
 };
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
@@ -73,6 +80,24 @@ __device__ __forceinline__ void dma16(const uint16_t* src, unsigned char* lds_ba
                                      (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Tile (tm, tn) of workgroup w of an ungrouped launch: workgroups are
+// dispatched to the 8 XCDs round robin; renumber them so each XCD gets a
+// contiguous run of tiles. Then groups of GM_GROUP_M tile rows sweep the tile
+// columns together, so the A rows of a group and the B columns in flight stay
+// in that XCD's L2.
+__device__ __forceinline__ void gemm_tile_of(const GemmDev& d, int w, int& tm, int& tn) {
+    const int nblocks = d.tiles_m * d.tiles_n;
+    const int per_xcd = nblocks / 8;
+    int pid = w;
+    if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
+    const int per_group = GM_GROUP_M * d.tiles_n;
+    const int group = pid / per_group;
+    const int first_m = group * GM_GROUP_M;
+    const int gsize = min(d.tiles_m - first_m, GM_GROUP_M);
+    tm = first_m + (pid % per_group) % gsize;
+    tn = (pid % per_group) / gsize;
+}
+
 template <int EPI, bool GRP>
 __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     constexpr bool SWI = (EPI == EPI_SWIGLU);
@@ -86,17 +111,16 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
 
-    // Workgroups are dispatched to the 8 XCDs round robin; renumber them so
-    // each XCD gets a contiguous run of tiles. Then groups of GM_GROUP_M tile
-    // rows sweep the tile columns together, so the A rows of a group and the
-    // B columns in flight stay in that XCD's L2.
-    // A grouped launch learns each group's row count on the device. Its grid
+    // Ungrouped: the tile order of gemm_tile_of; a tail tile's K is split over
+    // d.split workgroups. A grouped launch learns each group's row count on the device. Its grid
     // covers the most tile rows the groups can need (sum of counts / 256 + G)
     // times the tile columns; workgroup (rt, tn) takes tile row rt of the
     // groups' rows laid end to end, tile column tn. Numbered row by row, the
     // live tiles are spread over all XCDs by the round-robin dispatch.
     int tm = 0, tn;
     int g = 0, M = d.M, grow0 = 0;
+    int kt0 = 0, kt1 = (d.K + GM_BK - 1) / GM_BK;   // K tiles of this workgroup
+    int tail = -1, tail_part = 0;                  // tail tile index and K range, or -1
     if (GRP) {
         int rt = (int)blockIdx.x / d.tiles_n;
         tn = (int)blockIdx.x % d.tiles_n;
@@ -117,21 +141,22 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
         }
         if (g < 0) return;      // past the last group's tiles
     } else {
-        const int nblocks = d.tiles_m * d.tiles_n;
-        const int per_xcd = nblocks / 8;
-        int pid = blockIdx.x;
-        if (pid < per_xcd * 8) pid = (pid % 8) * per_xcd + pid / 8;
-        const int per_group = GM_GROUP_M * d.tiles_n;
-        const int group = pid / per_group;
-        const int first_m = group * GM_GROUP_M;
-        const int gsize = min(d.tiles_m - first_m, GM_GROUP_M);
-        tm = first_m + (pid % per_group) % gsize;
-        tn = (pid % per_group) / gsize;
+        int w = blockIdx.x;
+        if (w >= d.full_tiles) {
+            const int q = w - d.full_tiles;
+            tail = q / d.split;
+            tail_part = q - tail * d.split;
+            w = d.full_tiles + tail;
+            kt0 = tail_part * d.kts;
+            kt1 = min(kt1, kt0 + d.kts);
+        }
+        gemm_tile_of(d, w, tm, tn);
     }
     const int m0 = tm * GM_BM;
     const int n0 = tn * BN_OUT;
     const int N = d.N, K = d.K;
-    const int KT = (K + GM_BK - 1) / GM_BK;
+    const int KT = (K + GM_BK - 1) / GM_BK;        // K tiles of the whole contraction
+    const int KL = kt1 - kt0;                      // K tiles of this workgroup
     const uint16_t* wb = d.w + (GRP ? (size_t)g * d.grp.b_group_stride : 0);
     const uint16_t* wub = SWI ? d.w_up + (GRP ? (size_t)g * d.grp.b_group_stride : 0) : nullptr;
 
@@ -226,23 +251,40 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
 
     // K tile kt lives in stage kt % 2; the loop body covers two tiles so each
     // access names its stage statically.
+    // kt counts this workgroup's K tiles from kt0; only the contraction's last
+    // K tile can be ragged.
     auto step = [&](int kt, unsigned char* cur, unsigned char* nxt) {
-        const bool more = kt + 1 < KT;
-        if (more) load_stage((kt + 1) * GM_BK, nxt);
+        const bool more = kt + 1 < KL;
+        if (more) load_stage((kt0 + kt + 1) * GM_BK, nxt);
         compute(cur);
         if (more) {
             __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
-            if (ragged && kt + 2 == KT) zero_tail((kt + 1) * GM_BK, nxt);
+            if (ragged && kt0 + kt + 2 == KT) zero_tail((kt0 + kt + 1) * GM_BK, nxt);
         }
         __syncthreads();
     };
-    load_stage(0, stage0);
+    load_stage(kt0 * GM_BK, stage0);
     __builtin_amdgcn_s_waitcnt(0);
-    if (ragged && KT == 1) zero_tail(0, stage0);
+    if (ragged && kt0 + 1 == KT) zero_tail(kt0 * GM_BK, stage0);
     __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
+    for (int kt = 0; kt < KL; kt += 2) {
         step(kt, stage0, stage1);
-        if (kt + 1 < KT) step(kt + 1, stage1, stage0);
+        if (kt + 1 < KL) step(kt + 1, stage1, stage0);
+    }
+
+    if (!GRP && tail >= 0) {
+        // A part of a tail tile: its float32 sums, [row][B row of the tile].
+        float* pt = d.part + ((size_t)tail * d.split + tail_part) * GM_BM * GM_BN;
+        const int row_l = 4 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 128 + i * 32 + 8 * (r >> 2) + row_l + (r & 3);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) pt[(size_t)row * GM_BN + b_row[j]] = acc[i][j][r];   // column lane % 32
+            }
+        return;
     }
 
     // Epilogue.
@@ -286,13 +328,82 @@ __global__ __launch_bounds__(GM_NT, 1) void gemm_bf16_kernel(GemmDev d) {
 }
 
 
+// The tail tiles of an ungrouped launch: the sum of their K ranges' float32
+// partials in range order, then the epilogue. One workgroup per 8 rows of a
+// tail tile, a thread per column.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_tail_kernel(GemmDev d) {
+    constexpr bool SWI = (EPI == EPI_SWIGLU);
+    constexpr int BN_OUT = SWI ? GM_BN / 2 : GM_BN;
+    constexpr int ROWS = 8;
+    const int t = blockIdx.x / (GM_BM / ROWS);
+    const int r0 = (blockIdx.x % (GM_BM / ROWS)) * ROWS;
+    int tm, tn;
+    gemm_tile_of(d, d.full_tiles + t, tm, tn);
+    const int c = threadIdx.x;
+    if (c >= BN_OUT) return;
+    const int n = tn * BN_OUT + c;
+    if (n >= d.N) return;
+    const float* pt = d.part + (size_t)t * d.split * GM_BM * GM_BN;
+    for (int rr = 0; rr < ROWS; ++rr) {
+        const int row = r0 + rr;
+        const int m = tm * GM_BM + row;
+        if (m >= d.M) break;
+        float v = 0.f, u = 0.f;
+        for (int q = 0; q < d.split; ++q) {
+            const float* pr = pt + ((size_t)q * GM_BM + row) * GM_BN;
+            v += pr[c];
+            if (SWI) u += pr[GM_BN / 2 + c];
+        }
+        if (SWI)
+            reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.N + n] = (uint16_t)f32_to_bf16_bits(silu_f32(v) * u);
+        else if (EPI == EPI_PARTIAL)
+            reinterpret_cast<float*>(d.y)[(size_t)m * d.N + n] = v;
+        else
+            reinterpret_cast<uint16_t*>(d.y)[(size_t)m * d.N + n] = (uint16_t)f32_to_bf16_bits(v);
+    }
+}
+
+// How an ungrouped launch splits the K of its tail tiles. With fewer than 256
+// tiles all of them are tail tiles; otherwise those of the last partial round
+// of 256. Each tail tile's K goes to `split` workgroups (at least 4 K tiles
+// each, at most one per compute unit in the last round); split 1 means none.
+struct TailPlan {
+    int tiles, full, tail, split, kts;
+};
+static TailPlan gemm_tail_plan(int M, int N, int K, int epi) {
+    TailPlan t{};
+    const int bn_out = epi == EPI_SWIGLU ? GM_BN / 2 : GM_BN;
+    t.tiles = ((M + GM_BM - 1) / GM_BM) * ((N + bn_out - 1) / bn_out);
+    const int KT = (K + GM_BK - 1) / GM_BK;
+    t.tail = t.tiles % 256;
+    t.full = t.tiles - t.tail;
+    int sp = t.tail ? std::min(256 / t.tail, KT / 4) : 1;
+    if (sp < 2) {
+        t.full = t.tiles;
+        t.tail = 0;
+        t.split = 1;
+        t.kts = KT;
+        return t;
+    }
+    t.kts = (KT + sp - 1) / sp;
+    t.split = (KT + t.kts - 1) / t.kts;           // no empty range
+    return t;
+}
+
+size_t gemm_scratch_bytes(int M, int N, int K, int epi) {
+    if (epi == EPI_QKV) return 0;
+    const TailPlan t = gemm_tail_plan(M, N, K, epi);
+    return (size_t)t.tail * t.split * GM_BM * GM_BN * 4;
+}
+
 bool gemm_supported(int M, int N, int K, int epi) {
     return M > 0 && N > 0 && K > 0 && (K % 8) == 0 && epi != EPI_QKV;
 }
 
 template <int EPI, bool GRP>
-static hipError_t gemm_launch_t(const GemmDev& d, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, GRP>), dim3(d.tiles_m * d.tiles_n), dim3(GM_NT), 0, s, d);
+static hipError_t gemm_launch_t(const GemmDev& d, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI, GRP>), dim3(grid), dim3(GM_NT), 0, s, d);
     return hipGetLastError();
 }
 
@@ -307,12 +418,27 @@ hipError_t gemm_launch(const GemmArgs& a, hipStream_t s) {
     d.tiles_m = (a.M + GM_BM - 1) / GM_BM;
     d.tiles_n = (a.N + bn_out - 1) / bn_out;
     d.ldb = a.K;
+    const TailPlan t = gemm_tail_plan(a.M, a.N, a.K, a.epi);
+    d.full_tiles = t.full;
+    d.split = t.split;
+    d.kts = t.kts;
+    d.part = reinterpret_cast<float*>(a.scratch);
+    if (t.tail && !a.scratch) return hipErrorInvalidValue;
+    const int grid = t.full + t.tail * t.split;
+    hipError_t e = hipErrorInvalidValue;
     switch (a.epi) {
-        case EPI_STORE: return gemm_launch_t<EPI_STORE, false>(d, s);
-        case EPI_PARTIAL: return gemm_launch_t<EPI_PARTIAL, false>(d, s);
-        case EPI_SWIGLU: return gemm_launch_t<EPI_SWIGLU, false>(d, s);
+        case EPI_STORE: e = gemm_launch_t<EPI_STORE, false>(d, grid, s); break;
+        case EPI_PARTIAL: e = gemm_launch_t<EPI_PARTIAL, false>(d, grid, s); break;
+        case EPI_SWIGLU: e = gemm_launch_t<EPI_SWIGLU, false>(d, grid, s); break;
     }
-    return hipErrorInvalidValue;
+    if (e != hipSuccess || !t.tail) return e;
+    const dim3 fg(t.tail * (GM_BM / 8));
+    switch (a.epi) {
+        case EPI_STORE: hipLaunchKernelGGL(gemm_tail_kernel<EPI_STORE>, fg, dim3(256), 0, s, d); break;
+        case EPI_PARTIAL: hipLaunchKernelGGL(gemm_tail_kernel<EPI_PARTIAL>, fg, dim3(256), 0, s, d); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL(gemm_tail_kernel<EPI_SWIGLU>, fg, dim3(256), 0, s, d); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t gemm_grouped_launch(const GemmArgs& a, const GemmGroups& g, hipStream_t s) {
@@ -327,9 +453,10 @@ hipError_t gemm_grouped_launch(const GemmArgs& a, const GemmGroups& g, hipStream
     d.tiles_n = (a.N + bn_out - 1) / bn_out;
     d.ldb = g.ldb;
     d.grp = g;
+    const int grid = d.tiles_m * d.tiles_n;
     switch (a.epi) {
-        case EPI_PARTIAL: return gemm_launch_t<EPI_PARTIAL, true>(d, s);
-        case EPI_SWIGLU: return gemm_launch_t<EPI_SWIGLU, true>(d, s);
+        case EPI_PARTIAL: return gemm_launch_t<EPI_PARTIAL, true>(d, grid, s);
+        case EPI_SWIGLU: return gemm_launch_t<EPI_SWIGLU, true>(d, grid, s);
     }
     return hipErrorInvalidValue;
 }

@@ -109,8 +109,12 @@ struct GemmArgs {
     void* y;            // [M, N] bf16 (EPI_STORE, EPI_SWIGLU) or float32 (EPI_PARTIAL)
     int M, N, K;
     int epi;
+    void* scratch;      // gemm_scratch_bytes(M, N, K, epi) bytes (ungrouped launches)
 };
 bool gemm_supported(int M, int N, int K, int epi);
+// Scratch an ungrouped launch needs: the float32 sums of the K ranges its
+// last, partly filled round of tiles is split into (0 when it is not split).
+size_t gemm_scratch_bytes(int M, int N, int K, int epi);
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t stream);
 
 // Grouped prefill projections of a mixture of experts: G independent GEMMs,
