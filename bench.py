@@ -29,6 +29,8 @@ partials):
                         2 x 2048 new tokens, the Mixtral-shaped MoE block at
                         16 decode tokens and at 4096 prefill tokens (each
                         expert over its routed tokens; TFLOP/s of routed flops).
+  tiny_mlp              the tiny float32 MLP block (hidden 256, t=2, 4 tokens),
+                        a correctness configuration; its time is launch-bound.
   hbm_read              the plain streaming-read rate alone.
 
 One step is one pass of that whole path; K steps are replayed from HIP graphs
@@ -73,7 +75,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="headline",
                     choices=["headline", "mlp_decode", "attn_proj", "mlp_prefill", "layer_decode", "attn_prefill",
-                             "layer_prefill", "moe_decode", "moe_prefill", "hbm_read"])
+                             "layer_prefill", "moe_decode", "moe_prefill", "tiny_mlp", "hbm_read"])
     ap.add_argument("--tokens", type=int, default=None, help="batch of the timed step (default: the workload's)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies the steps rotate over")
     ap.add_argument("--no-cpu", action="store_true")
@@ -115,7 +117,7 @@ def main():
     bench = {"headline": bench_headline, "hbm_read": bench_hbm_read, "mlp_decode": bench_mlp_decode, "attn_proj": bench_attn_proj, "mlp_prefill": bench_mlp_prefill,
              "layer_decode": bench_layer_decode, "attn_prefill": bench_attn_prefill,
              "layer_prefill": bench_layer_prefill, "moe_decode": bench_moe_decode,
-             "moe_prefill": bench_moe_prefill}[args.workload]
+             "moe_prefill": bench_moe_prefill, "tiny_mlp": bench_tiny_mlp}[args.workload]
     if args.calibrate_copy:
         calibrate_copy(torch)
     res = bench(ctx)
@@ -1179,6 +1181,75 @@ def bench_moe_decode(ctx):
                                "kind": "oracle",
                                "sample": f"{n} float64 passes (sharded oracle, numpy einsum on one thread) of rank 0's MoE shard (router + all {E} experts) over "
                                          f"{n_tok} of the {M} tokens, {el:.1f} s; scaled by 1/{t} for the {t} ranks"}
+    return res
+
+
+def bench_tiny_mlp(ctx):
+    """The tiny float32 MLP block (hidden 256, intermediate 1024, t=2, 4 tokens): a correctness
+    configuration whose time is launch-bound; reported for completeness."""
+    torch, tp, W, args = ctx.torch, ctx.tp, ctx.W, ctx.args
+    wl = W.WORKLOADS[1]
+    H, I, t = wl.hidden, wl.intermediate, wl.t
+    M = args.tokens or wl.tokens[0]
+    inp = W.mlp_inputs(1, H, I, M, "f32")
+    desc = tp.make_desc(H, I, bytes_per_elem=4)
+    plans = [tp.tp_shard_plan(desc, t, r) for r in range(t)]
+    ranks = []
+    for p in plans:
+        b, n = p.inter_begin, p.inter_cols
+        ranks.append({"w_gate": ctx.dev(ctx.phys(inp["w_gate"][:, b:b + n]), "f32"),
+                      "w_up": ctx.dev(ctx.phys(inp["w_up"][:, b:b + n]), "f32"),
+                      "w_down": ctx.dev(ctx.phys(inp["w_down"][b:b + n]), "f32")})
+    x = ctx.dev(inp["x"], "f32")
+    ws = tp.workspace(max(tp.tp_layer_workspace_bytes(desc, p, tp.TP_STAGE_MLP, M, tp.TP_F32) for p in plans))
+    parts = [torch.empty(M, H, device="cuda") for _ in range(t)]
+    out = torch.empty(M, H, device="cuda")
+
+    def step(i):
+        for r, p in enumerate(plans):
+            tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], x, parts[r], ws=ws)
+        tp.tp_partial_sum(parts, out)
+
+    def shard(i):
+        tp.tp_layer_shard_forward(desc, plans[i % t], tp.TP_STAGE_MLP, ranks[i % t], x, parts[i % t], ws=ws)
+
+    for i in range(8):
+        shard(i)
+    sh = event_time_ms(torch, shard, 64)
+    I_r = plans[0].inter_cols
+    rank_bytes = 3 * I_r * H * 4 + M * H * 4 + M * H * 4
+    total_ms = time_steps(ctx, step, 1)
+    ms_step = total_ms / args.steps
+    extra = {
+        "per_rank": {"shard_us": sh[0] * 1e3, "bytes": rank_bytes},
+        "roofline": roofline_hbm("gemv_kernel (float32 fma decode projections), both of one rank's MLP launches",
+                                 f"tiny_mlp_m{M}", rank_bytes, *sh),
+    }
+    config = {"workload": f"tiny float32 MLP block, all t={t} rank shards + on-device sum (launch-bound)",
+              "hidden": H, "intermediate": I, "t": t, "tokens": M}
+    res = result(ctx, M * args.steps / (total_ms * 1e-3), "tokens/s", ms_step, config, extra)
+    res["dtype"] = "f32"
+    if not args.no_cpu:
+        from oracle import layer as L
+        from oracle import plan as OP
+        od = OP.ModelDesc(hidden=H, intermediate=I)
+
+        def rank(r):
+            op = OP.rank_plan(od, t, r)
+            b, c = op["inter_begin"], op["inter_cols"]
+            return L.mlp_block(inp["x"], inp["w_gate"][:, b:b + c], inp["w_up"][:, b:b + c],
+                               inp["w_down"][b:b + c])["y"]
+
+        legs = time_legs(ctx, {"one_rank_shard": (lambda: rank(0), M),
+                               "all_ranks_and_sum": (lambda: sum(rank(r) for r in range(t)), M),
+                               "unsharded_block": (lambda: L.mlp_block(inp["x"], inp["w_gate"], inp["w_up"],
+                                                                       inp["w_down"])["y"], M)},
+                         "tokens_per_s", single_thread=("one_rank_shard", "all_ranks_and_sum"))
+        res["cpu_baseline"] = {"value": legs["all_ranks_and_sum"]["tokens_per_s"], "unit": "tokens/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"float64 oracle (BLAS products), the whole step of {M} tokens; legs also "
+                                         f"one rank and the unsharded block, and on one thread", "legs": legs,
+                               "host": host_info()}
     return res
 
 
