@@ -116,8 +116,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t key_block(const uint16_t* rows
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(rows + (size_t)key0 * d), (short)0,
                                              min(nvalid, PF_BK) * d * 2, 0x00020000);
 }
+// The transfer of 16 bytes per lane from the buffer at byte offset off into
+// LDS at lds_base + 16 lane. Written out rather than through the builtin:
+// the compiler orders every later LDS read behind a transfer into LDS it
+// knows of (it cannot tell that they read the other stage), which would keep
+// the next block's transfers from being issued ahead of this block's reads.
+// The kernel waits for them itself (s_waitcnt vmcnt(0) before the barrier
+// that hands the stage over).
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned off, uint16_t* lds_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+    const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
 }
 typedef short pf_s4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
@@ -133,13 +141,16 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
     constexpr int TOK = PF_ROWS / GQ;              // tokens per query block
     constexpr int KTILE = PF_BK * D;               // elements
     constexpr int VTILE = PF_BK * D;
-    constexpr int NV = DT * 8 + 4;                 // floats a lane publishes in the merge
+    constexpr int NV = DT * 8 + 4;                 // floats a lane publishes in the merge (NV / 4 float4)
     static_assert(KDMA >= 1, "blocks must split evenly over the threads");
-    static_assert(4 * NV * 64 * 4 <= 2 * (KTILE + VTILE) * 2, "merge area exceeds the tiles");
 
-    // Two stages, each a K tile then a V tile.
+    // Two stages, each a K tile then a V tile. The merge areas (four of NV
+    // floats per lane) start at the second stage, clear of the first, which
+    // meanwhile takes the next query block's first K and V block.
     constexpr int BUF = KTILE + VTILE;
-    __shared__ __align__(16) uint16_t smem[2 * BUF];
+    constexpr int MERGE_END = BUF + 4 * NV * 64 * 2;  // elements
+    __shared__ __align__(16) uint16_t smem[2 * BUF > MERGE_END ? 2 * BUF : MERGE_END];
+    static_assert(sizeof(smem) <= 160 * 1024, "LDS of one compute unit");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
@@ -210,28 +221,45 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
         const int cc = dt * 2 + (tr_q >> 1);
         vto[dt] = tr_key * D + v_chunk<D>(tr_key, cc) * 8 + (tr_q & 1) * 4;
     }
-    // Query blocks pair and nqb - 1 - pair (once when they coincide).
+    // The query fragments of this lane's two rows of query block qb (one row
+    // per MFMA column tile): token qb TOK + r / GQ, head g GQ + r % GQ.
+    uint4 qf[2][DS];
+    auto load_q = [&](int qb) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int r = rg * 32 + rt * 16 + col;
+            const int tk = min(qb * TOK + r / GQ, S - 1);
+            const int hq = g * GQ + r % GQ;
+            const uint16_t* qrow = qbase + ((size_t)b * S + tk) * a.q_stride + (size_t)hq * D;
+#pragma unroll
+            for (int s = 0; s < DS; ++s) qf[rt][s] = load_u4(qrow + s * 32 + kg * 8);
+        }
+    };
+    // Query blocks pair and nqb - 1 - pair (once when they coincide). The
+    // first walks its key blocks backwards and so ends on block 0 (in stage
+    // 0), which the second walks first, forwards: only the second block's
+    // query fragments are requested between them, during the first one's
+    // merge, which works above stage 0. Block kb always sits in stage kb % 2.
+    int qblk = pair;
+    {
+        const int nblk0 = (p0 + min(qblk * TOK + TOK, S) - 1) / PF_BK + 1;
+        load_q(qblk);
+        load_k(nblk0 - 1, smem + ((nblk0 - 1) & 1) * BUF);
+        load_v(nblk0 - 1, smem + ((nblk0 - 1) & 1) * BUF + KTILE);
+    }
     for (int ph = 0; ph < 2; ++ph) {
-        const int qblk = ph == 0 ? pair : nqb - 1 - pair;
-        if (ph == 1 && qblk == pair) break;
         const int i0 = qblk * TOK;                  // first token of the query block
         const int ilast = min(i0 + TOK, S) - 1;
         const int nblk = (p0 + ilast) / PF_BK + 1;  // blocks up to the last token's position
         const int nfull = (p0 + i0 + 1) / PF_BK;    // blocks every row sees whole
         const int plast = p0 + ilast;
 
-        // This lane's two query rows (one per column tile): token and head.
+        // This lane's two query rows: token and position.
         int tok[2], pos[2];
-        uint4 qf[2][DS];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            const int r = rg * 32 + rt * 16 + col;
-            tok[rt] = i0 + r / GQ;
+            tok[rt] = i0 + (rg * 32 + rt * 16 + col) / GQ;
             pos[rt] = p0 + tok[rt];
-            const int hq = g * GQ + r % GQ;
-            const uint16_t* qrow = qbase + ((size_t)b * S + min(tok[rt], S - 1)) * a.q_stride + (size_t)hq * D;
-#pragma unroll
-            for (int s = 0; s < DS; ++s) qf[rt][s] = load_u4(qrow + s * 32 + kg * 8);
         }
 
         float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
@@ -250,10 +278,9 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) ot[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        load_k(0, smem);
-        load_v(0, smem + KTILE);
         // Every load issued so far (the query fragments included) has landed,
-        // so the waits inside the loop only ever cover the next block's loads.
+        // so the waits inside the loop only ever cover the next block's loads;
+        // past this barrier every wave has also left the last merge.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
 
@@ -363,67 +390,84 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
             }
         };
 
-        // One block for the workgroup. The next block's K and V go by DMA into
-        // the other stage once this block's LDS reads are issued (a transfer
-        // into LDS ahead of them would make the compiler wait for it before
-        // reading).
-        auto step = [&](int kb, bool masked) {
+        // One block for the workgroup; kn is the block that follows it (-1:
+        // none). The next block's K and V go by DMA into the other stage
+        // first thing, so that they have the whole block to land: every read
+        // of that stage ended before the last barrier.
+        auto step = [&](int kb, int kn, bool masked) {
             const int buf = kb & 1;
-            const bool more = kb + 1 < nblk;
+            const bool more = kn >= 0;
             uint16_t* cur = smem + buf * BUF;
             uint16_t* nxt = smem + (buf ^ 1) * BUF;
+            if (more) {
+                load_k(kn, nxt);
+                load_v(kn, nxt + KTILE);
+            }
             // a quarter wholly past the last token's position holds no visible key
             const bool active = !masked || kb * PF_BK + kq * PF_KW <= plast;
             if (active) front(cur, cur + KTILE);
-            if (more) {
-                load_k(kb + 1, nxt);
-                load_v(kb + 1, nxt + KTILE);
-            }
             if (active) back(kb, masked);
             if (more) __builtin_amdgcn_s_waitcnt(0);  // the K and V transfers have landed in LDS
             __syncthreads();
         };
-        // Blocks every row sees whole, then the diagonal ones, in two loops so
-        // that each has a single body.
-        int kb = 0;
-        for (; kb < nfull; ++kb) step(kb, false);
-        for (; kb < nblk; ++kb) step(kb, true);
+        // Blocks every row sees whole and the diagonal ones in loops of their
+        // own, so that each has a single body: the first query block from its
+        // last block down to block 0, the second from block 0 up.
+        if (ph == 0) {
+            int kb = nblk - 1;
+            for (; kb >= nfull; --kb) step(kb, kb - 1, true);
+            for (; kb >= 0; --kb) step(kb, kb - 1, false);
+        } else {
+            int kb = 0;
+            for (; kb < nfull; ++kb) step(kb, kb + 1 < nblk ? kb + 1 : -1, false);
+            for (; kb < nblk; ++kb) step(kb, kb + 1 < nblk ? kb + 1 : -1, true);
+        }
         if (MSUM) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) lrun[rt] = lacc[rt][0];
         }
 
-        // Merge the key quarters by their log-sum-exp weights, in two rounds
-        // through the idle tiles: quarters 2, 3 into 0, 1, then 1 into 0.
-        // Layout [value][lane]: lane-contiguous.
+        // The next query block's fragments, under this block's merge; its
+        // first K and V block is block 0, still in stage 0.
+        const int qnext = nqb - 1 - pair;
+        const bool next = ph == 0 && qnext != pair;
+        if (next) load_q(qnext);
+
+        // Merge the key quarters by their log-sum-exp weights, in two rounds:
+        // quarters 2, 3 into 0, 1, then 1 into 0. Layout [float4][lane]:
+        // (m, l) of both rows first, then the outputs by (d tile, row tile).
         auto publish = [&](float* mg) {
+            float4* m4 = reinterpret_cast<float4*>(mg);
+            m4[lane] = make_float4(mrun[0], lrun[0], mrun[1], lrun[1]);
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                mg[(2 * rt) * 64 + lane] = mrun[rt];
-                mg[(2 * rt + 1) * 64 + lane] = lrun[rt];
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) mg[(4 + (dt * 2 + rt) * 4 + j) * 64 + lane] = ot[dt][rt][j];
-            }
+                for (int rt = 0; rt < 2; ++rt)
+                    m4[(1 + dt * 2 + rt) * 64 + lane] =
+                        make_float4(ot[dt][rt][0], ot[dt][rt][1], ot[dt][rt][2], ot[dt][rt][3]);
         };
         auto combine = [&](const float* mg) {
+            const float4* m4 = reinterpret_cast<const float4*>(mg);
+            const float4 ml = m4[lane];
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                const float mb = mg[(2 * rt) * 64 + lane], lb = mg[(2 * rt + 1) * 64 + lane];
+                const float mb = rt ? ml.z : ml.x, lb = rt ? ml.w : ml.y;
                 const float m = fmaxf(mrun[rt], mb);
                 const float mr = m == -INFINITY ? 0.f : m;      // both halves empty: stay empty
                 const float wa = __builtin_amdgcn_exp2f(mrun[rt] - mr), wb = __builtin_amdgcn_exp2f(mb - mr);
                 mrun[rt] = m;
                 lrun[rt] = lrun[rt] * wa + lb * wb;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        ot[dt][rt][j] = ot[dt][rt][j] * wa + mg[(4 + (dt * 2 + rt) * 4 + j) * 64 + lane] * wb;
+                for (int dt = 0; dt < DT; ++dt) {
+                    const float4 o = m4[(1 + dt * 2 + rt) * 64 + lane];
+                    ot[dt][rt][0] = ot[dt][rt][0] * wa + o.x * wb;
+                    ot[dt][rt][1] = ot[dt][rt][1] * wa + o.y * wb;
+                    ot[dt][rt][2] = ot[dt][rt][2] * wa + o.z * wb;
+                    ot[dt][rt][3] = ot[dt][rt][3] * wa + o.w * wb;
+                }
             }
         };
-        auto region = [&](int i) -> float* { return reinterpret_cast<float*>(smem) + i * NV * 64; };
+        auto region = [&](int i) -> float* { return reinterpret_cast<float*>(smem + BUF) + i * NV * 64; };
         if (kq >= 2) publish(region(rg * 2 + (kq - 2)));
         __syncthreads();
         if (kq < 2) combine(region(rg * 2 + kq));
@@ -446,7 +490,8 @@ __global__ __launch_bounds__(PF_NT, 1) void attn_prefill_kernel(PrefillArgs a) {
                                    pack_bf16x2(ot[dt][rt][2] * inv, ot[dt][rt][3] * inv));
             }
         }
-        __syncthreads();                            // the next query block reuses the tiles
+        if (!next) break;
+        qblk = qnext;
     }
 }
 

@@ -612,6 +612,7 @@ PREFILL_CASES = [
     (1, 4, 4, 128, 64, 64, 64),        # GQ 1 with several kv heads, one key block
     (2, 8, 1, 128, 2048, 2048, 2048),  # 70B t=8 head shard at batch 2 x 2048 tokens
     (1, 8, 1, 128, 1000, 128, 640),    # whole key blocks only, cache longer than kv_len
+    (1, 16, 1, 64, 128, 5, 128),       # one-token query block ending on a key-block boundary
 ]
 
 
