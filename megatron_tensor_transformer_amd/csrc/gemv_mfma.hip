@@ -17,7 +17,9 @@
 //    DMA into the wave's own LDS tiles (4 rows x 256 bytes per transfer),
 //    activation operands are read straight from memory, and the waves meet
 //    only when their sums are added at the end: no workgroup barrier while
-//    streaming, no second kernel, no float32 slices in memory.
+//    streaming. Where K is also split over workgroups (narrow outputs), each
+//    publishes its float32 slice with coherent stores and the last of them
+//    to arrive adds the slices and runs the epilogue: no second kernel.
 //  - Narrow projections and the stacked experts (gemv_mfma_kernel): waves
 //    own 16 rows each and share a K range, walked in stages of 256 elements
 //    with two stages of loads in flight; weights are read as 2 rows x 512
@@ -52,6 +54,44 @@ constexpr int SK_MAX_STAGES = 8;               // K chunk of at most 2048
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
                                                    c, 0, 0, 0);
+}
+
+// K split over workgroups: every split publishes its tile's sums res[m][RPT]
+// (and, with a fused RMSNorm, its squared-sum slice ssl[m]) with coherent
+// stores, and the last of the tile's splits to arrive adds the slices in
+// split order (deterministic) into res and ssl. Returns true in that
+// workgroup, which then runs the epilogue; the others return. A thread's
+// loads of its element's slices are in flight together.
+template <int RPT, bool NORM, int NT>
+__device__ __forceinline__ bool split_merge(const GemvDev& d, float* res, float* ssl, int tile_id, int split,
+                                            int mvalid, int* s_last) {
+    const int tid = threadIdx.x, S = d.splits;
+    float* base = d.part + (size_t)tile_id * S * (SK_MT * RPT);
+    float* sqb = d.ssq + (size_t)tile_id * S * SK_MT;
+    const int live = mvalid * RPT;              // token rows past m are never read back
+    for (int e = tid; e < live; e += NT) store_coherent(base + (size_t)split * (SK_MT * RPT) + e, res[e]);
+    if (NORM && tid < mvalid) store_coherent(sqb + (size_t)split * SK_MT + tid, ssl[tid]);
+    if (!last_arriver(&d.cnt[tile_id], (unsigned)S, s_last)) return false;
+    constexpr int UNR = 4;
+    for (int e = tid; e < live; e += NT) {
+        float v = 0.f;
+        for (int sp0 = 0; sp0 < S; sp0 += UNR) {
+            float u[UNR];
+#pragma unroll
+            for (int i = 0; i < UNR; ++i) u[i] = load_coherent(base + (size_t)min(sp0 + i, S - 1) * (SK_MT * RPT) + e);
+#pragma unroll
+            for (int i = 0; i < UNR; ++i)
+                if (sp0 + i < S) v += u[i];
+        }
+        res[e] = v;
+    }
+    if (NORM && tid < mvalid) {
+        float v = 0.f;
+        for (int sp = 0; sp < S; ++sp) v += load_coherent(sqb + (size_t)sp * SK_MT + tid);
+        ssl[tid] = v;
+    }
+    __syncthreads();
+    return true;
 }
 
 // NST: stages per K range (a K range is NST * 256 elements). RG: waves that
@@ -197,7 +237,9 @@ __global__ __launch_bounds__(RG * KS * 64) void gemv_mfma_kernel(GemvDev d) {
     if (KS == 1 && d.splits > 1) {
         if (NORM) __syncthreads();             // ssl written by the stagers
         // This split's slice goes out with plain stores; the merge kernel that
-        // follows on the stream adds the slices and runs the epilogue.
+        // follows on the stream adds the slices and runs the epilogue (an
+        // in-kernel merge by the last split to arrive measured slower here:
+        // 70B attention projections at t=4, 89.2 -> 93.2 us per step).
         const int tile_id = blockIdx.z * d.n_tiles + tile;
         float* mine = d.part + ((size_t)tile_id * d.splits + split) * (SK_MT * RPT);
 #pragma unroll
@@ -433,15 +475,9 @@ __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
     }
     __syncthreads();
     if (d.splits > 1) {
-        // K split over workgroups: this split's slice goes out with plain
-        // stores; the merge kernel that follows adds the slices in split
-        // order and runs the epilogue.
-        const int tile_id = blockIdx.z * d.n_tiles + tile;
-        const size_t sl = (size_t)tile_id * d.splits + blockIdx.y;
-        float* mine = d.part + sl * (SK_MT * ROWS);
-        for (int e = tid; e < mvalid * ROWS; e += NT) mine[e] = res[e];
-        if (NORM && tid < mvalid) d.ssq[sl * SK_MT + tid] = ssl[0][tid];
-        return;
+        __shared__ int s_last;
+        if (!split_merge<ROWS, NORM, NT>(d, res, ssl[0], blockIdx.z * d.n_tiles + tile, blockIdx.y, mvalid, &s_last))
+            return;
     }
     gemv_epilogue<uint16_t, SK_MT, ROWS, EPI, NORM, NT>(a, res, ssl[0], tile, m0, mvalid, opt);
 }
@@ -453,8 +489,7 @@ template <int EPI, bool NORM, int RPT>
 __global__ __launch_bounds__(256) void gemv_mfma_merge_kernel(GemvDev d) {
     // The plan splits K about four ways, so one batch of loads usually
     // covers every slice; the squared-sum slices of a fused RMSNorm travel in
-    // the same batch. RPT: rows of a slice (64 from the narrow kernel, 32
-    // from the wide kernel split over workgroups).
+    // the same batch. RPT: rows of a slice (64, the narrow kernel's tile).
     constexpr int NT = 256, PER = SK_MT * RPT / NT, UNR = 4;
     __shared__ float res[SK_MT * RPT];
     __shared__ float ssl[SK_MT];
@@ -501,7 +536,7 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
     p.mfma = 1;
     p.mt = SK_MT;
     p.mblocks = (m + SK_MT - 1) / SK_MT;
-    p.mb_per_launch = p.mblocks;                // the merge uses no counters
+    p.mb_per_launch = p.mblocks;                // capped below where split workgroups count arrivals
     p.lds_bytes = 0;                            // static LDS only
     const bool swi = epi == EPI_SWIGLU;
     const int64_t mb = p.mblocks;
@@ -567,7 +602,8 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
     // filling and draining; 8-wave workgroups of 16 to 32 rows stream longer
     // K ranges: K split S ways (2 to 16), the fewest splits whose tiles,
     // sized to about 256 workgroups, hold at least WIDE_MIN_ROWS rows and
-    // leave no split without K to cover; the merge kernel adds the slices.
+    // leave no split without K to cover; the last split to finish a tile
+    // adds its slices (a counter per tile and m-block in the header).
     // The 70B QKV shard at t=8 (1280 rows, K 8192): 4 splits of 20-row
     // tiles, 557 -> 546 us per layer step; at t=4 (chunk 2048) two splits
     // of 20-row tiles measured 1 us per step slower, so it stays here.
@@ -590,6 +626,9 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
             p.n_tiles = (N + p.out_per_tile - 1) / p.out_per_tile;
             p.kc = kc2;
             p.splits = S2;
+            // one counter per (tile, m-block) of a launch
+            if ((int64_t)p.n_tiles * p.mb_per_launch > WS_MAX_COUNTERS)
+                p.mb_per_launch = std::max(1, WS_MAX_COUNTERS / p.n_tiles);
             const size_t tl = (size_t)p.n_tiles * p.mb_per_launch;
             p.ws_bytes = (tl * S2 * SK_MT * 32 * 4 + 255) / 256 * 256 + (tl * S2 * SK_MT * 4 + 255) / 256 * 256;
             return p;
@@ -609,7 +648,7 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
 
 GemvPlan gemv_plan_mfma(int m, int K, int N, int epi) {
     GemvPlan p = plan_mfma(m, K, N, epi);
-    p.tiles_per_launch = p.n_tiles;             // slices are indexed by tile; no counters
+    p.tiles_per_launch = p.n_tiles;             // slices and counters are indexed by tile and m-block
     return p;
 }
 
@@ -625,9 +664,8 @@ static hipError_t mfma_launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t
             hipLaunchKernelGGL((gemv_mfma_kernel<EPI, NORM, NST, RG, KS>), grid, dim3(RG * KS * 64), 0, s, dl);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (p.splits > 1) {
-            constexpr int SR = RG * KS == WD_NW ? 16 * RG : SK_RPT;     // rows of a slice
-            hipLaunchKernelGGL((gemv_mfma_merge_kernel<EPI, NORM, SR>), dim3(p.n_tiles, 1, grid.z), dim3(256), 0, s, dl);
+        if (RG * KS != WD_NW && p.splits > 1) {  // the wide kernel merges its splits itself
+            hipLaunchKernelGGL((gemv_mfma_merge_kernel<EPI, NORM, SK_RPT>), dim3(p.n_tiles, 1, grid.z), dim3(256), 0, s, dl);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

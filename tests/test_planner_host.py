@@ -1,9 +1,12 @@
 """The library's launch planners, queried on the host through a small C++ probe
 (tests/plan_probe.cpp, linked against libtpshard.so; no GPU call is made).
 
-- Split-K decode projections on the v_dot2 kernel keep one completion counter
-  per (row tile, m-block) of a launch: a launch must never use more counters
-  than the workspace header holds, however many row tiles the output has.
+- Split-K decode projections that merge in-kernel (the v_dot2 kernel, and the
+  8-wave matrix-core kernel when it splits K over workgroups) keep one
+  completion counter per (row tile, m-block) of a launch: a launch must never
+  use more counters than the workspace header holds, however many row tiles
+  the output has or however many tokens the batch has. (The 4-wave
+  matrix-core kernel's splits go to a merge kernel and use no counters.)
 - The decode attention's split-KV scratch depends on kv_len in a way that is
   not monotone, so the layer workspace sizes it by a bound over every kv_len up
   to the cache capacity; the bound must cover each kv_len.
@@ -44,21 +47,26 @@ def test_split_k_counters_fit_the_header(probe):
     queries = []
     for bf in (0, 1):
         for epi in ((0, 1, 2, 3) if bf else (0, 1, 2)):
-            for m in (1, 2, 3, 4, 5, 8, 16):
-                for K in (256, 4096, 8192, 8200, 17000):
-                    for N in (8, 1000, 70000, 128256, 150000):
+            for m in (1, 2, 3, 4, 5, 8, 16, 20, 40, 64):
+                for K in (256, 1024, 4096, 8192, 8200, 17000):
+                    for N in (8, 1000, 1280, 70000, 128256, 150000, 600000):
                         queries.append((m, K, N, bf, epi))
     plans = probe([f"gemv {m} {K} {N} {bf} {epi}" for m, K, N, bf, epi in queries])
-    big = 0
+    big = mfma_split = 0
     for q, p in zip(queries, plans):
         assert 1 <= p["tiles_per_launch"] <= p["n_tiles"], (q, p)
-        if p["splits"] > 1 and not p["mfma"]:
+        assert 1 <= p["mb_per_launch"] <= p["mblocks"], (q, p)
+        counted = p["splits"] > 1 and (not p["mfma"] or p["waves"] == 8)
+        if counted:
             assert p["tiles_per_launch"] * p["mb_per_launch"] <= p["header_counters"], (q, p)
+            mfma_split += p["mfma"]
+        if p["splits"] > 1:
             # the scratch holds every slice of one launch
             assert p["ws_bytes"] >= p["tiles_per_launch"] * p["mb_per_launch"] * p["splits"] * p["mt"] * \
                 p["rows_per_tile"] * 4, (q, p)
             big += p["n_tiles"] > p["header_counters"]
     assert big > 0      # the sweep reaches outputs with more row tiles than counters
+    assert mfma_split > 0   # and matrix-core plans that split K
 
 
 @pytest.mark.parametrize("batch,q_heads,kv_heads,head_dim,capacity", [
