@@ -232,30 +232,89 @@ def projection_kernel(m, dtype="bf16", wide=False):
     return "gemv_kernel (v_dot2 decode projection)"
 
 
-def code_digest():
-    """Digest of the library's device code (the .hip_fatbin section of libtpshard.so): hardware-counter
-    figures are only reported while the kernels they were taken on are the ones loaded."""
+_KERNEL_DIGESTS = None
+
+
+def kernel_digests():
+    """Digest of each kernel's machine code in libtpshard.so, by kernel symbol: the gfx950 code objects
+    in the .hip_fatbin section (clang offload bundles), each kernel's function bytes and its kernel
+    descriptor (register, LDS and launch settings) without the descriptor's position-dependent code
+    offset. A kernel keeps its digest while its own code is unchanged, whatever else is rebuilt."""
+    global _KERNEL_DIGESTS
+    if _KERNEL_DIGESTS is not None:
+        return _KERNEL_DIGESTS
     import struct
+
+    def sections(b):
+        shoff = struct.unpack_from("<Q", b, 0x28)[0]
+        shentsize, shnum, shstrndx = struct.unpack_from("<HHH", b, 0x3A)
+        return [struct.unpack_from("<IIQQQQIIQQ", b, shoff + i * shentsize) for i in range(shnum)], shstrndx
+
+    def cstr(b, at):
+        return b[at:b.index(b"\0", at)]
+
+    def code_object(co, out):
+        secs, _ = sections(co)
+        tabs = [x for x in secs if x[1] == 2]              # SHT_SYMTAB
+        if not tabs:
+            return
+        st = tabs[0]
+        strtab = secs[st[6]]
+        funcs, descs = {}, {}
+        for j in range(st[5] // 24):
+            nm, info, _other, shndx, value, size = struct.unpack_from("<IBBHQQ", co, st[4] + j * 24)
+            if shndx == 0 or shndx >= len(secs) or size == 0:
+                continue
+            name = cstr(co, strtab[4] + nm).decode()
+            at = secs[shndx][4] + (value - secs[shndx][3])
+            body = co[at:at + size]
+            if info & 0xF == 2:                                 # STT_FUNC
+                funcs[name] = body
+            elif name.endswith(".kd") and size == 64:
+                descs[name[:-3]] = body[:16] + b"\0" * 8 + body[24:]
+        for name, body in funcs.items():
+            out[name] = hashlib.sha256(body + descs.get(name, b"")).hexdigest()[:16]
+
     path = os.path.join(ROOT, "megatron_tensor_transformer_amd", "libtpshard.so")
     with open(path, "rb") as f:
         data = f.read()
-    shoff = struct.unpack_from("<Q", data, 0x28)[0]
-    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
-    secs = [struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize) for i in range(shnum)]
-    names = secs[shstrndx][4]
-    for name, _typ, _flags, _addr, off, size in secs:
-        if data[names + name:data.index(b"\0", names + name)] == b".hip_fatbin":
-            return hashlib.sha256(data[off:off + size]).hexdigest()[:16]
-    return None
+    secs, shstrndx = sections(data)
+    out = {}
+    for name, _t, _f, _a, off, size, *_ in secs:
+        if cstr(data, secs[shstrndx][4] + name) != b".hip_fatbin":
+            continue
+        fb = data[off:off + size]
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        i = fb.find(magic)
+        while i >= 0:
+            p = i + len(magic) + 8
+            for _ in range(struct.unpack_from("<Q", fb, i + len(magic))[0]):
+                eoff, esz, tsz = struct.unpack_from("<QQQ", fb, p)
+                triple = fb[p + 24:p + 24 + tsz].decode()
+                p += 24 + tsz
+                if triple.endswith("gfx950") and esz:
+                    code_object(fb[i + eoff:i + eoff + esz], out)
+            i = fb.find(magic, i + 1)
+    _KERNEL_DIGESTS = out
+    return out
+
+
+def code_digest(symbols):
+    """One digest over the listed kernels' digests, or None if one is not in the library."""
+    dig = kernel_digests()
+    if not symbols or any(s not in dig for s in symbols):
+        return None
+    return hashlib.sha256(",".join(dig[s] for s in symbols).encode()).hexdigest()[:16]
 
 
 def counted_traffic(kernel_key):
     """HBM bytes per launch of a kernel from the committed counter summary, or None.
 
     The summary holds, per (kernel, workload) key, FETCH_SIZE and WRITE_SIZE
-    in KiB per dispatch from two counter runs, and the same counters for the
-    plain copy of known size that scales them to bytes. Figures taken for
-    other kernel sources are not used."""
+    in KiB per dispatch from two counter runs, the kernels they cover (by
+    symbol) with a digest of their machine code, and the same counters for the
+    plain copy of known size that scales them to bytes. Figures taken on other
+    code than the kernels loaded now are not used."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -266,7 +325,8 @@ def counted_traffic(kernel_key):
                 continue
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("code_digest") != code_digest():
+    code = vals.get(f"{kernel_key}.code")
+    if code is None or code != code_digest(vals.get(f"{kernel_key}.kernels", "").split()):
         return None
     try:
         fetch_scale = COPY_BYTES / (float(vals["copy.FETCH_SIZE_KiB"]) * 1024.0)
