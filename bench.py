@@ -187,6 +187,60 @@ def time_steps(ctx, step, n_graphs):
     return e0.elapsed_time(e1)
 
 
+class Marks:
+    """HIP event pairs around the calls of a timed region's dominant kernels, by name, on torch's
+    current stream (the stream the binding passes to every entry point)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def around(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        self.pairs.setdefault(name, []).append((e0, e1))
+
+    def stats(self, name):
+        """(mean, median, min) ms per call over every marked call (after a synchronize)."""
+        ms = [a.elapsed_time(b) for a, b in self.pairs[name]]
+        return float(np.mean(ms)), float(np.median(ms)), float(np.min(ms)), len(ms)
+
+
+def marked(mk, name, fn):
+    if mk is None:
+        fn()
+    else:
+        mk.around(name, fn)
+
+
+def time_steps_eager(ctx, step):
+    """Warm up eagerly, then time ``steps`` eager steps between two HIP events; ``step(i, marks)``
+    records event pairs around its dominant calls, so their durations come from the timed region
+    itself. For steps of milliseconds (the GEMM-bound prefill workloads), where launching from the host
+    costs nothing against the kernels; steps of short kernels stay graph-replayed (time_steps). (Event
+    nodes inside a captured graph, which would serve both, are refused by torch on ROCm.) Returns
+    (total ms, Marks)."""
+    torch, args = ctx.torch, ctx.args
+    log(f"[bench] warmup {args.warmup} eager steps")
+    for i in range(max(args.warmup, 1)):
+        step(i, None)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} eager steps")
+    marks = Marks(torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_hold(torch)
+    e0.record()
+    for i in range(args.steps):
+        step(i, marks)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), marks
+
+
 def event_time_ms(torch, fn, n, reps=5):
     """Average ms per call of fn: n calls launched back to back between two HIP
     events on the stream they run on (torch's current stream, which the
@@ -647,29 +701,22 @@ def prefill_mlp_gpu(ctx):
     out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
     a_out = torch.empty(M, I_r, dtype=torch.bfloat16, device="cuda")
 
-    def step(i):
-        for r, p in enumerate(plans):
-            tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], x, parts[r], ws=ws)
+    # A rank's MLP block: the gate/up + SwiGLU GEMM and the down GEMM (the MLP stage's two library
+    # calls), each rank in turn, then the sum of the partials. The GEMMs are timed inside the timed
+    # steps themselves.
+    def step(i, mk=None):
+        for r in range(t):
+            rw = ranks[r]
+            marked(mk, "gateup", lambda: tp.tp_column_linear(x, rw["w_gate"], a_out, w_up=rw["w_up"], ws=ws))
+            marked(mk, "down", lambda: tp.tp_row_linear_partial(a_out, rw["w_down"], parts[r], ws=ws))
         tp.tp_partial_sum(parts, out)
 
-    def gateup(i):
-        rw = ranks[i % t]
-        tp.tp_column_linear(x, rw["w_gate"], a_out, w_up=rw["w_up"], ws=ws)
-
-    def down(i):
-        rw = ranks[i % t]
-        tp.tp_row_linear_partial(a_out, rw["w_down"], parts[i % t], ws=ws)
-
-    for i in range(4):
-        gateup(i)
-        down(i)
-    g_t = event_time_ms(torch, gateup, 8, reps=3)
-    d_t = event_time_ms(torch, down, 8, reps=3)
+    total_ms, mk = time_steps_eager(ctx, step)
+    ms_step = total_ms / args.steps
+    g_t, d_t = mk.stats("gateup"), mk.stats("down")
     g_fl, d_fl = 2.0 * M * H * 2 * I_r, 2.0 * M * I_r * H
     log(f"[bench] gate/up {g_t[0] * 1e3:.1f} us ({g_fl / (g_t[0] * 1e-3) / 1e12:.0f} TFLOP/s), "
-        f"down {d_t[0] * 1e3:.1f} us ({d_fl / (d_t[0] * 1e-3) / 1e12:.0f} TFLOP/s)")
-    total_ms = time_steps(ctx, step, 1)
-    ms_step = total_ms / args.steps
+        f"down {d_t[0] * 1e3:.1f} us ({d_fl / (d_t[0] * 1e-3) / 1e12:.0f} TFLOP/s), over {g_t[3]} calls each")
     step_flops = t * (g_fl + d_fl)
     tflops = step_flops * args.steps / (total_ms * 1e-3) / 1e12
     g_tf = g_fl / (g_t[0] * 1e-3) / 1e12
@@ -680,10 +727,12 @@ def prefill_mlp_gpu(ctx):
         "step_flops": step_flops,
         "per_rank": {"gateup_us": g_t[0] * 1e3, "gateup_TFLOPs": g_tf, "down_us": d_t[0] * 1e3,
                      "down_TFLOPs": d_fl / (d_t[0] * 1e-3) / 1e12, "flops": g_fl + d_fl},
-        "roofline": {"kernel": projection_kernel(M) + ": gate/up + SwiGLU, one rank shard", "bound": "mfma",
+        "roofline": {"kernel": projection_kernel(M) + ": gate/up + SwiGLU, one rank shard (one library call: "
+                               "the GEMM and the tail of its last round)", "bound": "mfma",
                      "achieved": g_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": g_tf / BF16_PEAK_TFLOPS,
                      "traffic": counted_traffic(f"gateup_mlp_prefill_m{M}"), "flops_per_launch": g_fl,
-                     "us_mean": g_t[0] * 1e3, "us_median": g_t[1] * 1e3, "us_min": g_t[2] * 1e3},
+                     "us_mean": g_t[0] * 1e3, "us_median": g_t[1] * 1e3, "us_min": g_t[2] * 1e3,
+                     "timed": f"every gate/up call of the {args.steps} timed steps ({g_t[3]} calls)"},
     }
     config = {"workload": f"70B-shaped MLP prefill block, all t={t} rank shards + on-device sum of partials",
               "hidden": H, "intermediate": I, "t": t, "tokens": M}
@@ -1013,6 +1062,9 @@ def bench_attn_prefill(ctx):
                       "o": torch.empty(B, S_, qn * d, dtype=torch.bfloat16, device="cuda")})
     p0 = plans[0]
 
+    # A step is the t ranks' attention calls back to back, replayed from a graph (the calls are too
+    # short for eager launches to keep up); every call of the timed region is the dominant kernel, so
+    # its average duration is the timed region's time over its calls.
     def step(i):
         for r, p in enumerate(plans):
             rw = ranks[r]
@@ -1022,14 +1074,15 @@ def bench_attn_prefill(ctx):
         rw = ranks[i % t]
         tp.tp_prefill_attention(rw["q"], rw["k"], rw["v"], rw["o"], kv_len, p0.q_heads)
 
-    for i in range(2 * t):
-        one(i)
-    at = event_time_ms(torch, one, 4 * t)
-    fl = causal_flops(B, S_, kv_len, p0.q_heads, d)
-    tf = fl / (at[0] * 1e-3) / 1e12
-    log(f"[bench] prefill attention {at[0] * 1e3:.1f} us ({tf:.0f} TFLOP/s)")
     total_ms = time_steps(ctx, step, 1)
     ms_step = total_ms / args.steps
+    n_calls = args.steps * t
+    bb = event_time_ms(torch, one, 4 * t)           # back to back, outside the timed region: for reference
+    at = (total_ms / n_calls, total_ms / n_calls, total_ms / n_calls, n_calls)
+    fl = causal_flops(B, S_, kv_len, p0.q_heads, d)
+    tf = fl / (at[0] * 1e-3) / 1e12
+    log(f"[bench] prefill attention {at[0] * 1e3:.1f} us ({tf:.0f} TFLOP/s) per call in the timed steps, "
+        f"{bb[0] * 1e3:.1f} us back to back")
     tflops = t * fl * args.steps / (total_ms * 1e-3) / 1e12
     extra = {
         "tokens_per_s": M * args.steps / (total_ms * 1e-3),
@@ -1038,8 +1091,10 @@ def bench_attn_prefill(ctx):
         "roofline": {"kernel": "attn_prefill_kernel (causal GQA prefill attention, one rank shard)",
                      "bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / BF16_PEAK_TFLOPS, "traffic": counted_traffic(f"prefill_attention_m{M}"),
-                     "flops_per_launch": fl, "us_mean": at[0] * 1e3, "us_median": at[1] * 1e3,
-                     "us_min": at[2] * 1e3},
+                     "flops_per_launch": fl, "us_mean": at[0] * 1e3,
+                     "timed": f"the timed region's {args.steps} graph-replayed steps over their {n_calls} calls "
+                              f"(every call is this kernel; gaps between calls included)",
+                     "us_back_to_back": bb[0] * 1e3},
     }
     config = {"workload": f"70B-shaped causal prefill attention, all t={t} rank shards (each {p0.q_heads} q heads "
                           f"on {p0.kv_heads} kv head)", "q_heads": nq, "kv_heads": nkv, "head_dim": d, "t": t,
@@ -1102,30 +1157,29 @@ def bench_layer_prefill(ctx):
     out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
     p0 = plans[0]
     a_out = torch.empty(M, p0.inter_cols, dtype=torch.bfloat16, device="cuda")
-    hn = torch.empty(M, H, dtype=torch.bfloat16, device="cuda").normal_()
 
-    def step(i):
+    # The attention stage of every rank, the sum, then every rank's MLP block as the MLP stage's two
+    # library calls (RMSNorm + gate/up + SwiGLU, then down), so the gate/up call is timed inside the
+    # timed steps; then the second sum.
+    def step(i, mk=None):
         for r, p in enumerate(plans):
             rw = ranks[r]
             tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_ATTN, rw, x, parts[r],
                                       kv={"k": rw["k"], "v": rw["v"], "kv_len": kv_len, "new_tokens": S_}, ws=ws)
         tp.tp_partial_sum(parts, h, residual=x)
-        for r, p in enumerate(plans):
-            tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, ranks[r], h, parts[r], ws=ws)
+        for r in range(t):
+            rw = ranks[r]
+            marked(mk, "gateup", lambda: tp.tp_column_linear(h, rw["w_gate"], a_out, w_up=rw["w_up"],
+                                                             gamma=rw["mlp_norm"], eps=wl.eps, ws=ws))
+            tp.tp_row_linear_partial(a_out, rw["w_down"], parts[r], ws=ws)
         tp.tp_partial_sum(parts, out, residual=h)
 
-    def gateup(i):
-        rw = ranks[i % t]
-        tp.tp_column_linear(hn, rw["w_gate"], a_out, w_up=rw["w_up"], ws=ws)
-
-    for i in range(2 * t):
-        gateup(i)
-    g_t = event_time_ms(torch, gateup, 2 * t, reps=3)
+    total_ms, mk = time_steps_eager(ctx, step)
+    ms_step = total_ms / args.steps
+    g_t = mk.stats("gateup")
     g_fl = 2.0 * M * H * 2 * p0.inter_cols
     g_tf = g_fl / (g_t[0] * 1e-3) / 1e12
-    log(f"[bench] gate/up GEMM {g_t[0] * 1e3:.1f} us ({g_tf:.0f} TFLOP/s)")
-    total_ms = time_steps(ctx, step, 1)
-    ms_step = total_ms / args.steps
+    log(f"[bench] RMSNorm + gate/up GEMM {g_t[0] * 1e3:.1f} us ({g_tf:.0f} TFLOP/s) over {g_t[3]} calls")
     rank_fl = (2.0 * M * H * p0.qkv_cols + causal_flops(B, S_, kv_len, p0.q_heads, d) + 2.0 * M * p0.o_rows * H
                + 2.0 * M * H * 3 * p0.inter_cols)
     tflops = t * rank_fl * args.steps / (total_ms * 1e-3) / 1e12
@@ -1133,10 +1187,12 @@ def bench_layer_prefill(ctx):
         "tokens_per_s": M * args.steps / (total_ms * 1e-3),
         "pct_mfma_peak": 100 * tflops / BF16_PEAK_TFLOPS,
         "per_rank": {"flops": rank_fl, "step_us_per_rank": ms_step * 1e3 / t, "gateup_us": g_t[0] * 1e3},
-        "roofline": {"kernel": projection_kernel(M) + ": MLP gate/up + SwiGLU, one rank shard", "bound": "mfma",
+        "roofline": {"kernel": projection_kernel(M) + ": MLP gate/up + SwiGLU, one rank shard (one library call: "
+                               "rmsnorm_kernel, then the GEMM; the RMSNorm's flops are not counted)", "bound": "mfma",
                      "achieved": g_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": g_tf / BF16_PEAK_TFLOPS,
                      "traffic": counted_traffic(f"gateup_layer_prefill_m{M}"), "flops_per_launch": g_fl,
-                     "us_mean": g_t[0] * 1e3, "us_median": g_t[1] * 1e3, "us_min": g_t[2] * 1e3},
+                     "us_mean": g_t[0] * 1e3, "us_median": g_t[1] * 1e3, "us_min": g_t[2] * 1e3,
+                     "timed": f"every MLP gate/up call of the {args.steps} timed steps ({g_t[3]} calls)"},
     }
     config = {"workload": f"70B-shaped full layer prefill, all t={t} rank shards (attention and MLP stages) + "
                           f"on-device sums with residual", "hidden": H, "intermediate": I, "q_heads": nq,
@@ -1341,24 +1397,21 @@ def bench_moe_prefill(ctx):
     out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
     gates = torch.empty(M, E, device="cuda")
 
-    def step(i):
+    def step(i, mk=None):
         for r in range(t):
-            tp.tp_moe_shard_forward(ranks[r], x, parts[r], E, k, cols, eps=wl.eps, ws=ws)
+            marked(mk, "moe", lambda: tp.tp_moe_shard_forward(ranks[r], x, parts[r], E, k, cols, eps=wl.eps, ws=ws))
         tp.tp_partial_sum(parts, out)
 
-    def shard(i):
-        tp.tp_moe_shard_forward(ranks[i % t], x, parts[i % t], E, k, cols, eps=wl.eps, gates=gates, ws=ws)
-
-    for i in range(2 * t):
-        shard(i)
+    # the routing, read back once for the routed flop count
+    tp.tp_moe_shard_forward(ranks[0], x, parts[0], E, k, cols, eps=wl.eps, gates=gates, ws=ws)
     torch.cuda.synchronize()
     routed = int((gates > 0).sum().item())                      # = M * k
     fl_rank = 2.0 * routed * H * 2 * cols + 2.0 * routed * cols * H + 2.0 * M * H * E
-    sh = event_time_ms(torch, shard, 2 * t, reps=3)
-    tf = fl_rank / (sh[0] * 1e-3) / 1e12
-    log(f"[bench] MoE shard {sh[0] * 1e3:.1f} us ({tf:.0f} TFLOP/s routed)")
-    total_ms = time_steps(ctx, step, 1)
+    total_ms, mk = time_steps_eager(ctx, step)
     ms_step = total_ms / args.steps
+    sh = mk.stats("moe")
+    tf = fl_rank / (sh[0] * 1e-3) / 1e12
+    log(f"[bench] MoE shard {sh[0] * 1e3:.1f} us ({tf:.0f} TFLOP/s routed) over {sh[3]} calls")
     tflops = t * fl_rank * args.steps / (total_ms * 1e-3) / 1e12
     extra = {
         "tokens_per_s": M * args.steps / (total_ms * 1e-3),
@@ -1368,8 +1421,9 @@ def bench_moe_prefill(ctx):
         "roofline": {"kernel": "one rank's MoE shard call (router projection and gates, token lists, grouped "
                                "gate/up + SwiGLU GEMM, grouped down GEMM, slot sum)", "bound": "mfma",
                      "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_PEAK_TFLOPS,
-                     "traffic": None, "flops_per_launch": fl_rank, "us_mean": sh[0] * 1e3, "us_median": sh[1] * 1e3,
-                     "us_min": sh[2] * 1e3},
+                     "traffic": counted_traffic(f"moe_prefill_m{M}"), "flops_per_launch": fl_rank,
+                     "us_mean": sh[0] * 1e3, "us_median": sh[1] * 1e3, "us_min": sh[2] * 1e3,
+                     "timed": f"every rank's call in the {args.steps} timed steps ({sh[3]} calls)"},
     }
     config = {"workload": f"Mixtral-8x7B-shaped MoE FFN prefill block, all t={t} rank shards + on-device sum, "
                           f"each expert over its routed tokens", "hidden": H, "intermediate": I, "experts": E,
