@@ -122,10 +122,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t key_block(const uint16_t* rows
 // knows of (it cannot tell that they read the other stage), which would keep
 // the next block's transfers from being issued ahead of this block's reads.
 // The kernel waits for them itself (s_waitcnt vmcnt(0) before the barrier
-// that hands the stage over).
+// that hands the stage over). The compiler writes M0 right before the
+// block; an LDS transfer needs one wait state after an M0 write (the
+// compiler puts the same s_nop before its own), which it cannot see here.
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned off, uint16_t* lds_base) {
     const unsigned lds = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(lds) : "memory");
 }
 typedef short pf_s4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
