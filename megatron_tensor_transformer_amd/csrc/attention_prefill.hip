@@ -63,18 +63,15 @@ __device__ __forceinline__ f32x4_t mfma16x32(const uint4& a, const uint4& b, con
                                                    c, 0, 0, 0);
 }
 
-// Maxima of finite or -inf scores. Written out because fmaxf quiets NaN
-// inputs first, which costs an extra instruction per operand here.
+// Maxima of finite or -inf scores: the IEEE maximum, which needs no quieting
+// of NaN operands first (fmaxf costs an extra instruction per operand) and
+// becomes v_maximum3_f32 on gfx950. A compiler operation, not inline asm, so
+// that the compiler keeps the wait states a matrix instruction's result needs
+// before a vector instruction reads it.
 __device__ __forceinline__ float pf_max3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
-__device__ __forceinline__ float pf_max2(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
+__device__ __forceinline__ float pf_max2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // op over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes of one MFMA
 // column): between the two results of a swap with itself every lane holds its
