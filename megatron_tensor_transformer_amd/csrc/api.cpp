@@ -49,6 +49,11 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 constexpr int kGemvMaxM = 16;   // above this a bf16 projection runs on MFMA when supported
+// ... unless its output is this narrow (a router's logits): a 256 x 256 GEMM tile would leave most of
+// its matrix work idle and split its few tiles' K into float32 tiles, while the decode projections
+// read the activations once in blocks of 16 tokens against one tile of weight rows (the Mixtral
+// router at 4096 tokens: 21 + 38 us on the GEMM and its tail kernel)
+constexpr int kGemmMinN = 65;
 
 tp_status check_dtype(tp_dtype dt) {
     if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d is neither TP_F32 nor TP_BF16", (int)dt);
@@ -89,7 +94,8 @@ tp_status check_ws(void* ws, size_t have, size_t need) {
     } while (0)
 
 bool use_gemm(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi) {
-    return dt == TP_BF16 && epi != tpk::EPI_QKV && m > kGemvMaxM && tpk::gemm_supported((int)m, (int)n, (int)k, epi);
+    return dt == TP_BF16 && epi != tpk::EPI_QKV && m > kGemvMaxM && n >= kGemmMinN &&
+           tpk::gemm_supported((int)m, (int)n, (int)k, epi);
 }
 
 // Scratch bytes (after the counter header) a projection needs: on the GEMM
