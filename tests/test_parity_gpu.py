@@ -490,7 +490,11 @@ LINEAR_CASES = [
     # split; and the t=8 shape at 20 tokens, which takes the prefill GEMM
     (16, 8192, 1280, "bf16"), (16, 6000, 2600, "bf16"), (20, 8192, 1280, "bf16"),
     # prefill GEMM with one to three K tiles (the pipeline's prologue alone), ragged and not
-    (17, 8, 3, "bf16"), (20, 24, 50, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"), (300, 104, 520, "bf16"),
+    (17, 8, 67, "bf16"), (20, 24, 130, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"), (300, 104, 520, "bf16"),
+    # outputs of at most 64 (a router's logits) stay on the decode GEMV at any batch: blocks of 16 tokens
+    # against one weight tile, K split over workgroups; the Mixtral router's shape at 4096 tokens, the
+    # last narrow width and the first on the GEMM
+    (4096, 4096, 8, "bf16"), (300, 1032, 64, "bf16"), (300, 1032, 65, "bf16"),
 ]
 
 
