@@ -82,8 +82,8 @@ def predict(layer_time_one_gpu_s: float, layers: int, hidden: int, tokens: int, 
     """Predicted per-step time and speedup for t = 1..max_t.
 
     ``layer_time_one_gpu_s`` is one layer's decode time with all of its work on
-    one GPU (on this build: the measured time of all t rank shards of a layer
-    run one after another on the single device). Decode is memory-bound, so
+    one GPU (for instance the measured time of all t rank shards of a layer
+    run one after another on a single device). Decode is memory-bound, so
     the whole of it is counted as T_memory.
     """
     link = Interconnect(latency_s, link_bytes_per_s, algorithm)
