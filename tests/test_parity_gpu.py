@@ -669,6 +669,61 @@ def test_prefill_last_token_matches_decode():
     check("decode of the same token", host(dec), ref, TOL["bf16"])
 
 
+def _random_attention_cases(n_cases=16, seed=2025, prefill=False):
+    """Seeded attention shapes: group sizes 1-16, 1-4 kv heads, both head sizes, caches longer than
+    kv_len; decode up to 20,000 keys at batch 1-24, prefill blocks of 1-700 tokens after a cached prefix
+    of up to 800 (work kept small enough for the float64 reference)."""
+    rng = np.random.default_rng(seed + int(prefill))
+    cases = []
+    while len(cases) < n_cases:
+        gq = int(rng.choice([1, 2, 4, 8, 16]))
+        kvh = int(rng.choice([1, 1, 2, 4]))
+        d = int(rng.choice([64, 128]))
+        if prefill:
+            B = int(rng.integers(1, 4))
+            S = int(rng.integers(1, 701))
+            kv_len = S + int(rng.integers(0, 801))
+            if B * gq * kvh * S * kv_len * d > 2e9:
+                continue
+        else:
+            B = int(rng.integers(1, 25))
+            S = 1
+            kv_len = int(rng.integers(1, 20001))
+        cap = kv_len + int(rng.integers(0, 301))
+        if not prefill and (B * gq * kvh * kv_len * d > 1e9 or B * kvh * cap * d > 2e7):
+            continue
+        cases.append((B, gq * kvh, kvh, d, cap, S, kv_len))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_attention_cases(), ids=lambda c: "x".join(map(str, c)))
+def test_decode_attention_random_shapes(case):
+    B, qh, kvh, d, cap, _, kv_len = case
+    seed = 900 + (7 * B + 3 * cap + kv_len) % 1000
+    q = W.to_bf16(W.normal(seed, 0, (B, qh * d)))
+    k = W.to_bf16(W.normal(seed, 1, (B, kvh, cap, d)))
+    v = W.to_bf16(W.normal(seed, 2, (B, kvh, cap, d)))
+    ref = L.decode_attention(q, k, v, kv_len, qh, kvh, d)
+    out = torch.full((B, qh * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tp.tp_decode_attention(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, kv_len, qh)
+    torch.cuda.synchronize()
+    check(f"decode attention {case}", host(out), ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("case", _random_attention_cases(prefill=True), ids=lambda c: "x".join(map(str, c)))
+def test_prefill_attention_random_shapes(case):
+    B, qh, kvh, d, cap, S, kv_len = case
+    seed = 950 + (7 * B + 3 * cap + S) % 1000
+    q = W.to_bf16(W.normal(seed, 0, (B, S, qh * d)))
+    k = W.to_bf16(W.normal(seed, 1, (B, kvh, cap, d)))
+    v = W.to_bf16(W.normal(seed, 2, (B, kvh, cap, d)))
+    ref = L.prefill_attention(q, k, v, kv_len, qh, kvh, d)
+    out = torch.full((B, S, qh * d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tp.tp_prefill_attention(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, kv_len, qh)
+    torch.cuda.synchronize()
+    check(f"prefill attention {case}", host(out), ref, TOL["bf16"])
+
+
 @pytest.mark.parametrize("t", [1, 3, 8])
 @pytest.mark.parametrize("shape", [(5, 7), (16, 8192), (3, 1)])
 @pytest.mark.parametrize("out_dt", ["f32", "bf16"])

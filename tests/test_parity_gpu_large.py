@@ -3,6 +3,8 @@
 - the decode attention stage over more than 16 sequences (the QKV projection with
   its KV-cache append runs over several 16-token blocks, then attention on the
   same batch), every rank's appended k, v and attention partial checked;
+- seeded random decode-layer shapes, both stages of every rank (kv-head
+  replication, odd hidden and intermediate sizes, batches across 16-token blocks);
 - the 70B-shaped layer prefill at t=8 over batch 2 x 2048 tokens, the timed
   prefill-layer shape, every row of the sums and of two ranks' partials;
 - split-K decode projections with more row tiles than the workspace holds
@@ -92,6 +94,66 @@ def test_decode_attention_stage_over_16_sequences(case):
         sr = S.rank_attention(a["x"], a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], kv_len,
                               nq, nkv, d, OP.rank_plan(odesc, t, r), a["gamma"])
         check(f"rank{r} attention partial", host(part), sr["partial"], TOL["bf16"])
+        del rw, kc, vc
+
+
+# ---------------------------------------------------------------- seeded random layer shapes, decode
+
+def _random_layer_cases(n_cases=10, seed=2026):
+    """Seeded decode-layer shapes: head sizes 64 and 128, 1-8 kv heads, groups of 1-8, every t in 1..8
+    the head counts allow (kv-head replication where t exceeds them), hidden and intermediate sizes off
+    the tile multiples, 1-40 sequences, caches of 1-3000 keys with spare capacity."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n_cases:
+        d = int(rng.choice([64, 128]))
+        nkv = int(rng.choice([1, 2, 4, 8]))
+        nq = nkv * int(rng.choice([1, 2, 4, 8]))
+        ts = [t for t in range(1, 9) if nq % t == 0 and (nkv % t == 0 or t % nkv == 0)]
+        t = int(rng.choice(ts))
+        H = 8 * int(rng.integers(8, 385))
+        inter = t * 8 * int(rng.integers(4, 161))
+        B = int(rng.choice([1, 2, 5, 16, 17, 40]))
+        kv_len = int(rng.integers(1, 3001))
+        cap = kv_len + int(rng.integers(0, 65))
+        cases.append((H, inter, nq, nkv, d, t, B, kv_len, cap))
+    return cases
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", _random_layer_cases(), ids=lambda c: "x".join(map(str, c)))
+def test_layer_decode_random_shapes(case):
+    """Both stages of every rank: appended k, v, the attention partial and the MLP partial against the
+    oracle's per-rank shards (the MLP stage reads x, so each stage is checked on its own)."""
+    H, inter, nq, nkv, d, t, B, kv_len, cap = case
+    say(f"random decode layer: hidden {H}, intermediate {inter}, {nq}/{nkv} heads, d {d}, t={t}, batch {B}, "
+        f"kv_len {kv_len}, capacity {cap}")
+    wid = 500 + (H + inter + kv_len) % 400
+    a = W.attention_inputs(wid, H, nq, nkv, d, B, cap, "bf16", "random")
+    mi = W.mlp_inputs(wid, H, inter, B, "bf16", "random")
+    desc = tp.make_desc(H, inter, nq, nkv, d, n_layers=1, seq_len=cap, batch=B)
+    odesc = OP.ModelDesc(hidden=H, intermediate=inter, n_q_heads=nq, n_kv_heads=nkv, head_dim=d, seq_len=cap,
+                         batch=B)
+    x = dev(a["x"], "bf16")
+    g1, g2 = dev(a["gamma"], "bf16"), dev(mi["gamma"], "bf16")
+    for r in range(t):
+        p = tp.tp_shard_plan(desc, t, r)
+        op = OP.rank_plan(odesc, t, r)
+        rw = rank_weights(a, mi, p, d, g1, g2)
+        kb, kn = p.kv_head_begin, p.kv_heads
+        kc = dev(a["k_cache"][:, kb:kb + kn], "bf16")
+        vc = dev(a["v_cache"][:, kb:kb + kn], "bf16")
+        pa, pm = empty((B, H), torch.float32), empty((B, H), torch.float32)
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_ATTN, rw, x, pa, kv={"k": kc, "v": vc, "kv_len": kv_len})
+        tp.tp_layer_shard_forward(desc, p, tp.TP_STAGE_MLP, rw, x, pm)
+        torch.cuda.synchronize()
+        sa = S.rank_attention(a["x"], a["w_q"], a["w_k"], a["w_v"], a["w_o"], a["k_cache"], a["v_cache"], kv_len,
+                              nq, nkv, d, op, a["gamma"])
+        sm = S.rank_mlp(a["x"], mi["w_gate"], mi["w_up"], mi["w_down"], op, mi["gamma"])
+        check(f"rank{r} appended k", host(kc)[:, :, kv_len - 1], sa["k_cache"][:, :, kv_len - 1], TOL["bf16"])
+        check(f"rank{r} appended v", host(vc)[:, :, kv_len - 1], sa["v_cache"][:, :, kv_len - 1], TOL["bf16"])
+        check(f"rank{r} attention partial", host(pa), sa["partial"], TOL["bf16"])
+        check(f"rank{r} MLP partial", host(pm), sm["partial"], TOL["bf16"])
         del rw, kc, vc
 
 
