@@ -36,8 +36,9 @@ STATUS = ["TP_OK", "TP_ERR_NULL", "TP_ERR_SHAPE", "TP_ERR_INDIVISIBLE", "TP_ERR_
 
 EXPORTS = ["tp_shard_plan", "tp_linear_workspace_bytes", "tp_column_linear", "tp_swiglu",
            "tp_row_linear_partial", "tp_partial_sum", "tp_row_linear_partial_bf16", "tp_partial_sum_bf16",
-           "tp_attention_workspace_bytes", "tp_decode_attention",
-           "tp_prefill_attention", "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward", "tp_layer_shard_forward_static", "tp_hbm_stream_read", "tp_status_name", "tp_last_error"]
+           "tp_attention_workspace_bytes", "tp_decode_attention", "tp_prefill_attention",
+           "tp_moe_workspace_bytes", "tp_moe_shard_forward", "tp_layer_workspace_bytes", "tp_layer_shard_forward",
+           "tp_layer_shard_forward_static", "tp_hbm_stream_read", "tp_status_name", "tp_last_error"]
 
 
 class tp_model_desc(ctypes.Structure):
