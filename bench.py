@@ -273,11 +273,12 @@ def calibrate_copy(torch):
     del src, dst
 
 
-def projection_kernel(m, dtype="bf16", wide=False):
-    """The kernel a projection of m tokens runs on (the library's dispatch rule); wide: one whose tiles
-    fill the chip without splitting K (the 8B gate/up and down, the 70B W_o and t=8 MLP), which runs
-    one K range per wave."""
-    if dtype == "bf16" and m > 16:
+def projection_kernel(m, dtype="bf16", wide=False, gemv_max_m=64):
+    """The kernel a projection of m tokens runs on (the library's dispatch rule: the decode projections up
+    to 64 tokens, or 16 for the stacked experts of an MoE decode batch); wide: one whose tiles fill the
+    chip without splitting K (the 8B gate/up and down, the 70B W_o and t=8 MLP), which runs one K range
+    per wave."""
+    if dtype == "bf16" and m > gemv_max_m:
         return "gemm_bf16_kernel (MFMA prefill GEMM)"
     if dtype == "bf16" and m >= 2:
         if wide:
@@ -1273,7 +1274,8 @@ def bench_moe_decode(ctx):
     extra = {
         "step_GBps": t * rank_bytes / (ms_step * 1e-3) / 1e9,
         "per_rank": {"weight_bytes": rank_bytes, "gateup_us": g_t[0] * 1e3, "experts": E, "top_k": k},
-        "roofline": roofline_hbm(projection_kernel(M) + ": every expert's gate/up + SwiGLU (stacked), one rank shard",
+        "roofline": roofline_hbm(projection_kernel(M, gemv_max_m=16) + ": every expert's gate/up + SwiGLU (stacked), "
+                                 "one rank shard",
                                  f"gateup_moe_decode_m{M}", g_bytes, *g_t),
     }
     config = {"workload": f"Mixtral-8x7B-shaped MoE FFN decode block, all t={t} rank shards + on-device sum",

@@ -48,12 +48,24 @@ size_t vec_elems(tp_dtype dt) { return dt == TP_BF16 ? 8 : 4; }
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
-constexpr int kGemvMaxM = 16;   // above this a bf16 projection runs on MFMA when supported
-// ... unless its output is this narrow (a router's logits): a 256 x 256 GEMM tile would leave most of
-// its matrix work idle and split its few tiles' K into float32 tiles, while the decode projections
-// read the activations once in blocks of 16 tokens against one tile of weight rows (the Mixtral
-// router at 4096 tokens: 21 + 38 us on the GEMM and its tail kernel)
+// Up to this many tokens a bf16 projection runs on the decode projections (blocks of 16 tokens, each
+// streaming the weights), above it on the MFMA GEMM, whose 256-row tiles at a few dozen rows leave most
+// of their matrix work idle and split K into float32 tiles. Measured per step: the 70B layer at t=8 with
+// 32 / 64 / 128 sequences 938 / 1624 / 3009 us on the decode projections against 1517 / 1690 / 2172 us
+// on the GEMM, the Llama-3-8B MLP at t=4 with 32 / 64 / 128 tokens 148 / 258 / 467 us against
+// 423 / 425 / 433 us.
+constexpr int kGemvMaxM = 64;
+// Above kGemvMaxM tokens a projection still stays on the decode projections when its output is this
+// narrow (a router's logits): a 256 x 256 GEMM tile would leave most of its matrix work idle and split
+// its few tiles' K into float32 tiles, while the decode projections read the activations once in blocks
+// of 16 tokens against one tile of weight rows (the Mixtral router at 4096 tokens: 21 + 38 us on the
+// GEMM and its tail kernel)
 constexpr int kGemmMinN = 65;
+// The stacked experts of a decode batch (every expert's blocks in one projection, hundreds of MB per
+// rank) go to the GEMM above one block of 16 tokens: there every further block of the decode
+// projections streams all of them again (Mixtral t=2 MoE step at 32 / 64 tokens: 913 / 920 us on the
+// GEMM against 996 / 1917 us on the decode projections).
+constexpr int kStackedGemvMaxM = 16;
 
 tp_status check_dtype(tp_dtype dt) {
     if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_DTYPE, "dtype %d is neither TP_F32 nor TP_BF16", (int)dt);
@@ -93,8 +105,8 @@ tp_status check_ws(void* ws, size_t have, size_t need) {
         if (st_ != TP_OK) return st_;   \
     } while (0)
 
-bool use_gemm(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi) {
-    return dt == TP_BF16 && epi != tpk::EPI_QKV && m > kGemvMaxM && n >= kGemmMinN &&
+bool use_gemm(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, int gemv_max_m = kGemvMaxM) {
+    return dt == TP_BF16 && epi != tpk::EPI_QKV && m > gemv_max_m && n >= kGemmMinN &&
            tpk::gemm_supported((int)m, (int)n, (int)k, epi);
 }
 
@@ -105,8 +117,9 @@ size_t gemm_norm_bytes(int64_t m, int64_t k, tp_dtype dt, bool norm) {
     return norm ? round256((size_t)m * k * esize(dt)) : 0;
 }
 
-size_t linear_scratch(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm) {
-    if (use_gemm(m, k, n, dt, epi))
+size_t linear_scratch(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool norm,
+                      int gemv_max_m = kGemvMaxM) {
+    if (use_gemm(m, k, n, dt, epi, gemv_max_m))
         return gemm_norm_bytes(m, k, dt, norm) + round256(tpk::gemm_scratch_bytes((int)m, (int)n, (int)k, epi));
     return round256(tpk::gemv_plan((int)m, (int)k, (int)n, dt == TP_BF16, epi).ws_bytes);
 }
@@ -125,9 +138,9 @@ size_t linear_ws(int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, bool nor
 // counters: the workspace header; scratch: this call's scratch region.
 tp_status run_linear(const void* x, const void* w, const void* w_up, const void* gamma, float eps, void* y,
                      int64_t m, int64_t k, int64_t n, tp_dtype dt, int epi, unsigned* counters, void* scratch,
-                     hipStream_t s, const tpk::GemvArgs* qkv = nullptr) {
+                     hipStream_t s, const tpk::GemvArgs* qkv = nullptr, int gemv_max_m = kGemvMaxM) {
     const bool norm = gamma != nullptr;
-    if (use_gemm(m, k, n, dt, epi)) {
+    if (use_gemm(m, k, n, dt, epi, gemv_max_m)) {
         const void* xin = x;
         if (norm) {
             hipError_t e = tpk::rmsnorm_launch(x, gamma, scratch, (int)m, (int)k, eps, 1, s);
@@ -451,8 +464,8 @@ MoeWs moe_ws(int64_t m, int64_t H, int32_t E, int64_t cols, bool norm, int32_t t
         w.parts = round256((size_t)top_k * m * H * 4);
     } else {
         w.act = round256((size_t)m * ecols * 2);
-        const size_t l2 = linear_scratch(m, H, ecols, TP_BF16, tpk::EPI_SWIGLU, false);
-        const size_t l3 = linear_scratch(m, ecols, H, TP_BF16, tpk::EPI_PARTIAL, false);
+        const size_t l2 = linear_scratch(m, H, ecols, TP_BF16, tpk::EPI_SWIGLU, false, kStackedGemvMaxM);
+        const size_t l3 = linear_scratch(m, ecols, H, TP_BF16, tpk::EPI_PARTIAL, false, kStackedGemvMaxM);
         if (l2 > l) l = l2;
         if (l3 > l) l = l3;
     }
@@ -569,13 +582,13 @@ tp_status tp_moe_shard_forward(const tp_moe_weights* w, const void* x, float* pa
     }
     // Every expert's gate/up column block at once (rows stacked expert by expert).
     TRY(run_linear(xin, w->w_gate, w->w_up, nullptr, 0.f, act, m, hidden, ecols, TP_BF16, tpk::EPI_SWIGLU, cnt,
-                   lin, s));
+                   lin, s, nullptr, kStackedGemvMaxM));
     e = tpk::moe_scale_launch(act, gates, (int)m, n_experts, inter_cols, s);
     if (e != hipSuccess) return hip_fail(e, "expert gate scaling launch");
     // Every expert's down row block at once: the gate-weighted sum over experts is the contraction over the
     // stacked intermediate columns.
     return run_linear(act, w->w_down, nullptr, nullptr, 0.f, partial, m, ecols, hidden, TP_BF16, tpk::EPI_PARTIAL,
-                      cnt, lin, s);
+                      cnt, lin, s, nullptr, kStackedGemvMaxM);
 }
 
 size_t tp_attention_workspace_bytes(int64_t batch, int32_t q_heads, int32_t kv_heads, int32_t head_dim,
