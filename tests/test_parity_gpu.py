@@ -487,10 +487,13 @@ LINEAR_CASES = [
     (16, 1032, 3300, "bf16"), (16, 8192, 2560, "bf16"), (16, 4104, 1280, "bf16"), (7, 1032, 1500, "bf16"),
     # 8-wave tiles of 16 to 32 rows with K split over workgroups and merged (where 64-row tiles would
     # stream chunks of 1024 or less): the 70B QKV shard at t=8, ragged n with K ending inside the second
-    # split; and the t=8 shape at 20 tokens, which takes the prefill GEMM
-    (16, 8192, 1280, "bf16"), (16, 6000, 2600, "bf16"), (20, 8192, 1280, "bf16"),
+    # split; the t=8 shape at 20 tokens (two token blocks) and at 65 tokens, the first batch on the GEMM
+    (16, 8192, 1280, "bf16"), (16, 6000, 2600, "bf16"), (20, 8192, 1280, "bf16"), (65, 8192, 1280, "bf16"),
+    # 17 to 64 tokens stay on the decode GEMV (two to four token blocks) with K of one to three stages
+    (17, 8, 67, "bf16"), (20, 24, 130, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"),
     # prefill GEMM with one to three K tiles (the pipeline's prologue alone), ragged and not
-    (17, 8, 67, "bf16"), (20, 24, 130, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"), (300, 104, 520, "bf16"),
+    (65, 8, 67, "bf16"), (80, 24, 130, "bf16"), (100, 64, 300, "bf16"), (129, 96, 260, "bf16"),
+    (300, 104, 520, "bf16"),
     # outputs of at most 64 (a router's logits) stay on the decode GEMV at any batch: blocks of 16 tokens
     # against one weight tile, K split over workgroups; the Mixtral router's shape at 4096 tokens, the
     # last narrow width and the first on the GEMM
@@ -525,13 +528,14 @@ def test_linear_shapes(case, mode):
     check(f"{mode} m={m} k={k} n={n} {dt}", host(y), ref, TOL[dt])
 
 
-def _random_linear_cases(n_cases=24, seed=2024):
-    """Seeded shapes across both decode projection kernels and the GEMM: m 1-40, k a multiple of 8 up
-    to 9000, n up to 9000 (work kept small enough for the float64 reference)."""
+def _random_linear_cases(n_cases=24, seed=2024, ms=(1, 3, 5, 8, 12, 16, 16, 16, 20, 40)):
+    """Seeded shapes across the decode projection kernels (m 1-64) and the GEMM (m above 64): m drawn
+    from `ms`, k a multiple of 8 up to 9000, n up to 9000 (work kept small enough for the float64
+    reference)."""
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n_cases:
-        m = int(rng.choice([1, 3, 5, 8, 12, 16, 16, 16, 20, 40]))
+        m = int(rng.choice(ms))
         k = 8 * int(rng.integers(1, 1126))
         n = int(rng.integers(1, 9001))
         if m * k * n > 1.5e8:
@@ -541,7 +545,8 @@ def _random_linear_cases(n_cases=24, seed=2024):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_linear_cases(), ids=lambda c: "x".join(map(str, c)))
+@pytest.mark.parametrize("case", _random_linear_cases() + _random_linear_cases(10, 2025, (65, 80, 128, 200)),
+                         ids=lambda c: "x".join(map(str, c)))
 def test_linear_random_shapes(case):
     m, k, n, mode = case
     seed = 700 + (13 * m + 5 * k + n) % 1000
