@@ -211,6 +211,7 @@ GemvPlan gemv_plan_dot2(int m, int K, int N, int is_bf16, int epi) {
     p.mt = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
     if (!is_bf16 && p.mt != 1 && p.mt != 4) p.mt = (m <= 4) ? 4 : 16;
     p.mblocks = (m + p.mt - 1) / p.mt;
+    p.mbw = 1;
     p.nw = GEMV_NW;
     p.rows_per_tile = GEMV_NW * rows_per_wave(p.mt);
     p.out_per_tile = (epi == EPI_SWIGLU) ? p.rows_per_tile / 2 : p.rows_per_tile;

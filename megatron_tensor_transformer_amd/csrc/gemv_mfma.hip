@@ -316,35 +316,41 @@ __device__ __forceinline__ uint4 wd_load16(__amdgpu_buffer_rsrc_t r, unsigned of
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int EPI, bool NORM, int NST, int ROWS>
+template <int EPI, bool NORM, int NST, int ROWS, int MB>
 __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
     static_assert(ROWS == 16 || ROWS == 32, "one or two 16-row operand tiles");
+    static_assert(MB == 1 || MB == 2, "one or two token blocks per weight fetch");
     constexpr int NT = WD_NW * 64;
     constexpr bool SWI = (EPI == EPI_SWIGLU);
     constexpr int NQ = ROWS / 4;                // transfers per stage, 4 rows x 256 bytes each
     constexpr int NTT = ROWS / 16;              // 16-row operand tiles
+    constexpr int MT = MB * SK_MT;              // tokens of the workgroup
     constexpr int WD_STAGE = ROWS * WD_SUB;     // elements of a wave's stage
-    constexpr int VM = 4 + (NORM ? 4 : 0) + NQ; // vector-memory operations per stage
+    constexpr int VM = 4 * MB + (NORM ? 4 : 0) + NQ;   // vector-memory operations per stage
     // A ring of NBUF stage tiles per wave, NBUF - 1 stages requested ahead;
     // each tile of the ring is its own array, so the compiler can tell one
-    // stage's transfers from another stage's reads.
-    constexpr int NBUF = ROWS == 32 ? 2 : WD16_NBUF;
+    // stage's transfers from another stage's reads. Two token blocks hold
+    // twice the activation registers per stage in flight, so 16-row tiles
+    // then keep three stages, not four.
+    constexpr int NBUF = ROWS == 32 ? 2 : (MB == 1 ? WD16_NBUF : 3);
     static_assert(NBUF >= 2 && NBUF <= 4 && VM * (NBUF - 1) <= 63, "the ring and the wait counter");
+    // a wave's first tile holds its MT x ROWS float32 sums at the end
+    static_assert(MT * ROWS * 4 <= WD_STAGE * 2, "the parked sums fit a stage tile");
     __shared__ __align__(16) uint16_t w0[WD_NW][WD_STAGE];
     __shared__ __align__(16) uint16_t w1[WD_NW][WD_STAGE];
     __shared__ __align__(16) uint16_t w2[WD_NW][NBUF > 2 ? WD_STAGE : 8];
     __shared__ __align__(16) uint16_t w3[WD_NW][NBUF > 3 ? WD_STAGE : 8];
-    __shared__ float res[SK_MT * ROWS];
-    __shared__ float ssl[WD_NW][SK_MT];
+    __shared__ float res[MT * ROWS];
+    __shared__ float ssl[WD_NW][MT];
 
     const GemvArgs& a = d.a;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases stay scalar
-    const int tile = blockIdx.x, mb = d.mb0 + blockIdx.z;
+    const int tile = blockIdx.x, mb = d.mb0 + blockIdx.z * MB;  // first token block of the workgroup
     const int K = a.K, N = a.N;
     const int kw = (blockIdx.y * WD_NW + wave) * (NST * WD_SUB);   // first K element of this wave's range
     const int m0 = mb * SK_MT;
-    const int mvalid = min(SK_MT, a.m - m0);
+    const int mvalid = min(MT, a.m - m0);
     const int col = lane & 15, kg = lane >> 4;
 
     // Weight views: for SwiGLU the gate rows and the up rows of outputs
@@ -371,18 +377,21 @@ __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) wck[q] = ((lane & 15) ^ ((4 * q + dr) & 15)) * 8;
-    // Activation and gamma views: token col's row, chunk kg of each 32.
+    // Activation and gamma views: token col's row of each token block, chunk
+    // kg of each 32. Rows past m lie past the view and arrive as zeros.
     const __amdgpu_buffer_rsrc_t xv = wd_view(reinterpret_cast<const uint16_t*>(a.x) + (size_t)m0 * K, mvalid * rowb);
     const __amdgpu_buffer_rsrc_t gv = wd_view(a.gamma, NORM ? rowb : 0);
     const unsigned xrow = col * K * 2;
 
-    struct Act { uint4 x[4]; uint4 g[4]; };
+    struct Act { uint4 x[MB][4]; uint4 g[4]; };
     auto issue = [&](Act& ac, uint16_t* dst, int st) {
         const int k0 = kw + st * WD_SUB;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int k = k0 + s * 32 + kg * 8;
-            ac.x[s] = wd_load16(xv, k < K ? xrow + k * 2 : WD_OOB);
+#pragma unroll
+            for (int b = 0; b < MB; ++b)
+                ac.x[b][s] = wd_load16(xv, k < K ? xrow + (unsigned)(b * SK_MT * K * 2) + k * 2 : WD_OOB);
             if (NORM) ac.g[s] = wd_load16(gv, k < K ? k * 2 : WD_OOB);
         }
 #pragma unroll
@@ -392,29 +401,52 @@ __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
         }
     };
 
-    float ss = 0.f;
-    f32x4_t acc[NTT];
+    float ss[MB];
+    f32x4_t acc[MB][NTT];
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < MB; ++b) {
+        ss[b] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NTT; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // One stage: the weight fragments are read from LDS once and serve every
+    // token block.
     auto run = [&](Act& cur, const uint16_t* tl) {
-        uint4 b[NTT][4];
+        uint4 wf[NTT][4];
 #pragma unroll
         for (int t = 0; t < NTT; ++t)
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int r = t * 16 + col;
-                b[t][s] = *reinterpret_cast<const uint4*>(&tl[r * WD_SUB + (((s * 4 + kg) ^ (r & 15)) * 8)]);
+                wf[t][s] = *reinterpret_cast<const uint4*>(&tl[r * WD_SUB + (((s * 4 + kg) ^ (r & 15)) * 8)]);
             }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 xa = cur.x[s];
-            if (NORM) {
-                ss += vsumsq(xa, (uint16_t*)nullptr);
-                xa = vscale(xa, cur.g[s], (uint16_t*)nullptr);
-            }
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int t = 0; t < NTT; ++t) acc[t] = mfma16(xa, b[t][s], acc[t]);
-        }
+            for (int b = 0; b < MB; ++b) {
+                uint4 xa = cur.x[b][s];
+                if (NORM) {
+                    if constexpr (MB == 1) {
+                        ss[b] += vsumsq(xa, (uint16_t*)nullptr);
+                    } else {            // squares by v_dot2 on the packed pairs: no unpacked copy kept
+                        float q = dot2_bf16(xa.x, xa.x, 0.f);
+                        q = dot2_bf16(xa.y, xa.y, q);
+                        q = dot2_bf16(xa.z, xa.z, q);
+                        ss[b] += dot2_bf16(xa.w, xa.w, q);
+                        // the sum is consumed only after the last stage: left free, the
+                        // compiler sinks the chain there and keeps every stage's
+                        // activations live; an empty asm reading it pins it to this stage
+                        asm volatile("" : "+v"(ss[b]));
+                    }
+                    xa = vscale(xa, cur.g[s], (uint16_t*)nullptr);
+                }
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) acc[b][t] = mfma16(xa, wf[t][s], acc[b][t]);
+                // with two token blocks, one 32-element slice at a time: scheduled
+                // as one region the unpacked activations and gamma of all four
+                // slices stay live together and spill
+                if constexpr (MB > 1) __builtin_amdgcn_sched_barrier(0);
+            }
     };
     // stage i's tile (i is a constant once the loops are unrolled)
     auto tile_of = [&](int i) -> uint16_t* {
@@ -447,39 +479,48 @@ __global__ __launch_bounds__(WD_NW * 64) void gemv_mfma_wide_kernel(GemvDev d) {
     }
 
     // Sums of the K ranges, added in wave order (deterministic): every wave
-    // parks its 16 tokens x ROWS rows in its first tile (its own reads of it
+    // parks its MT tokens x ROWS rows in its first tile (its own reads of it
     // and transfers into it are complete).
     float* park = reinterpret_cast<float*>(w0[wave]);
 #pragma unroll
-    for (int t = 0; t < NTT; ++t)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) park[(4 * kg + j) * ROWS + t * 16 + col] = acc[t][j];
+        for (int t = 0; t < NTT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) park[(b * SK_MT + 4 * kg + j) * ROWS + t * 16 + col] = acc[b][t][j];
     if (NORM) {
         // lanes col, col + 16, col + 32, col + 48 hold token col's squares
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (lane < 16) ssl[wave][lane] = ss;
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            float v = ss[b];
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            if (lane < 16) ssl[wave][b * SK_MT + lane] = v;
+        }
     }
     __syncthreads();
-    for (int e = tid; e < SK_MT * ROWS; e += NT) {
+    for (int e = tid; e < MT * ROWS; e += NT) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < WD_NW; ++w) v += reinterpret_cast<const float*>(w0[w])[e];
         res[e] = v;
     }
-    if (NORM && tid < SK_MT) {
+    if (NORM && tid < MT) {
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < WD_NW; ++w) v += ssl[w][tid];
         ssl[0][tid] = v;
     }
     __syncthreads();
-    if (d.splits > 1) {
-        __shared__ int s_last;
-        if (!split_merge<ROWS, NORM, NT>(d, res, ssl[0], blockIdx.z * d.n_tiles + tile, blockIdx.y, mvalid, &s_last))
-            return;
+    if constexpr (MB == 1) {                    // the plan splits K over workgroups only for one token block
+        if (d.splits > 1) {
+            __shared__ int s_last;
+            if (!split_merge<ROWS, NORM, NT>(d, res, ssl[0], blockIdx.z * d.n_tiles + tile, blockIdx.y, mvalid,
+                                             &s_last))
+                return;
+        }
     }
-    gemv_epilogue<uint16_t, SK_MT, ROWS, EPI, NORM, NT>(a, res, ssl[0], tile, m0, mvalid, opt);
+    gemv_epilogue<uint16_t, MT, ROWS, EPI, NORM, NT>(a, res, ssl[0], tile, m0, mvalid, opt);
 }
 
 // Split-K merge: one workgroup per output tile adds the tile's slices in
@@ -536,6 +577,7 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
     p.mfma = 1;
     p.mt = SK_MT;
     p.mblocks = (m + SK_MT - 1) / SK_MT;
+    p.mbw = 1;
     p.mb_per_launch = p.mblocks;                // capped below where split workgroups count arrivals
     p.lds_bytes = 0;                            // static LDS only
     const bool swi = epi == EPI_SWIGLU;
@@ -552,13 +594,19 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
     // over workgroups. Measured on replayed 8B MLP and 70B attention
     // projection steps and the 70B layer: tiles of 10 rows (70B QKV, t=4)
     // or 5 (t=8) lose to the split, by 0.3 and 3 us per call.
+    // A wide workgroup takes two blocks of 16 tokens per weight fetch (the
+    // weight fragments it reads from LDS serve both), so 17 to 32 tokens
+    // stream the weights once and 33 to 64 twice; the tiles are sized as for
+    // the blocks of 16 tokens a launch then has in z (wb).
+    const int64_t mbw = mb >= 2 ? 2 : 1;
+    const int64_t wb = (mb + mbw - 1) / mbw;
     const int64_t t2 = swi ? (N + 15) / 16 : (N + 31) / 32;
-    const int64_t want = std::max<int64_t>(1, 256 / mb);
+    const int64_t want = std::max<int64_t>(1, 256 / wb);
     const int64_t per = (N + want - 1) / want;  // outputs per tile for ~256 workgroups
     const int64_t cap16 = swi ? 8 : 16, cap32 = swi ? 16 : 32;
     int rg = SK_NW, ks = 1, opt = swi ? 8 * SK_NW : 16 * SK_NW;
     if (K <= 4 * SK_MAX_STAGES * SK_SUB) {
-        if (swi && t2 * mb >= 512 && K <= 2 * SK_MAX_STAGES * SK_SUB) {
+        if (swi && t2 * wb >= 512 && K <= 2 * SK_MAX_STAGES * SK_SUB) {
             rg = 2, ks = 2, opt = 16;
         } else if (per > cap16) {
             rg = 2, ks = 4, opt = (int)std::min(cap32, per);
@@ -581,6 +629,7 @@ static GemvPlan plan_mfma(int m, int K, int N, int epi) {
         while (kc * span < K) kc *= 2;          // at most SK_MAX_STAGES stages by the guard above
         p.kc = kc;
         p.splits = 1;
+        if (rg * ks == WD_NW) p.mbw = (int)mbw; // the wide kernel
         return p;
     }
     // Narrow projections, 4 waves per 64-row tile, K split over workgroups.
@@ -657,11 +706,18 @@ static hipError_t mfma_launch_t(const GemvDev& d, const GemvPlan& p, hipStream_t
     for (int mb0 = 0; mb0 < p.mblocks; mb0 += p.mb_per_launch) {
         GemvDev dl = d;
         dl.mb0 = mb0;
-        dim3 grid(p.n_tiles, p.splits, min(p.mb_per_launch, p.mblocks - mb0));
-        if constexpr (RG * KS == WD_NW)         // 16 RG rows; 8 K ranges of NST stages of 128
-            hipLaunchKernelGGL((gemv_mfma_wide_kernel<EPI, NORM, NST, 16 * RG>), grid, dim3(WD_NW * 64), 0, s, dl);
-        else
+        const int blocks = min(p.mb_per_launch, p.mblocks - mb0);
+        dim3 grid(p.n_tiles, p.splits, (blocks + p.mbw - 1) / p.mbw);   // z: groups of mbw token blocks
+        if constexpr (RG * KS == WD_NW) {       // 16 RG rows; 8 K ranges of NST stages of 128
+            if (p.mbw == 2)
+                hipLaunchKernelGGL((gemv_mfma_wide_kernel<EPI, NORM, NST, 16 * RG, 2>), grid, dim3(WD_NW * 64), 0, s,
+                                   dl);
+            else
+                hipLaunchKernelGGL((gemv_mfma_wide_kernel<EPI, NORM, NST, 16 * RG, 1>), grid, dim3(WD_NW * 64), 0, s,
+                                   dl);
+        } else {
             hipLaunchKernelGGL((gemv_mfma_kernel<EPI, NORM, NST, RG, KS>), grid, dim3(RG * KS * 64), 0, s, dl);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (RG * KS != WD_NW && p.splits > 1) {  // the wide kernel merges its splits itself
@@ -697,6 +753,8 @@ static hipError_t mfma_launch_shape(const GemvDev& d, const GemvPlan& p, hipStre
 
 hipError_t gemv_mfma_launch(const GemvDev& d, const GemvPlan& p, hipStream_t s) {
     if (p.splits > 1 && p.ks != 1 && p.rg * p.ks != WD_NW) return hipErrorInvalidValue;
+    // two token blocks per workgroup: the wide kernel only, K not split over workgroups
+    if (p.mbw != 1 && (p.mbw != 2 || p.splits != 1 || p.rg * p.ks != WD_NW)) return hipErrorInvalidValue;
     const bool nrm = d.a.norm != 0;
     switch (d.a.epi) {
         case EPI_STORE:

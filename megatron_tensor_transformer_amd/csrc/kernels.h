@@ -48,6 +48,7 @@ struct GemvPlan {
     int rg, ks;    // matrix-core kernels: (4, 1) 64-row tiles split over workgroups, (2, 2) two K ranges of
                    // 2 waves; (2, 4) and (1, 8) the wide kernel's 32- and 16-row tiles, 8 waves, one K range each
     int mblocks;   // ceil(m / mt)
+    int mbw;       // token blocks one workgroup of the wide matrix-core kernel takes per weight fetch (1 or 2)
     int mb_per_launch;  // m-blocks per launch, so a launch's tiles fit the counter header
     int tiles_per_launch;  // row tiles per launch (all of them unless the counters would not fit)
     int rows_per_tile;  // weight rows a workgroup covers

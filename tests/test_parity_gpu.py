@@ -489,6 +489,12 @@ LINEAR_CASES = [
     # stream chunks of 1024 or less): the 70B QKV shard at t=8, ragged n with K ending inside the second
     # split; the t=8 shape at 20 tokens (two token blocks) and at 65 tokens, the first batch on the GEMM
     (16, 8192, 1280, "bf16"), (16, 6000, 2600, "bf16"), (20, 8192, 1280, "bf16"), (65, 8192, 1280, "bf16"),
+    # 17 to 64 tokens on the 8-wave GEMV, two token blocks per workgroup: the 70B gate/up, down and W_o
+    # shards at t=8 and the 8B down shard at t=4 (16-row tiles); ragged K and n; 16-row tiles at four
+    # blocks and, for SwiGLU, at two; a second block of one row (17, 33 tokens) or none (40, 48 tokens)
+    (32, 8192, 3584, "bf16"), (40, 3584, 8192, "bf16"), (24, 1024, 8192, "bf16"), (32, 3584, 4096, "bf16"),
+    (48, 8136, 2600, "bf16"), (64, 4104, 4096, "bf16"), (56, 2048, 2000, "bf16"), (20, 4096, 2000, "bf16"),
+    (17, 2056, 6200, "bf16"), (33, 136, 6100, "bf16"),
     # 17 to 64 tokens stay on the decode GEMV (two to four token blocks) with K of one to three stages
     (17, 8, 67, "bf16"), (20, 24, 130, "bf16"), (18, 64, 300, "bf16"), (64, 96, 260, "bf16"),
     # prefill GEMM with one to three K tiles (the pipeline's prologue alone), ragged and not

@@ -7,6 +7,9 @@
   use more counters than the workspace header holds, however many row tiles
   the output has or however many tokens the batch has. (The 4-wave
   matrix-core kernel's splits go to a merge kernel and use no counters.)
+- The 8-wave matrix-core kernel takes two blocks of 16 tokens per weight fetch
+  only where it does not split K over workgroups (its slices and counters are
+  per token block), and the decode shapes of 17 to 64 tokens take it.
 - The decode attention's split-KV scratch depends on kv_len in a way that is
   not monotone, so the layer workspace sizes it by a bound over every kv_len up
   to the cache capacity; the bound must cover each kv_len.
@@ -75,3 +78,27 @@ def test_split_k_counters_fit_the_header(probe):
 def test_attention_scratch_bound_covers_every_kv_len(probe, batch, q_heads, kv_heads, head_dim, capacity):
     (r,) = probe([f"attn {batch} {q_heads} {kv_heads} {head_dim} {capacity}"])
     assert r["max_ws"] <= r["bound"], r
+
+
+def test_two_token_blocks_per_weight_fetch(probe):
+    queries = []
+    for epi in (0, 1, 2, 3):
+        for m in (1, 2, 16, 17, 20, 32, 33, 40, 48, 64):
+            for K in (136, 1024, 3584, 4096, 8192, 8200):
+                for N in (64, 1000, 1280, 2100, 4096, 7168, 8192, 14336):
+                    queries.append((m, K, N, epi))
+    plans = probe([f"gemv {m} {K} {N} 1 {epi}" for m, K, N, epi in queries])
+    paired = 0
+    for q, p in zip(queries, plans):
+        assert p["mbw"] in (1, 2), (q, p)
+        if p["mbw"] == 2:
+            assert p["mfma"] == 1 and p["waves"] == 8 and p["splits"] == 1 and p["mblocks"] >= 2, (q, p)
+            assert p["mb_per_launch"] == p["mblocks"], (q, p)
+            paired += 1
+        if p["mblocks"] == 1:
+            assert p["mbw"] == 1, (q, p)
+    assert paired > 0
+    # the 70B layer's gate/up, down and W_o shards at t=8 and the Llama-3-8B MLP shard at t=4, 17-64 tokens
+    shapes = [(8192, 3584, 2), (3584, 8192, 1), (1024, 8192, 1), (4096, 3584, 2), (3584, 4096, 1)]
+    got = probe([f"gemv {m} {K} {N} 1 {epi}" for m in (17, 32, 40, 64) for K, N, epi in shapes])
+    assert all(p["mbw"] == 2 for p in got), got
