@@ -277,10 +277,13 @@ def projection_kernel(m, dtype="bf16", wide=False, gemv_max_m=64):
     """The kernel a projection of m tokens runs on (the library's dispatch rule: the decode projections up
     to 64 tokens, or 16 for the stacked experts of an MoE decode batch); wide: one whose tiles fill the
     chip without splitting K (the 8B gate/up and down, the 70B W_o and t=8 MLP), which runs one K range
-    per wave."""
+    per wave and, above 16 tokens, two blocks of 16 tokens per weight fetch."""
     if dtype == "bf16" and m > gemv_max_m:
         return "gemm_bf16_kernel (MFMA prefill GEMM)"
     if dtype == "bf16" and m >= 2:
+        if wide and m > 16:
+            return ("gemv_mfma_wide_kernel (matrix-core decode projection, one K range per wave, two 16-token "
+                    "blocks per weight fetch)")
         if wide:
             return "gemv_mfma_wide_kernel (matrix-core decode projection, one K range per wave)"
         return "gemv_mfma_kernel (matrix-core decode projection)"
