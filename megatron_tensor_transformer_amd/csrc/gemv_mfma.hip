@@ -1,5 +1,5 @@
-// Decode projections of a few to 16 tokens on the matrix cores
-// (v_mfma_f32_16x16x32_bf16).
+// Decode projections of 2 to 64 tokens on the matrix cores
+// (v_mfma_f32_16x16x32_bf16), in blocks of 16 tokens.
 //
 // At 16 tokens a v_dot2 projection needs more VALU issue slots than the
 // weight stream leaves, although the work is still a dense contraction of a
@@ -17,7 +17,10 @@
 //    DMA into the wave's own LDS tiles (4 rows x 256 bytes per transfer),
 //    activation operands are read straight from memory, and the waves meet
 //    only when their sums are added at the end: no workgroup barrier while
-//    streaming. Where K is also split over workgroups (narrow outputs), each
+//    streaming. Above 16 tokens, unless K is split over workgroups, a
+//    workgroup takes two token blocks, each weight fragment feeding one MFMA
+//    per block, so the weights stream once per 32 tokens. Where K is also
+//    split over workgroups (narrow outputs), each
 //    publishes its float32 slice with coherent stores and the last of them
 //    to arrive adds the slices and runs the epilogue: no second kernel.
 //  - Narrow projections and the stacked experts (gemv_mfma_kernel): waves
