@@ -17,9 +17,9 @@ int main() {
             if (scanf("%d %d %d %d %d", &m, &K, &N, &bf, &epi) != 5) return 2;
             const tpk::GemvPlan p = tpk::gemv_plan(m, K, N, bf, epi);
             printf("mfma=%d mt=%d mblocks=%d mbw=%d mb_per_launch=%d tiles_per_launch=%d rows_per_tile=%d "
-                   "n_tiles=%d kc=%d splits=%d ws_bytes=%zu header_counters=%d waves=%d\n",
-                   p.mfma, p.mt, p.mblocks, p.mbw, p.mb_per_launch, p.tiles_per_launch, p.rows_per_tile, p.n_tiles,
-                   p.kc, p.splits, p.ws_bytes, tpk::WS_MAX_COUNTERS, p.nw);
+                   "out_per_tile=%d n_tiles=%d kc=%d splits=%d ws_bytes=%zu header_counters=%d waves=%d\n",
+                   p.mfma, p.mt, p.mblocks, p.mbw, p.mb_per_launch, p.tiles_per_launch, p.rows_per_tile,
+                   p.out_per_tile, p.n_tiles, p.kc, p.splits, p.ws_bytes, tpk::WS_MAX_COUNTERS, p.nw);
         } else if (!strcmp(kind, "attn")) {
             int b, q, kv, d, cap;
             if (scanf("%d %d %d %d %d", &b, &q, &kv, &d, &cap) != 5) return 2;

@@ -98,6 +98,23 @@ def test_two_token_blocks_per_weight_fetch(probe):
         if p["mblocks"] == 1:
             assert p["mbw"] == 1, (q, p)
     assert paired > 0
+    # every (output, token) pair is covered exactly once: row tiles of out_per_tile outputs (the gate and up
+    # rows of each output sit in one tile), launches of mb_per_launch token blocks, and in each launch z
+    # groups of mbw blocks of 16 tokens
+    for q, p in zip(queries, plans):
+        m, K, N, epi = q
+        opt, rows = p["out_per_tile"], p["rows_per_tile"]
+        assert 1 <= opt <= (rows // 2 if epi == 2 else rows), (q, p)
+        assert p["n_tiles"] == -(-N // opt), (q, p)
+        seen = [0] * p["mblocks"]
+        for mb0 in range(0, p["mblocks"], p["mb_per_launch"]):
+            blocks = min(p["mb_per_launch"], p["mblocks"] - mb0)
+            for z in range(-(-blocks // p["mbw"])):
+                first = mb0 + z * p["mbw"]
+                for b in range(p["mbw"]):
+                    if first + b < min(mb0 + blocks, p["mblocks"]):
+                        seen[first + b] += 1
+        assert seen == [1] * p["mblocks"] and p["mblocks"] * p["mt"] >= m > (p["mblocks"] - 1) * p["mt"], (q, p)
     # the 70B layer's gate/up, down and W_o shards at t=8 and the Llama-3-8B MLP shard at t=4, 17-64 tokens
     shapes = [(8192, 3584, 2), (3584, 8192, 1), (1024, 8192, 1), (4096, 3584, 2), (3584, 4096, 1)]
     got = probe([f"gemv {m} {K} {N} 1 {epi}" for m in (17, 32, 40, 64) for K, N, epi in shapes])
