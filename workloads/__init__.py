@@ -179,7 +179,7 @@ def prefill_attention_inputs(workload_id: int, batch: int, seq: int, n_q: int, n
     }
 
 
-MOE_EXPERTS, MOE_TOP_K = 8, 2       # the Mixtral-8x7B routing of workload 8
+MOE_EXPERTS, MOE_TOP_K = 8, 2       # the Mixtral-8x7B routing: 8 experts, the top 2 per token
 
 
 def moe_inputs(workload_id: int, hidden: int, intermediate: int, n_experts: int, m: int,
