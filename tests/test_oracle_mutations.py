@@ -223,6 +223,54 @@ def _append_wrong_slot(kc, vc, kn, vn, kv_len, n_kv, d):
     return kc2, vc2
 
 
+def _rank_mlp_silu_on_up(x, w_gate, w_up, w_down, p, gamma=None, eps=1e-5):
+    b, c = p["inter_begin"], p["inter_cols"]
+    u = S._norm(x, gamma, eps)
+    g = S._mm(u, S.column_shard(w_gate, b, c))
+    v = S._mm(u, S.column_shard(w_up, b, c))
+    a = S._silu(v) * g
+    return {"gate": g, "up": v, "a": a, "partial": S._mm(a, S.row_shard(w_down, b, c))}
+
+
+def _layer_mlp_reads_x(x, w, k_cache, v_cache, kv_len, n_q, n_kv, d, eps=1e-5, residual=True):
+    attn = L.attention_block(x, w["w_q"], w["w_k"], w["w_v"], w["w_o"], k_cache, v_cache, kv_len,
+                             n_q, n_kv, d, w.get("gamma1"), eps)
+    h = L.f64(x) + attn["y"] if residual else attn["y"]
+    mlp = L.mlp_block(x if residual else h, w["w_gate"], w["w_up"], w["w_down"], w.get("gamma2"), eps)
+    out = h + mlp["y"] if residual else mlp["y"]
+    return {"attn": attn, "h": h, "mlp": mlp, "out": out}
+
+
+def _layer_out_skips_attention(x, w, k_cache, v_cache, kv_len, n_q, n_kv, d, eps=1e-5, residual=True):
+    r = _orig_layer(x, w, k_cache, v_cache, kv_len, n_q, n_kv, d, eps, residual)
+    if residual:
+        r["out"] = L.f64(x) + r["mlp"]["y"]
+    return r
+
+
+def _moe_block_experts_reversed(x, gamma, w_router, experts, k, eps=1e-5, gates=None):
+    u = L.rmsnorm(x, gamma, eps) if gamma is not None else L.f64(x)
+    logits = L.linear(u, w_router)
+    if gates is None:
+        gates = L.moe_route(logits, k)
+    y = np.zeros((u.shape[0], np.shape(experts[0][2])[1]))
+    E = len(experts)
+    for e, (wg, wu, wd) in enumerate(experts):
+        y += gates[:, E - 1 - e:E - e] * L.linear(L.swiglu(L.linear(u, wg), L.linear(u, wu)), wd)
+    return {"u": u, "logits": logits, "gates": gates, "y": y}
+
+
+def _rank_attention_q_from_kv_block(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len, n_q, n_kv, d, p, gamma=None,
+                                    eps=1e-5):
+    # the rank reads the next rank's q heads (an off-by-one-rank slip; t = 1 has no other rank)
+    p2 = dict(p)
+    p2["q_head_begin"] = (p["q_head_begin"] + p["q_heads"]) % n_q
+    return _orig_rank_attention(x, w_q, w_k, w_v, w_o, k_cache, v_cache, kv_len, n_q, n_kv, d, p2, gamma, eps)
+
+
+_orig_layer = L.layer
+
+
 MUTATIONS = {
     # elementwise
     "silu_sign": (L, "silu", lambda z: np.asarray(z, float) * L.sigmoid(-np.asarray(z, float)), _all_layer_pins),
@@ -262,7 +310,12 @@ MUTATIONS = {
     "rank_moe_ignores_gate_weights": (S, "rank_moe", _rank_moe_no_gates, _all_moe_pins),
     "attn_proj_feeds_x_to_w_o": (L, "attn_proj_block", _attn_proj_x_to_wo, _all_proj_pins),
     "attn_proj_swaps_k_and_v": (L, "attn_proj_block", _attn_proj_kv_swapped, _all_proj_pins),
+    "layer_mlp_reads_x_not_h": (L, "layer", _layer_mlp_reads_x, _all_layer_pins),
+    "layer_out_skips_attention": (L, "layer", _layer_out_skips_attention, _all_layer_pins),
+    "moe_gates_of_reversed_experts": (L, "moe_block", _moe_block_experts_reversed, _all_moe_pins),
     # decomposition
+    "rank_mlp_silu_on_up": (S, "rank_mlp", _rank_mlp_silu_on_up, _all_sharded_pins),
+    "rank_attention_wrong_q_heads": (S, "rank_attention", _rank_attention_q_from_kv_block, _all_sharded_pins),
     "sum_drops_last_rank": (S, "sum_partials", lambda parts, residual=None: np.sum(
         [np.asarray(p, float) for p in parts[:-1]] or [np.zeros_like(parts[0])], axis=0)
         + (0.0 if residual is None else np.asarray(residual, float)), _all_sharded_pins),
